@@ -1,0 +1,494 @@
+"""Pins of the float64 oracle to facts outside itself: values the model cards print, closed
+forms, invariants, brute force on tiny inputs and independent library routines
+(transformers' WhisperFeatureExtractor, torch.nn.functional on the CPU).
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a wrong sign,
+index or transposed operand) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as Fn
+
+import oracle as O
+from audio_encoder_amd import synth as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "card_facts.json")
+
+
+def facts():
+    with open(GOLDEN) as f:
+        return {d["name"]: d["value"] for d in json.load(f)["facts"]}
+
+
+# --------------------------------------------------------------------------------------------
+# configuration and sizes (card figures)
+# --------------------------------------------------------------------------------------------
+def test_full_config_matches_card_figures():
+    f = facts()
+    c = O.FULL
+    assert O.SAMPLE_RATE == f["sample_rate"] and O.N_MELS == f["n_mels"]
+    assert O.N_FFT == f["n_fft"] and O.HOP == f["hop"]
+    assert c["conv_channels"] == f["conv_channels"]
+    assert c["conv_channels"] * (c["n_mels"] // 8) == f["conv_out_in"]  # 480*16 = 7680
+    for k in ("d_model", "n_layers", "n_heads", "head_dim", "d_ffn", "d_out", "d_adapter"):
+        assert c[k] == f[k], k
+    assert c["n_heads"] * c["head_dim"] == c["d_model"]
+    # 64 s piece = 800 tokens at 12.5 Hz
+    assert c["piece_tokens"] == f["long_audio_piece_seconds"] * f["frames_per_second"]
+
+
+def test_tower_parameter_count_is_065B():
+    n = O.tower_parameter_count(O.FULL)
+    assert n == 647_927_168
+    assert round(n / 1e9, 2) == facts()["encoder_params_billion"]
+    total = sum(int(np.prod(s)) for _, s in O.tensor_shapes(O.FULL))
+    assert total - n == 3 * 2048 * 8192  # adapter: gate, up, down, no biases
+    assert total == 698_258_816
+    assert sum(int(np.prod(s)) for _, s in O.tensor_shapes(O.TINY)) == 3_500_160
+
+
+def test_blob_layout_agrees_with_input_generator():
+    for cfg in (O.TINY, O.FULL):
+        assert O.tensor_shapes(cfg) == S.weight_spec(cfg)
+
+
+def test_bf16_rounding_of_blob_matches_torch():
+    x = np.random.default_rng(5).standard_normal(100000).astype(np.float32) * 0.02
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(S.round_to_bf16(x), ref)
+
+
+# --------------------------------------------------------------------------------------------
+# O1 framing, frame counts, 12.5 Hz
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [799, 801, 3000, 3001, 3007, 6399, 51200, 360000])
+def test_window_ceil_chain_equals_whole_clip_ceil_chain(T):
+    got = sum(w["L3"] for w in O.window_plan(T, 100))
+    assert got == math.ceil(T / 8)
+    a = T
+    for _ in range(3):
+        a = (a + 1) // 2
+    assert got == a
+
+
+@pytest.mark.parametrize("seconds,frames", [(4, 50), (30, 375), (64, 800), (16, 200),
+                                            (3600, 45000)])
+def test_output_rate_is_12_5_hz(seconds, frames):
+    f = facts()
+    n = seconds * f["sample_rate"]
+    assert O.n_mel_frames(n) == n // f["mel_frames_per_sample_hop"]
+    assert O.n_output_frames(n, 100) == frames == seconds * f["frames_per_second"]
+    assert O.n_output_frames(n, 25) == frames  # window size does not change the count
+
+
+def test_window_plan_tiles_the_clip():
+    plan = O.window_plan(3001, 100)
+    assert [w["start"] for w in plan] == [0, 800, 1600, 2400]
+    assert [w["L0"] for w in plan] == [800, 800, 800, 601]
+    assert [(w["L1"], w["L2"], w["L3"]) for w in plan[-1:]] == [(301, 151, 76)]
+    assert [w["tok"] for w in plan] == [0, 100, 200, 300]
+
+
+def test_reflect_pad_matches_numpy():
+    x = np.arange(1000, dtype=np.float64) ** 1.5
+    assert np.array_equal(O.reflect_pad(x, 200), np.pad(x, 200, mode="reflect"))
+    with pytest.raises(ValueError):
+        O.reflect_pad(x[:200], 200)
+
+
+def test_frames_are_centred_on_hop_multiples():
+    x = np.arange(2000, dtype=np.float64)
+    fr = O.frames(x)
+    assert fr.shape == (2000 // 160, 400)
+    assert np.array_equal(fr[:, 200], 160.0 * np.arange(fr.shape[0]))
+    assert np.array_equal(fr[0, :200], np.arange(200, 0, -1))  # mirrored left edge
+
+
+# --------------------------------------------------------------------------------------------
+# O2 STFT power
+# --------------------------------------------------------------------------------------------
+def test_stft_matches_numpy_rfft():
+    fr = np.random.default_rng(1).standard_normal((7, 400))
+    ref = np.abs(np.fft.rfft(fr * O.hann_periodic()[None], axis=1)) ** 2
+    np.testing.assert_allclose(O.stft_power(fr), ref, rtol=1e-11, atol=1e-9)
+
+
+def test_hann_is_periodic():
+    w = O.hann_periodic()
+    assert w[0] == 0.0 and abs(w[200] - 1.0) < 1e-15 and abs(w[100] - 0.5) < 1e-15
+    np.testing.assert_allclose(w[1:], w[1:][::-1], atol=1e-15)  # symmetric about n = 200
+
+
+@pytest.mark.parametrize("k,A", [(25, 0.3), (7, 1.0), (130, 0.05)])
+def test_stft_closed_form_for_bin_centred_sine(k, A):
+    # A*sin(2 pi k n / 400) under a periodic Hann window: |X[k]| = 100 A, |X[k+-1]| = 50 A,
+    # every other bin exactly 0 (three-term window, orthogonal exponentials).
+    x = A * np.sin(2.0 * np.pi * 40.0 * k * np.arange(8000) / 16000.0)  # fp64, not float32
+    P = O.stft_power(O.frames(x)[5:45])
+    np.testing.assert_allclose(P[:, k], (100 * A) ** 2, rtol=1e-9)
+    np.testing.assert_allclose(P[:, k - 1], (50 * A) ** 2, rtol=1e-9)
+    np.testing.assert_allclose(P[:, k + 1], (50 * A) ** 2, rtol=1e-9)
+    rest = np.delete(P, [k - 1, k, k + 1], axis=1)
+    assert rest.max() < 1e-20 * (100 * A) ** 2
+
+
+def test_parseval_per_frame():
+    fr = O.frames(S.pink_plus_bursts()[:40000].astype(np.float64))
+    P = O.stft_power(fr)
+    lhs = P[:, 0] + P[:, 200] + 2.0 * P[:, 1:200].sum(axis=1)
+    rhs = 400.0 * np.square(fr * O.hann_periodic()[None]).sum(axis=1)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-10)
+
+
+# --------------------------------------------------------------------------------------------
+# O3 mel filterbank (Slaney)
+# --------------------------------------------------------------------------------------------
+def test_slaney_mel_scale_values():
+    assert abs(float(O.hz_to_mel(1000.0)) - 15.0) < 1e-12
+    assert abs(float(O.hz_to_mel(6400.0)) - 42.0) < 1e-12  # 27 mel per factor 6.4
+    assert abs(float(O.hz_to_mel(8000.0)) - 45.2456) < 1e-4
+    assert abs(float(O.hz_to_mel(600.0)) - 9.0) < 1e-12
+    f = np.array([0.0, 50.0, 999.0, 1000.0, 3000.0, 8000.0])
+    np.testing.assert_allclose(O.mel_to_hz(O.hz_to_mel(f)), f, rtol=1e-12, atol=1e-9)
+    np.testing.assert_allclose(O.mel_points()[:4], [0.0, 23.383, 46.766, 70.148], atol=1e-3)
+
+
+def test_filterbank_shape_support_and_area():
+    W = O.mel_filterbank()
+    f = O.mel_points()
+    fb = 40.0 * np.arange(201)
+    assert W.shape == (128, 201) and W.min() >= 0.0
+    taps = (W > 0).sum(axis=1)
+    assert taps.min() >= 1 and taps.max() <= 9
+    for m in range(128):
+        nz = fb[W[m] > 0]
+        assert nz.min() > f[m] and nz.max() < f[m + 2]
+        # peak at the bin nearest the centre frequency f_{m+1}
+        assert abs(fb[np.argmax(W[m])] - f[m + 1]) <= 20.0 + 1e-9
+        base = f[m + 2] - f[m]
+        if base >= 300.0:  # wide triangles: the 40 Hz Riemann sum approximates unit area
+            assert abs(40.0 * W[m].sum() - 1.0) < 0.03
+
+
+def test_filterbank_matches_whisper_feature_extractor():
+    from transformers import WhisperFeatureExtractor
+    fe = WhisperFeatureExtractor(feature_size=128)
+    np.testing.assert_allclose(O.mel_filterbank(), fe.mel_filters.T, rtol=1e-12, atol=1e-15)
+
+
+# --------------------------------------------------------------------------------------------
+# O4 log-mel
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("which", ["sines", "pink_bursts", "tone", "stream"])
+def test_log_mel_matches_whisper_feature_extractor(which):
+    from transformers import WhisperFeatureExtractor
+    fe = WhisperFeatureExtractor(feature_size=128)
+    x = {"sines": lambda: S.three_sines(),
+         "pink_bursts": lambda: S.pink_plus_bursts()[:96000],
+         "tone": lambda: S.pure_tone_bin(25, 0.3, 32000),
+         "stream": lambda: S.hour_stream(seconds=45.0)}[which]()
+    ref = fe._np_extract_fbank_features(x[None].astype(np.float64), "cpu")[0].T
+    got = O.log_mel(x)
+    assert got.shape == ref.shape == (x.size // 160, 128)
+    # the library computes its spectrogram partly in float32
+    assert np.abs(got - ref).max() < 1e-6
+
+
+def test_log_mel_of_silence_is_minus_1_5():
+    m = O.log_mel(np.zeros(16000))
+    assert m.shape == (100, 128) and np.all(m == -1.5)
+
+
+def test_log_mel_range_and_active_clamp():
+    m = O.log_mel(S.pink_plus_bursts()[:160000])
+    top = m.max()
+    assert m.min() >= top - 2.0 - 1e-12
+    # a pure bin-centred sine leaves most bins at the 1e-10 floor: the clamp must bite
+    t = O.log_mel(S.pure_tone_bin(25, 0.3, 32000))
+    assert abs(t.min() - (t.max() - 2.0)) < 1e-12
+    assert (t == t.min()).mean() > 0.5
+
+
+# --------------------------------------------------------------------------------------------
+# O6 conv stack
+# --------------------------------------------------------------------------------------------
+def conv_brute(x, w, b):
+    Cin, H, T = x.shape
+    Cout = w.shape[0]
+    Ho, To = (H + 1) // 2, (T + 1) // 2
+    y = np.zeros((Cout, Ho, To))
+    for o in range(Cout):
+        for i in range(Ho):
+            for j in range(To):
+                s = b[o]
+                for c in range(Cin):
+                    for a in range(3):
+                        for bb in range(3):
+                            hi, tj = 2 * i + a - 1, 2 * j + bb - 1
+                            if 0 <= hi < H and 0 <= tj < T:
+                                s += w[o, c, a, bb] * x[c, hi, tj]
+                y[o, i, j] = s
+    return y
+
+
+@pytest.mark.parametrize("shape", [(2, 5, 7), (3, 8, 6), (1, 4, 1), (2, 1, 9)])
+def test_conv_matches_brute_force_and_torch(shape):
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(shape)
+    w = rng.standard_normal((4, shape[0], 3, 3))
+    b = rng.standard_normal(4)
+    got = O.conv2d_s2(x, w, b)
+    np.testing.assert_allclose(got, conv_brute(x, w, b), rtol=1e-12, atol=1e-12)
+    ref = Fn.conv2d(torch.from_numpy(x)[None], torch.from_numpy(w), torch.from_numpy(b),
+                    stride=2, padding=1)[0].numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("a0,b0", [(0, 0), (1, 1), (2, 0), (0, 2), (2, 2), (1, 2)])
+def test_conv_index_probe_one_hot_tap(a0, b0):
+    # a one-hot 3x3 kernel with an identity channel map reproduces the input shifted by
+    # (a0-1, b0-1) on the stride-2 grid, zeros outside the image; exact in any precision
+    C, H, T = 3, 10, 13
+    x = np.arange(C * H * T, dtype=np.float64).reshape(C, H, T) + 1.0
+    w = np.zeros((C, C, 3, 3))
+    for c in range(C):
+        w[c, c, a0, b0] = 1.0
+    y = O.conv2d_s2(x, w, np.zeros(C))
+    for i in range(y.shape[1]):
+        for j in range(y.shape[2]):
+            hi, tj = 2 * i + a0 - 1, 2 * j + b0 - 1
+            want = x[:, hi, tj] if (0 <= hi < H and 0 <= tj < T) else np.zeros(C)
+            assert np.array_equal(y[:, i, j], want)
+
+
+def test_conv_stack_sizes_give_7680_features():
+    rng = np.random.default_rng(0)
+    Wt = {f"conv{i}.w": rng.standard_normal((480, 1 if i == 1 else 480, 3, 3)) * 0.02
+          for i in (1, 2, 3)}
+    Wt.update({f"conv{i}.b": np.zeros(480) for i in (1, 2, 3)})
+    ys = O.conv_stack(rng.standard_normal((37, 128)), Wt)
+    assert [y.shape for y in ys] == [(480, 64, 19), (480, 32, 10), (480, 16, 5)]
+    assert O.flatten_tokens(ys[2]).shape == (5, 7680)
+
+
+def test_flatten_is_channel_major():
+    C, F, L = 3, 4, 2
+    y = np.zeros((C, F, L))
+    for c in range(C):
+        for f in range(F):
+            for j in range(L):
+                y[c, f, j] = 1000 * j + 10 * c + f
+    h = O.flatten_tokens(y)
+    for j in range(L):
+        for c in range(C):
+            for f in range(F):
+                assert h[j, c * F + f] == 1000 * j + 10 * c + f
+
+
+# --------------------------------------------------------------------------------------------
+# O7 positions, LN, activations
+# --------------------------------------------------------------------------------------------
+def test_sinusoids():
+    pe = O.sinusoids(100, 1280)
+    assert np.array_equal(pe[0], np.concatenate([np.zeros(640), np.ones(640)]))
+    np.testing.assert_allclose(pe[:, :640] ** 2 + pe[:, 640:] ** 2, 1.0, atol=1e-14)
+    w = O.inv_timescales(1280)
+    assert w[0] == 1.0 and abs(w[-1] - 1e-4) < 1e-18
+    assert abs(pe[1, 0] - math.sin(1.0)) < 1e-15 and abs(pe[7, 640] - math.cos(7.0)) < 1e-15
+    np.testing.assert_allclose(np.diff(np.log(w)), -math.log(1e4) / 639, rtol=1e-12)
+
+
+def test_layer_norm_matches_torch():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((9, 1280)) * 3 + 1
+    g = rng.standard_normal(1280)
+    b = rng.standard_normal(1280)
+    ref = Fn.layer_norm(torch.from_numpy(x), (1280,), torch.from_numpy(g), torch.from_numpy(b),
+                        eps=1e-5).numpy()
+    np.testing.assert_allclose(O.layer_norm(x, g, b), ref, rtol=1e-12, atol=1e-12)
+    z = O.layer_norm(x, np.ones(1280), np.zeros(1280))
+    np.testing.assert_allclose(z.mean(axis=1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(z.var(axis=1), 1.0 / (1.0 + 1e-5 / x.var(axis=1)), rtol=1e-10)
+
+
+def test_gelu_and_silu():
+    x = np.linspace(-8, 8, 1001)
+    np.testing.assert_allclose(O.gelu(x) - O.gelu(-x), x, atol=1e-14)
+    np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, atol=1e-14)
+    t = torch.from_numpy(x)
+    np.testing.assert_allclose(O.gelu(x), Fn.gelu(t).numpy(), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(O.silu(x), Fn.silu(t).numpy(), rtol=1e-13, atol=1e-15)
+    assert abs(float(O.gelu(np.array([1.0]))[0]) - 0.5 * (1 + math.erf(1 / math.sqrt(2)))) < 1e-15
+
+
+# --------------------------------------------------------------------------------------------
+# O8 attention
+# --------------------------------------------------------------------------------------------
+def attention_brute(q, k, v, nh):
+    n, d = q.shape
+    hd = d // nh
+    o = np.zeros_like(q)
+    for h in range(nh):
+        for i in range(n):
+            s = [sum(q[i, h * hd + c] * k[j, h * hd + c] for c in range(hd)) / math.sqrt(hd)
+                 for j in range(n)]
+            m = max(s)
+            e = [math.exp(t - m) for t in s]
+            z = sum(e)
+            for c in range(hd):
+                o[i, h * hd + c] = sum(e[j] / z * v[j, h * hd + c] for j in range(n))
+    return o
+
+
+def test_window_attention_matches_brute_force():
+    rng = np.random.default_rng(6)
+    q, k, v = (rng.standard_normal((7, 128)) for _ in range(3))
+    np.testing.assert_allclose(O.window_attention(q, k, v, 2), attention_brute(q, k, v, 2),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_block_diagonal_equals_dense_masked_attention():
+    rng = np.random.default_rng(7)
+    d, nh = 128, 2
+    wins = [(0, 5), (5, 5), (10, 3)]
+    n = 13
+    Wt = {"layers.0.ln1.g": np.ones(d), "layers.0.ln1.b": np.zeros(d),
+          "layers.0.ln2.g": rng.standard_normal(d), "layers.0.ln2.b": rng.standard_normal(d)}
+    for nm in ("q", "k", "v", "o"):
+        Wt[f"layers.0.{nm}.w"] = rng.standard_normal((d, d)) * 0.1
+        Wt[f"layers.0.{nm}.b"] = rng.standard_normal(d) * 0.1
+    Wt["layers.0.fc1.w"] = rng.standard_normal((64, d)) * 0.1
+    Wt["layers.0.fc1.b"] = rng.standard_normal(64)
+    Wt["layers.0.fc2.w"] = rng.standard_normal((d, 64)) * 0.1
+    Wt["layers.0.fc2.b"] = rng.standard_normal(d)
+    x = rng.standard_normal((n, d))
+    got = O.encoder_layer(x, Wt, 0, wins, nh)
+    # dense attention over all tokens with -inf outside each window (torch SDPA, fp64)
+    T = {k_: torch.from_numpy(v_) for k_, v_ in Wt.items()}
+    xt = torch.from_numpy(x)
+    a = Fn.layer_norm(xt, (d,), T["layers.0.ln1.g"], T["layers.0.ln1.b"], 1e-5)
+    q = Fn.linear(a, T["layers.0.q.w"], T["layers.0.q.b"]).view(n, nh, 64).transpose(0, 1)
+    k = Fn.linear(a, T["layers.0.k.w"], T["layers.0.k.b"]).view(n, nh, 64).transpose(0, 1)
+    v = Fn.linear(a, T["layers.0.v.w"], T["layers.0.v.b"]).view(n, nh, 64).transpose(0, 1)
+    mask = torch.full((n, n), float("-inf"), dtype=torch.float64)
+    for t0, m in wins:
+        mask[t0:t0 + m, t0:t0 + m] = 0.0
+    o = Fn.scaled_dot_product_attention(q, k, v, attn_mask=mask).transpose(0, 1).reshape(n, d)
+    xt = xt + Fn.linear(o, T["layers.0.o.w"], T["layers.0.o.b"])
+    h = Fn.gelu(Fn.linear(Fn.layer_norm(xt, (d,), T["layers.0.ln2.g"], T["layers.0.ln2.b"],
+                                        1e-5), T["layers.0.fc1.w"], T["layers.0.fc1.b"]))
+    ref = xt + Fn.linear(h, T["layers.0.fc2.w"], T["layers.0.fc2.b"])
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-11, atol=1e-11)
+
+
+def test_attention_invariants():
+    rng = np.random.default_rng(8)
+    q, k, v = (rng.standard_normal((9, 128)) for _ in range(3))
+    base = O.window_attention(q, k, v, 2)
+    # a key bias (same vector added to every key) cancels in the softmax
+    kb = k + rng.standard_normal(128)[None, :]
+    np.testing.assert_allclose(O.window_attention(q, kb, v, 2), base, rtol=1e-11, atol=1e-12)
+    # zero queries: uniform weights, output = mean of v over the window
+    z = O.window_attention(np.zeros_like(q), k, v, 2)
+    np.testing.assert_allclose(z, np.broadcast_to(v.mean(axis=0), z.shape), atol=1e-14)
+    # position probe: v = position in window -> (n - 1) / 2
+    pos = np.broadcast_to(np.arange(9.0)[:, None], (9, 128)).copy()
+    assert np.allclose(O.window_attention(np.zeros_like(q), k, pos, 2), 4.0)
+
+
+# --------------------------------------------------------------------------------------------
+# whole tower: an independent fp64 torch assembly from library ops, and the window invariants
+# --------------------------------------------------------------------------------------------
+def torch_tower(mel, Wt, cfg):
+    """The tower written with torch.nn.functional library routines (conv2d, layer_norm, SDPA
+    with a block-diagonal mask, gelu, silu) instead of the oracle's own loops and matmuls."""
+    T = {k: torch.from_numpy(v) for k, v in Wt.items()}
+    Wn = cfg["window_tokens"]
+    outs, wins, tok = [], [], 0
+    for s in range(0, mel.shape[0], 8 * Wn):
+        x = torch.from_numpy(mel[s:s + 8 * Wn].T.copy())[None, None]
+        for i in (1, 2, 3):
+            x = Fn.gelu(Fn.conv2d(x, T[f"conv{i}.w"], T[f"conv{i}.b"], stride=2, padding=1))
+        x = x[0].permute(2, 0, 1).reshape(x.shape[-1], -1)
+        L = x.shape[0]
+        pos = torch.arange(L, dtype=torch.float64)[:, None]
+        h = cfg["d_model"] // 2
+        inv = torch.exp(-math.log(10000.0) * torch.arange(h, dtype=torch.float64) / (h - 1))
+        pe = torch.cat([torch.sin(pos * inv), torch.cos(pos * inv)], dim=1)
+        outs.append(Fn.linear(x, T["conv_out.w"]) + pe)
+        wins.append((tok, L))
+        tok += L
+    x = torch.cat(outs)
+    n, d, nh = x.shape[0], cfg["d_model"], cfg["n_heads"]
+    mask = torch.full((n, n), float("-inf"), dtype=torch.float64)
+    for t0, m in wins:
+        mask[t0:t0 + m, t0:t0 + m] = 0.0
+    for i in range(cfg["n_layers"]):
+        p = f"layers.{i}."
+        a = Fn.layer_norm(x, (d,), T[p + "ln1.g"], T[p + "ln1.b"], 1e-5)
+        q, k, v = (Fn.linear(a, T[p + nm + ".w"], T[p + nm + ".b"]).view(n, nh, -1)
+                   .transpose(0, 1) for nm in ("q", "k", "v"))
+        o = Fn.scaled_dot_product_attention(q, k, v, attn_mask=mask).transpose(0, 1).reshape(n, d)
+        x = x + Fn.linear(o, T[p + "o.w"], T[p + "o.b"])
+        a = Fn.layer_norm(x, (d,), T[p + "ln2.g"], T[p + "ln2.b"], 1e-5)
+        x = x + Fn.linear(Fn.gelu(Fn.linear(a, T[p + "fc1.w"], T[p + "fc1.b"])),
+                          T[p + "fc2.w"], T[p + "fc2.b"])
+    z = Fn.layer_norm(x, (d,), T["ln_post.g"], T["ln_post.b"], 1e-5)
+    z = Fn.linear(Fn.gelu(Fn.linear(z, T["proj1.w"], T["proj1.b"])), T["proj2.w"], T["proj2.b"])
+    return Fn.linear(Fn.silu(Fn.linear(z, T["gate.w"])) * Fn.linear(z, T["up.w"]),
+                     T["down.w"]).numpy()
+
+
+@pytest.fixture(scope="module")
+def tiny_weights():
+    return O.unpack_weights(S.make_weights(O.TINY, seed=0), O.TINY)
+
+
+def test_tiny_tower_matches_torch_library_assembly(tiny_weights):
+    mel = O.log_mel(S.three_sines())
+    got = O.encode_mel(mel, tiny_weights, O.TINY)
+    assert got.shape == (50, 512)
+    ref = torch_tower(mel, tiny_weights, O.TINY)
+    np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-12 * np.abs(ref).max())
+
+
+def test_tiny_tower_partial_window_matches_torch(tiny_weights):
+    # 3.37 s: 337 frames -> one full window of 200 frames and a 137-frame partial window
+    x = S.pink_plus_bursts(seed=9, n=53920)
+    mel = O.log_mel(x)
+    assert mel.shape[0] == 337
+    got = O.encode_mel(mel, tiny_weights, O.TINY)
+    assert got.shape[0] == 25 + 18
+    np.testing.assert_allclose(got, torch_tower(mel, tiny_weights, O.TINY), rtol=1e-9,
+                               atol=1e-12)
+
+
+def test_pieces_equal_whole_clip(tiny_weights):
+    # long-audio mode (64 s pieces, one log-mel maximum for the whole recording) reproduces the
+    # whole-clip encoding; with window-local encoding this holds exactly in the oracle
+    x = S.segment_stream(11, 150.0)
+    whole = O.encode(x, tiny_weights, O.TINY)
+    pieces = O.encode_long(x, tiny_weights, O.TINY)
+    assert whole.shape == pieces.shape == (O.n_output_frames(x.size, 25), 512)
+    assert np.array_equal(whole, pieces)
+
+
+def test_windows_are_independent(tiny_weights):
+    mel = O.log_mel(S.pink_plus_bursts(seed=3, n=160000))  # 1000 frames = 5 windows of 200
+    y = O.encode_mel(mel, tiny_weights, O.TINY)
+    # permuting whole windows permutes the output windows
+    perm = [3, 0, 4, 1, 2]
+    mp = np.concatenate([mel[200 * p:200 * p + 200] for p in perm])
+    yp = O.encode_mel(mp, tiny_weights, O.TINY)
+    for i, p in enumerate(perm):
+        np.testing.assert_allclose(yp[25 * i:25 * i + 25], y[25 * p:25 * p + 25], rtol=1e-12,
+                                   atol=1e-15)
+    # deleting a window leaves the others unchanged
+    md = np.concatenate([mel[:400], mel[600:]])
+    yd = O.encode_mel(md, tiny_weights, O.TINY)
+    np.testing.assert_allclose(yd, np.concatenate([y[:50], y[75:]]), rtol=1e-12, atol=1e-15)
