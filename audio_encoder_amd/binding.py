@@ -1,0 +1,272 @@
+"""ctypes binding of ``libaudio_encoder.so`` (declared in ``include/audio_encoder.h``).
+
+Argument marshalling only: every step of the forward pass runs in the library's HIP kernels.
+PyTorch is used for device memory and the current stream.  There is no fallback: if the library
+is missing or the GPU is absent, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_double, c_float, c_int32, c_int64, c_void_p
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaudio_encoder.so")
+
+ENC_OK = 0
+ENC_E_INVALID_ARG = -1
+ENC_E_OUT_OF_MEMORY = -2
+ENC_E_DEVICE = -3
+ENC_E_UNSUPPORTED = -4
+ENC_BF16 = 0
+ENC_F32 = 1
+
+# kernel ids of encoder_timing_read
+KERNELS = ["mel", "conv1", "conv2", "conv3", "conv_out", "layernorm", "qkv", "attention", "o_proj",
+           "ffn1", "ffn2", "proj1", "proj2", "gate_up", "down", "other"]
+
+STAGE_MEL, STAGE_CONV1, STAGE_CONV2, STAGE_CONV3, STAGE_EMBED, STAGE_LAYER, STAGE_HEAD, \
+    STAGE_OUT = range(8)
+
+# Full-size tower ("cstr/MOSS-Transcribe-preview-2B-GGUF" card, "Architecture"), and a tiny
+# fp32 stand-in of the same structure for fast end-to-end checks.
+FULL = dict(sample_rate=16000, n_fft=400, hop=160, n_mels=128, conv_channels=480, d_model=1280,
+            n_layers=32, n_heads=20, head_dim=64, d_ffn=5120, window_tokens=100, d_out=2048,
+            d_adapter=8192, piece_tokens=800, dtype="bf16", ln_eps=1e-5, max_tokens_per_pass=8192)
+TINY = dict(FULL, conv_channels=32, d_model=256, n_layers=2, n_heads=4, d_ffn=1024,
+            window_tokens=25, d_out=512, d_adapter=1024, dtype="f32")
+
+
+class EncoderCfg(ctypes.Structure):
+    _fields_ = [("sample_rate", c_int32), ("n_fft", c_int32), ("hop", c_int32),
+                ("n_mels", c_int32), ("conv_channels", c_int32), ("d_model", c_int32),
+                ("n_layers", c_int32), ("n_heads", c_int32), ("head_dim", c_int32),
+                ("d_ffn", c_int32), ("window_tokens", c_int32), ("d_out", c_int32),
+                ("d_adapter", c_int32), ("piece_tokens", c_int32), ("dtype", c_int32),
+                ("ln_eps", c_float), ("max_tokens_per_pass", c_int64)]
+
+
+def make_cfg(cfg: dict) -> EncoderCfg:
+    c = EncoderCfg()
+    for name, _ in EncoderCfg._fields_:
+        v = cfg[name]
+        if name == "dtype":
+            v = {"bf16": ENC_BF16, "f32": ENC_F32}.get(v, v)
+        setattr(c, name, v)
+    return c
+
+
+class EncoderError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+_SIGS = {
+    "encoder_validate_cfg": [POINTER(EncoderCfg)],
+    "encoder_weight_count": [POINTER(EncoderCfg), POINTER(c_int64)],
+    "encoder_output_frames": [POINTER(EncoderCfg), c_int64, POINTER(c_int64)],
+    "encoder_plan_windows": [POINTER(EncoderCfg), c_int64, c_int32, POINTER(c_int32), c_int32,
+                             POINTER(c_int32)],
+    "encoder_create": [POINTER(c_float), c_int64, POINTER(EncoderCfg), POINTER(c_void_p)],
+    "encoder_destroy": [c_void_p],
+    "encoder_memory_stats": [c_void_p, POINTER(c_int64), POINTER(c_int64)],
+    "encoder_forward": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
+    "encoder_forward_long": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
+    "encoder_log_mel": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
+    "encoder_debug_stage": [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p,
+                            c_int64, c_void_p],
+    "encoder_timing_enable": [c_void_p, c_int32],
+    "encoder_timing_read": [c_void_p, POINTER(c_double), POINTER(c_int64), c_int32],
+    "encoder_op_linear": [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32,
+                          c_int32, c_int32, c_void_p],
+    "encoder_op_attention": [c_void_p, c_void_p, c_int32, c_int32, c_int64, c_void_p, c_int32,
+                             c_void_p],
+    "encoder_op_layernorm": [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_float,
+                             c_int32, c_void_p],
+    "encoder_last_error": [],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m audio_encoder_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = None if name == "encoder_destroy" else c_int32
+        L.encoder_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(st: int):
+    if st != ENC_OK:
+        raise EncoderError(st, lib().encoder_last_error().decode())
+
+
+# ---- host-only calls ---------------------------------------------------------------------------
+def encoder_validate_cfg(cfg: dict) -> int:
+    c = make_cfg(cfg)
+    return lib().encoder_validate_cfg(ctypes.byref(c))
+
+
+def encoder_weight_count(cfg: dict) -> int:
+    c, n = make_cfg(cfg), c_int64()
+    _check(lib().encoder_weight_count(ctypes.byref(c), ctypes.byref(n)))
+    return n.value
+
+
+def encoder_output_frames(cfg: dict, n_samples: int) -> int:
+    c, n = make_cfg(cfg), c_int64()
+    _check(lib().encoder_output_frames(ctypes.byref(c), n_samples, ctypes.byref(n)))
+    return n.value
+
+
+def encoder_plan_windows(cfg: dict, n_samples: int, batch: int) -> np.ndarray:
+    c, nw = make_cfg(cfg), c_int32()
+    _check(lib().encoder_plan_windows(ctypes.byref(c), n_samples, batch, None, 0, ctypes.byref(nw)))
+    tab = np.zeros((nw.value, 7), dtype=np.int32)
+    _check(lib().encoder_plan_windows(ctypes.byref(c), n_samples, batch,
+                                      tab.ctypes.data_as(POINTER(c_int32)), nw.value,
+                                      ctypes.byref(nw)))
+    return tab
+
+
+# ---- device calls (torch tensors for memory and stream) ---------------------------------------
+def _stream():
+    import torch
+    return c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t) -> c_void_p:
+    return c_void_p(t.data_ptr()) if t is not None else c_void_p(0)
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    return ENC_BF16 if dt == torch.bfloat16 else ENC_F32
+
+
+class Encoder:
+    """One packed copy of the weights on the current GPU plus its workspace."""
+
+    def __init__(self, weights: np.ndarray, cfg: dict):
+        import torch
+        if not torch.cuda.is_available():
+            raise RuntimeError("audio_encoder_amd needs a GPU; none is visible")
+        self.cfg = dict(cfg)
+        self._c = make_cfg(self.cfg)
+        w = np.ascontiguousarray(weights, dtype=np.float32)
+        h = c_void_p()
+        _check(lib().encoder_create(w.ctypes.data_as(POINTER(c_float)), w.size,
+                                    ctypes.byref(self._c), ctypes.byref(h)))
+        self._h = h
+        self.out_dtype = torch.bfloat16 if self.cfg["dtype"] == "bf16" else torch.float32
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().encoder_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def output_frames(self, n_samples: int) -> int:
+        return encoder_output_frames(self.cfg, n_samples)
+
+    def forward(self, pcm, out=None):
+        """pcm: float32 CUDA tensor [batch, n_samples] -> [batch, F, d_out]."""
+        import torch
+        assert pcm.is_cuda and pcm.dtype == torch.float32 and pcm.is_contiguous()
+        B, N = pcm.shape
+        F = self.output_frames(N)
+        if out is None:
+            out = torch.empty((B, F, self.cfg["d_out"]), dtype=self.out_dtype, device=pcm.device)
+        _check(lib().encoder_forward(self._h, _ptr(pcm), N, B, _ptr(out), _stream()))
+        return out
+
+    def forward_long(self, pcm, pieces_per_pass: int = 1, out=None):
+        """pcm: float32 CUDA tensor [n_samples] (one recording) -> [F, d_out]."""
+        import torch
+        assert pcm.is_cuda and pcm.dtype == torch.float32 and pcm.is_contiguous()
+        N = pcm.numel()
+        F = self.output_frames(N)
+        if out is None:
+            out = torch.empty((F, self.cfg["d_out"]), dtype=self.out_dtype, device=pcm.device)
+        _check(lib().encoder_forward_long(self._h, _ptr(pcm), N, pieces_per_pass, _ptr(out),
+                                          _stream()))
+        return out
+
+    def log_mel(self, pcm):
+        import torch
+        B, N = pcm.shape
+        mel = torch.empty((B, N // 160, 128), dtype=torch.float32, device=pcm.device)
+        _check(lib().encoder_log_mel(self._h, _ptr(pcm), N, B, _ptr(mel), _stream()))
+        return mel
+
+    def debug_stage(self, pcm, stage: int, layer: int = 0):
+        """float32 copy of one stage's output (layouts in include/audio_encoder.h)."""
+        import torch
+        B, N = pcm.shape
+        cfg = self.cfg
+        T = N // 160
+        F = self.output_frames(N) * B
+        nw = len(encoder_plan_windows(cfg, N, B))
+        W, C = cfg["window_tokens"], cfg["conv_channels"]
+        shape = {STAGE_MEL: (B, T, 128), STAGE_CONV1: (nw, 4 * W, 64, C),
+                 STAGE_CONV2: (nw, 2 * W, 32, C), STAGE_CONV3: (F, 16, C),
+                 STAGE_EMBED: (F, cfg["d_model"]), STAGE_LAYER: (F, cfg["d_model"]),
+                 STAGE_HEAD: (F, cfg["d_out"]), STAGE_OUT: (F, cfg["d_out"])}[stage]
+        dst = torch.empty(shape, dtype=torch.float32, device=pcm.device)
+        _check(lib().encoder_debug_stage(self._h, _ptr(pcm), N, B, stage, layer, _ptr(dst),
+                                         dst.numel(), _stream()))
+        return dst
+
+    def memory_stats(self) -> tuple[int, int]:
+        w, ws = c_int64(), c_int64()
+        _check(lib().encoder_memory_stats(self._h, ctypes.byref(w), ctypes.byref(ws)))
+        return w.value, ws.value
+
+    def timing_enable(self, on: bool = True):
+        _check(lib().encoder_timing_enable(self._h, 1 if on else 0))
+
+    def timing_read(self, reset: bool = True) -> dict:
+        ms = (c_double * len(KERNELS))()
+        n = (c_int64 * len(KERNELS))()
+        _check(lib().encoder_timing_read(self._h, ms, n, 1 if reset else 0))
+        return {k: (ms[i], n[i]) for i, k in enumerate(KERNELS)}
+
+
+# ---- single-kernel entry points ------------------------------------------------------------------
+def op_linear(A, W, bias, C, epi: int):
+    """C = epi(A W^T) (see encoder_op_linear)."""
+    M, K = A.shape
+    N = W.shape[0]
+    _check(lib().encoder_op_linear(_ptr(A), _ptr(W), _ptr(bias), _ptr(C), M, N, K, epi,
+                                   _dtype_code(A.dtype), _stream()))
+    return C
+
+
+def op_attention(qkv, windows, n_heads: int, out):
+    _check(lib().encoder_op_attention(_ptr(qkv), _ptr(windows), windows.shape[0], n_heads,
+                                      qkv.shape[0], _ptr(out), _dtype_code(qkv.dtype), _stream()))
+    return out
+
+
+def op_layernorm(x, gamma, beta, y, eps: float = 1e-5):
+    M, D = x.shape
+    _check(lib().encoder_op_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), M, D, eps,
+                                      _dtype_code(y.dtype), _stream()))
+    return y

@@ -1,0 +1,977 @@
+// Host side of the C ABI (include/audio_encoder.h): configuration checks, the window planner,
+// weight packing, workspace management and the order of kernel launches of one forward pass.
+//
+// Forward pass ("cstr/MOSS-Transcribe-preview-2B-GGUF" card, "Architecture"):
+//   log-mel (+ per-clip max) -> conv1 -> conv2 -> conv3 -> conv_out + positions ->
+//   n_layers x [LN1 -> QKV -> windowed attention -> out-proj + residual ->
+//               LN2 -> FFN1 + GELU -> FFN2 + residual] ->
+//   ln_post -> proj1 + GELU -> proj2 -> gate|up + SwiGLU -> down.
+// Windows are the independent units (8*W mel frames each, zero time-padding at their own
+// edges, positions restarting at 0), so a call is split into passes of whole windows that fit
+// the workspace; the long-audio path groups whole 64 s pieces per pass ("SILVERTHRONE/Ossicle-4B"
+// card, "Long Audio").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "ae_internal.h"
+
+namespace ae {
+
+static thread_local std::string g_err;
+void set_error(const std::string& msg) { g_err = msg; }
+encoder_status hip_fail(hipError_t err, const char* what) {
+  set_error(std::string(what) + ": " + hipGetErrorString(err));
+  return err == hipErrorOutOfMemory ? ENC_E_OUT_OF_MEMORY : ENC_E_DEVICE;
+}
+
+static encoder_status invalid(const std::string& msg) {
+  set_error(msg);
+  return ENC_E_INVALID_ARG;
+}
+
+// ------------------------------------------------------------------------------------------
+// configuration
+// ------------------------------------------------------------------------------------------
+static encoder_status check_cfg(const encoder_cfg* c) {
+  if (!c) return invalid("cfg is NULL");
+  if (c->n_fft != 400 || c->hop != 160 || c->n_mels != 128)
+    return invalid("the front end is fixed at n_fft=400, hop=160, n_mels=128");
+  if (c->conv_channels <= 0 || c->conv_channels % 32 != 0)
+    return invalid("conv_channels must be a positive multiple of 32");
+  if (c->head_dim != 64) return invalid("head_dim must be 64");
+  if (c->n_heads <= 0 || c->n_heads * c->head_dim != c->d_model)
+    return invalid("n_heads * head_dim must equal d_model");
+  if (c->d_model % 64 || c->d_ffn <= 0 || c->d_ffn % 64 || c->d_out <= 0 || c->d_out % 64 ||
+      c->d_adapter <= 0 || c->d_adapter % 64)
+    return invalid("d_model, d_ffn, d_out and d_adapter must be positive multiples of 64");
+  if (c->n_layers < 0) return invalid("n_layers must be >= 0");
+  if (c->window_tokens < 1 || c->window_tokens > 128)
+    return invalid("window_tokens must be in [1, 128]");
+  if (c->piece_tokens < c->window_tokens || c->piece_tokens % c->window_tokens)
+    return invalid("piece_tokens must be a positive multiple of window_tokens");
+  if (c->dtype != ENC_BF16 && c->dtype != ENC_F32) return invalid("dtype must be ENC_BF16 or ENC_F32");
+  if (!(c->ln_eps > 0.0f)) return invalid("ln_eps must be > 0");
+  if (c->max_tokens_per_pass < 0) return invalid("max_tokens_per_pass must be >= 0");
+  if (c->max_tokens_per_pass > 0 && c->max_tokens_per_pass < c->window_tokens)
+    return invalid("max_tokens_per_pass must hold at least one window");
+  if (c->sample_rate != 16000) {
+    set_error("only 16 kHz input is supported (no resampling)");
+    return ENC_E_UNSUPPORTED;
+  }
+  return ENC_OK;
+}
+
+static int64_t max_tokens(const encoder_cfg& c) {
+  return c.max_tokens_per_pass > 0 ? c.max_tokens_per_pass : 8192;
+}
+static int64_t max_windows(const encoder_cfg& c) { return max_tokens(c) / c.window_tokens + 32; }
+
+struct TensorSpec { const char* name; int64_t n; };
+
+// blob order, see encoder_weight_count in the header
+static std::vector<int64_t> blob_sizes(const encoder_cfg& c) {
+  const int64_t C = c.conv_channels, d = c.d_model, f = c.d_ffn, o = c.d_out, a = c.d_adapter;
+  std::vector<int64_t> s = {C * 9, C, C * C * 9, C, C * C * 9, C, d * C * 16};
+  for (int i = 0; i < c.n_layers; ++i) {
+    const int64_t L[] = {d, d, d * d, d, d * d, d, d * d, d, d * d, d, d, d, f * d, f, d * f, d};
+    s.insert(s.end(), std::begin(L), std::end(L));
+  }
+  const int64_t H[] = {d, d, d * d, d, o * d, o, a * o, a * o, o * a};
+  s.insert(s.end(), std::begin(H), std::end(H));
+  return s;
+}
+
+// ------------------------------------------------------------------------------------------
+// window plan
+// ------------------------------------------------------------------------------------------
+static void plan_windows(const encoder_cfg& c, int64_t n_samples, int32_t batch,
+                         std::vector<Win>& out) {
+  const int64_t T = n_samples / c.hop;
+  const int64_t wf = 8 * (int64_t)c.window_tokens;
+  out.clear();
+  int64_t tok = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    for (int64_t s = 0; s < T; s += wf) {
+      Win w;
+      w.clip = b;
+      w.start = (int32_t)s;
+      w.L0 = (int32_t)std::min<int64_t>(wf, T - s);
+      w.L1 = (w.L0 + 1) / 2;
+      w.L2 = (w.L1 + 1) / 2;
+      w.L3 = (w.L2 + 1) / 2;
+      w.tok = (int32_t)tok;
+      w.pad = 0;
+      tok += w.L3;
+      out.push_back(w);
+    }
+  }
+}
+
+static int64_t frames_out(const encoder_cfg& c, int64_t n_samples) {
+  const int64_t T = n_samples / c.hop;
+  const int64_t wf = 8 * (int64_t)c.window_tokens;
+  const int64_t full = T / wf, r = T % wf;
+  int64_t f = full * c.window_tokens;
+  if (r) f += (((r + 1) / 2 + 1) / 2 + 1) / 2;
+  return f;
+}
+
+struct Pass { int64_t win0, nwin, tok0, ntok; };
+
+// consecutive windows grouped into passes; a pass ends where `boundary(window)` says so or
+// where the next window would overflow the workspace
+template <class F>
+static std::vector<Pass> split_passes(const std::vector<Win>& w, int64_t mt, int64_t mw, F boundary) {
+  std::vector<Pass> ps;
+  Pass cur{0, 0, 0, 0};
+  for (size_t i = 0; i < w.size(); ++i) {
+    const bool brk = cur.nwin > 0 &&
+                     (cur.ntok + w[i].L3 > mt || cur.nwin + 1 > mw || boundary((int64_t)i));
+    if (brk) {
+      ps.push_back(cur);
+      cur = Pass{(int64_t)i, 0, w[i].tok, 0};
+    }
+    if (cur.nwin == 0) cur.tok0 = w[i].tok, cur.win0 = (int64_t)i;
+    cur.nwin += 1;
+    cur.ntok += w[i].L3;
+  }
+  if (cur.nwin) ps.push_back(cur);
+  return ps;
+}
+
+// ------------------------------------------------------------------------------------------
+// host tables: twiddles, window, Slaney filterbank, positions
+// ------------------------------------------------------------------------------------------
+static void mel_host_tables(std::vector<float>& tw, std::vector<float>& win,
+                            std::vector<int32_t>& fstart, std::vector<int32_t>& flen,
+                            std::vector<float>& fw) {
+  const double PI = 3.14159265358979323846;
+  tw.resize(800);
+  win.resize(400);
+  for (int j = 0; j < 400; ++j) {
+    tw[2 * j] = (float)std::cos(2.0 * PI * j / 400.0);
+    tw[2 * j + 1] = (float)std::sin(2.0 * PI * j / 400.0);
+    win[j] = (float)(0.5 - 0.5 * std::cos(2.0 * PI * j / 400.0));
+  }
+  // Slaney mel scale: 3 mel per 200 Hz below 1 kHz, then 27 mel per factor 6.4
+  auto hz2mel = [](double f) {
+    return f < 1000.0 ? f * 3.0 / 200.0 : 15.0 + std::log(f / 1000.0) * 27.0 / std::log(6.4);
+  };
+  auto mel2hz = [](double m) {
+    return m < 15.0 ? m * 200.0 / 3.0 : 1000.0 * std::exp((m - 15.0) * std::log(6.4) / 27.0);
+  };
+  const double top = hz2mel(8000.0);
+  double edge[130];
+  for (int i = 0; i < 130; ++i) edge[i] = mel2hz(top * i / 129.0);
+  fstart.assign(128, 0);
+  flen.assign(128, 0);
+  fw.assign(128 * 16, 0.0f);
+  for (int m = 0; m < 128; ++m) {
+    const double lo = edge[m], ce = edge[m + 1], hi = edge[m + 2];
+    const double norm = 2.0 / (hi - lo);
+    int first = -1, cnt = 0;
+    for (int k = 0; k <= 200; ++k) {
+      const double f = 40.0 * k;
+      const double v = std::max(0.0, std::min((f - lo) / (ce - lo), (hi - f) / (hi - ce))) * norm;
+      if (v > 0.0) {
+        if (first < 0) first = k;
+        const int j = k - first;
+        if (j < 16) fw[m * 16 + j] = (float)v;
+        cnt = j + 1;
+      }
+    }
+    fstart[m] = first < 0 ? 0 : first;
+    flen[m] = std::min(cnt, 16);
+  }
+}
+
+static std::vector<float> pe_table(int W, int d) {
+  std::vector<float> pe((size_t)W * d);
+  const int h = d / 2;
+  for (int p = 0; p < W; ++p)
+    for (int i = 0; i < h; ++i) {
+      const double om = std::exp(-std::log(10000.0) * i / (double)(h - 1));
+      pe[(size_t)p * d + i] = (float)std::sin(p * om);
+      pe[(size_t)p * d + h + i] = (float)std::cos(p * om);
+    }
+  return pe;
+}
+
+template <class F>
+static void parallel_for(int64_t n, F fn) {
+  const int nt = (int)std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  if (n < (1 << 20) || nt == 1) {
+    fn(0, n);
+    return;
+  }
+  std::vector<std::thread> th;
+  const int64_t step = (n + nt - 1) / nt;
+  for (int t = 0; t < nt; ++t) {
+    const int64_t a = t * step, b = std::min(n, a + step);
+    if (a < b) th.emplace_back([=] { fn(a, b); });
+  }
+  for (auto& x : th) x.join();
+}
+
+}  // namespace ae
+
+using namespace ae;
+
+// ------------------------------------------------------------------------------------------
+// handle
+// ------------------------------------------------------------------------------------------
+struct LayerW {
+  void *wqkv, *wo, *w1, *w2;
+  float *bqkv, *bo, *b1, *b2, *ln1g, *ln1b, *ln2g, *ln2b;
+};
+
+struct TimedLaunch { int kid; hipEvent_t a, b; };
+
+struct encoder {
+  encoder_cfg cfg;
+  int device = 0;
+  bool bf16 = true;
+  size_t esz = 2;
+  // packed parameters
+  void* wdev = nullptr;   // dtype weights
+  float* fdev = nullptr;  // float32 parameters and tables
+  int64_t wbytes = 0, fbytes = 0;
+  float *conv1_w, *conv1_b, *conv2_b, *conv3_b;
+  void *conv2_w, *conv3_w, *conv_out_w;
+  std::vector<LayerW> layers;
+  float *lnp_g, *lnp_b, *proj1_b, *proj2_b;
+  void *proj1_w, *proj2_w, *gateup_w, *down_w;
+  float* pe;
+  MelTables mel;
+  // workspace (grown on demand)
+  struct Buf { void* p = nullptr; int64_t bytes = 0; };
+  Buf mel_raw, max_key, wtab, tpos, act1, act2, tokA, resid, xn, qkv, attn, hid, hid2, z, dbg;
+  int64_t ws_bytes = 0, ws_peak = 0;
+  // host staging for the plan upload
+  void* pinned = nullptr;
+  int64_t pinned_bytes = 0;
+  hipEvent_t upload_done = nullptr;
+  // timing
+  bool timing = false;
+  std::vector<TimedLaunch> timed;
+  std::vector<hipEvent_t> event_pool;
+  size_t event_next = 0;
+};
+
+namespace {
+
+encoder_status ensure(encoder* e, encoder::Buf& b, int64_t bytes) {
+  if (b.bytes >= bytes) return ENC_OK;
+  if (b.p) {
+    AE_HIP(hipDeviceSynchronize());  // the old buffer may still be read by queued work
+    AE_HIP(hipFree(b.p));
+    e->ws_bytes -= b.bytes;
+    b.p = nullptr;
+    b.bytes = 0;
+  }
+  const int64_t want = (bytes + 4095) & ~int64_t(4095);
+  if (getenv("ENCODER_FAIL_ALLOC")) {
+    set_error("allocation refused (ENCODER_FAIL_ALLOC is set)");
+    return ENC_E_OUT_OF_MEMORY;
+  }
+  hipError_t err = hipMalloc(&b.p, want);
+  if (err != hipSuccess) {
+    b.p = nullptr;
+    return hip_fail(err, "hipMalloc(workspace)");
+  }
+  b.bytes = want;
+  e->ws_bytes += want;
+  e->ws_peak = std::max(e->ws_peak, e->ws_bytes);
+  return ENC_OK;
+}
+
+hipEvent_t next_event(encoder* e) {
+  if (e->event_next == e->event_pool.size()) {
+    hipEvent_t ev;
+    if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+    e->event_pool.push_back(ev);
+  }
+  return e->event_pool[e->event_next++];
+}
+
+// brackets one launch with events when timing is on
+struct Tm {
+  encoder* e;
+  int kid;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  Tm(encoder* e_, int k, hipStream_t s_) : e(e_), kid(k), s(s_) {
+    if (e->timing && (a = next_event(e))) hipEventRecord(a, s);
+  }
+  ~Tm() {
+    if (!a) return;
+    hipEvent_t b = next_event(e);
+    if (!b) return;
+    hipEventRecord(b, s);
+    e->timed.push_back({kid, a, b});
+  }
+};
+
+#define LAUNCH(kid, call)                              \
+  do {                                                 \
+    hipError_t _err;                                   \
+    {                                                  \
+      Tm _tm(e, kid, s);                               \
+      _err = (call);                                   \
+    }                                                  \
+    if (_err != hipSuccess) return hip_fail(_err, #call); \
+  } while (0)
+
+// workspace for passes of up to mt tokens / mw windows, and a log-mel of nclip x T frames
+encoder_status size_workspace(encoder* e, int64_t nclip, int64_t T, int64_t mt, int64_t mw,
+                              int64_t n_win_total, int64_t n_tok_total) {
+  const encoder_cfg& c = e->cfg;
+  const int64_t es = (int64_t)e->esz, C = c.conv_channels, W = c.window_tokens, d = c.d_model;
+  encoder_status st;
+  if ((st = ensure(e, e->mel_raw, nclip * T * 128 * 4))) return st;
+  if ((st = ensure(e, e->max_key, std::max<int64_t>(nclip, 1) * 4))) return st;
+  if ((st = ensure(e, e->wtab, n_win_total * (int64_t)sizeof(Win)))) return st;
+  if ((st = ensure(e, e->tpos, std::max<int64_t>(n_tok_total, 1) * 4))) return st;
+  if ((st = ensure(e, e->act1, mw * 4 * W * 64 * C * es))) return st;
+  if ((st = ensure(e, e->act2, mw * 2 * W * 32 * C * es))) return st;
+  if ((st = ensure(e, e->tokA, mt * 16 * C * es))) return st;
+  if ((st = ensure(e, e->resid, mt * d * 4))) return st;
+  if ((st = ensure(e, e->xn, mt * d * es))) return st;
+  if ((st = ensure(e, e->qkv, mt * 3 * d * es))) return st;
+  if ((st = ensure(e, e->attn, mt * d * es))) return st;
+  const int64_t hidw = std::max<int64_t>({c.d_ffn, d, c.d_adapter});
+  if ((st = ensure(e, e->hid, mt * hidw * es))) return st;
+  if (!e->bf16 && (st = ensure(e, e->hid2, mt * 2 * c.d_adapter * es))) return st;
+  if ((st = ensure(e, e->z, mt * c.d_out * es))) return st;
+  return ENC_OK;
+}
+
+// plan + per-pass relative token indices, uploaded once per call
+encoder_status upload_plan(encoder* e, const std::vector<Win>& wins, const std::vector<Pass>& ps,
+                           hipStream_t s) {
+  std::vector<Win> rel(wins);
+  int64_t ntok = 0;
+  for (const Pass& p : ps) ntok += p.ntok;
+  std::vector<int32_t> tp((size_t)ntok);
+  for (const Pass& p : ps)
+    for (int64_t i = p.win0; i < p.win0 + p.nwin; ++i) {
+      rel[i].tok = (int32_t)(wins[i].tok - p.tok0);
+      for (int j = 0; j < wins[i].L3; ++j) tp[wins[i].tok + j] = j;
+    }
+  const int64_t wb = (int64_t)rel.size() * (int64_t)sizeof(Win), tb = ntok * 4;
+  if (e->pinned_bytes < wb + tb) {
+    if (e->pinned) {
+      AE_HIP(hipEventSynchronize(e->upload_done));
+      AE_HIP(hipHostFree(e->pinned));
+      e->pinned = nullptr;
+      e->pinned_bytes = 0;
+    }
+    AE_HIP(hipHostMalloc(&e->pinned, wb + tb, hipHostMallocDefault));
+    e->pinned_bytes = wb + tb;
+  }
+  AE_HIP(hipEventSynchronize(e->upload_done));  // the previous upload has left the staging area
+  std::memcpy(e->pinned, rel.data(), wb);
+  std::memcpy((char*)e->pinned + wb, tp.data(), tb);
+  AE_HIP(hipMemcpyAsync(e->wtab.p, e->pinned, wb, hipMemcpyHostToDevice, s));
+  AE_HIP(hipMemcpyAsync(e->tpos.p, (char*)e->pinned + wb, tb, hipMemcpyHostToDevice, s));
+  AE_HIP(hipEventRecord(e->upload_done, s));
+  return ENC_OK;
+}
+
+template <typename T>
+encoder_status launch_linear_t(encoder* e, int kid, const void* A, int64_t lda, const void* Wt,
+                               const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
+                               int epi, hipStream_t s, const float* pe = nullptr,
+                               const int32_t* tok_pos = nullptr) {
+  LinearArgs a{A, lda, Wt, bias, C, ldc, M, N, K, pe, tok_pos};
+  LAUNCH(kid, launch_linear<T>(a, epi, kid, s));
+  return ENC_OK;
+}
+
+// stage ids of encoder_debug_stage
+enum { ST_MEL = 0, ST_CONV1, ST_CONV2, ST_CONV3, ST_EMBED, ST_LAYER, ST_HEAD, ST_OUT };
+
+// One pass over windows [p.win0, p.win0 + p.nwin): conv stack -> ... -> adapter, writing
+// rows [p.tok0, p.tok0 + p.ntok) of `out`.  Stops after `stop` (debug) when stop >= 0.
+template <typename T>
+encoder_status run_pass(encoder* e, const Pass& p, int64_t T_frames, void* out, hipStream_t s,
+                        int stop = -1, int stop_layer = -1) {
+  const encoder_cfg& c = e->cfg;
+  const int C = c.conv_channels, d = c.d_model, W = c.window_tokens;
+  PassGeom g;
+  g.wins = reinterpret_cast<const Win*>(e->wtab.p) + p.win0;
+  g.n_win = (int32_t)p.nwin;
+  g.W = W;
+  g.n_tok = p.ntok;
+  g.tok_pos = reinterpret_cast<const int32_t*>(e->tpos.p) + p.tok0;
+  const int64_t M = p.ntok;
+  T* act1 = (T*)e->act1.p;
+  T* act2 = (T*)e->act2.p;
+  T* tokA = (T*)e->tokA.p;
+  float* resid = (float*)e->resid.p;
+  T* xn = (T*)e->xn.p;
+  T* qkv = (T*)e->qkv.p;
+  T* attn = (T*)e->attn.p;
+  T* hid = (T*)e->hid.p;
+  T* z = (T*)e->z.p;
+
+  LAUNCH(ENC_K_CONV1, launch_conv1<T>(g, (const float*)e->mel_raw.p, T_frames,
+                                      (const uint32_t*)e->max_key.p, e->conv1_w, e->conv1_b, C,
+                                      act1, s));
+  if (stop == ST_CONV1) return ENC_OK;
+  LAUNCH(ENC_K_CONV2, launch_conv_igemm<T>(g, 2, act1, (const T*)e->conv2_w, e->conv2_b, C, act2, s));
+  if (stop == ST_CONV2) return ENC_OK;
+  LAUNCH(ENC_K_CONV3, launch_conv_igemm<T>(g, 3, act2, (const T*)e->conv3_w, e->conv3_b, C, tokA, s));
+  if (stop == ST_CONV3) return ENC_OK;
+  encoder_status st;
+  if ((st = launch_linear_t<T>(e, ENC_K_CONV_OUT, tokA, 16 * C, e->conv_out_w, nullptr, resid, d, M,
+                               d, 16 * C, EPI_PE, s, e->pe, g.tok_pos)))
+    return st;
+  if (stop == ST_EMBED) return ENC_OK;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = e->layers[l];
+    LAUNCH(ENC_K_LN, launch_layernorm<T>(resid, L.ln1g, L.ln1b, xn, M, d, c.ln_eps, s));
+    if ((st = launch_linear_t<T>(e, ENC_K_QKV, xn, d, L.wqkv, L.bqkv, qkv, 3 * d, M, 3 * d, d,
+                                 EPI_BIAS, s)))
+      return st;
+    LAUNCH(ENC_K_ATTN, launch_attention<T>(qkv, g.wins, nullptr, g.n_win, c.n_heads, d, attn, s));
+    if ((st = launch_linear_t<T>(e, ENC_K_OPROJ, attn, d, L.wo, L.bo, resid, d, M, d, d, EPI_RESADD, s)))
+      return st;
+    LAUNCH(ENC_K_LN, launch_layernorm<T>(resid, L.ln2g, L.ln2b, xn, M, d, c.ln_eps, s));
+    if ((st = launch_linear_t<T>(e, ENC_K_FFN1, xn, d, L.w1, L.b1, hid, c.d_ffn, M, c.d_ffn, d,
+                                 EPI_BIAS_GELU, s)))
+      return st;
+    if ((st = launch_linear_t<T>(e, ENC_K_FFN2, hid, c.d_ffn, L.w2, L.b2, resid, d, M, d, c.d_ffn,
+                                 EPI_RESADD, s)))
+      return st;
+    if (stop == ST_LAYER && stop_layer == l) return ENC_OK;
+  }
+  LAUNCH(ENC_K_LN, launch_layernorm<T>(resid, e->lnp_g, e->lnp_b, xn, M, d, c.ln_eps, s));
+  if ((st = launch_linear_t<T>(e, ENC_K_PROJ1, xn, d, e->proj1_w, e->proj1_b, hid, d, M, d, d,
+                               EPI_BIAS_GELU, s)))
+    return st;
+  if ((st = launch_linear_t<T>(e, ENC_K_PROJ2, hid, d, e->proj2_w, e->proj2_b, z, c.d_out, M,
+                               c.d_out, d, EPI_BIAS, s)))
+    return st;
+  if (stop == ST_HEAD) return ENC_OK;
+  const int da = c.d_adapter;
+  if (e->bf16) {
+    if ((st = launch_linear_t<T>(e, ENC_K_GATE_UP, z, c.d_out, e->gateup_w, nullptr, hid, da, M,
+                                 2 * da, c.d_out, EPI_SWIGLU, s)))
+      return st;
+  } else {
+    T* hid2 = (T*)e->hid2.p;
+    if ((st = launch_linear_t<T>(e, ENC_K_GATE_UP, z, c.d_out, e->gateup_w, nullptr, hid2, 2 * da,
+                                 M, 2 * da, c.d_out, EPI_BIAS, s)))
+      return st;
+    LAUNCH(ENC_K_OTHER, launch_swiglu_split<T>(hid2, M, 2 * da, hid, s));
+  }
+  T* dst = (T*)out + p.tok0 * c.d_out;
+  if ((st = launch_linear_t<T>(e, ENC_K_DOWN, hid, da, e->down_w, nullptr, dst, c.d_out, M, c.d_out,
+                               da, EPI_BIAS, s)))
+    return st;
+  return ENC_OK;
+}
+
+// log-mel of [nclip, n_samples] into mel_raw + max keys
+encoder_status run_mel(encoder* e, const float* pcm, int64_t n_samples, int32_t nclip,
+                       hipStream_t s) {
+  LAUNCH(ENC_K_OTHER, launch_clear_u32((uint32_t*)e->max_key.p, nclip, s));
+  LAUNCH(ENC_K_MEL, launch_log_mel(pcm, n_samples, nclip, e->mel, (float*)e->mel_raw.p,
+                                   (uint32_t*)e->max_key.p, s));
+  return ENC_OK;
+}
+
+encoder_status check_forward_args(encoder* e, const void* pcm, int64_t n_samples, int32_t batch,
+                                  const void* out) {
+  if (!e) return invalid("encoder handle is NULL");
+  if (!pcm || !out) return invalid("pcm and output pointers must be non-NULL");
+  if (batch < 1) return invalid("batch must be >= 1");
+  if (n_samples <= e->cfg.n_fft / 2)
+    return invalid("n_samples must exceed n_fft/2 = 200 (reflect padding)");
+  if (n_samples / e->cfg.hop >= (int64_t(1) << 30)) return invalid("clip too long");
+  if ((int64_t)batch * frames_out(e->cfg, n_samples) >= (int64_t(1) << 31))
+    return invalid("too many output frames for one call");
+  return ENC_OK;
+}
+
+encoder_status forward_impl(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+                            void* out, hipStream_t s, int64_t piece_windows, int stop = -1,
+                            int stop_layer = -1, float* dst = nullptr, int64_t dst_elems = 0) {
+  AE_HIP(hipSetDevice(e->device));
+  const encoder_cfg& c = e->cfg;
+  std::vector<Win> wins;
+  plan_windows(c, n_samples, batch, wins);
+  const int64_t mt = max_tokens(c), mw = max_windows(c);
+  std::vector<Pass> ps = split_passes(wins, mt, mw, [&](int64_t i) {
+    return piece_windows > 0 && i % piece_windows == 0;
+  });
+  if (stop >= 0 && ps.size() > 1) return invalid("debug stages need a single pass");
+  const int64_t T = n_samples / c.hop;
+  int64_t ntok = 0;
+  for (auto& p : ps) ntok += p.ntok;
+  encoder_status st = size_workspace(e, batch, T, mt, mw, (int64_t)wins.size(), ntok);
+  if (st) return st;
+  if ((st = upload_plan(e, wins, ps, s))) return st;
+  if ((st = run_mel(e, pcm, n_samples, batch, s))) return st;
+  if (stop == ST_MEL) {
+    LAUNCH(ENC_K_OTHER, launch_mel_normalize((const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
+                                             T, batch, dst, s));
+    return ENC_OK;
+  }
+  for (const Pass& p : ps) {
+    if (e->bf16) st = run_pass<bf16_t>(e, p, T, out, s, stop, stop_layer);
+    else st = run_pass<float>(e, p, T, out, s, stop, stop_layer);
+    if (st) return st;
+  }
+  if (stop >= 0) {
+    const Pass& p = ps[0];
+    const int64_t W = c.window_tokens, C = c.conv_channels;
+    const void* src = nullptr;
+    int64_t n = 0;
+    switch (stop) {
+      case ST_CONV1: src = e->act1.p; n = p.nwin * 4 * W * 64 * C; break;
+      case ST_CONV2: src = e->act2.p; n = p.nwin * 2 * W * 32 * C; break;
+      case ST_CONV3: src = e->tokA.p; n = p.ntok * 16 * C; break;
+      case ST_EMBED:
+      case ST_LAYER:
+        if (dst_elems < p.ntok * c.d_model) return invalid("dst too small for this stage");
+        AE_HIP(hipMemcpyAsync(dst, e->resid.p, p.ntok * c.d_model * 4, hipMemcpyDeviceToDevice, s));
+        return ENC_OK;
+      case ST_HEAD: src = e->z.p; n = p.ntok * c.d_out; break;
+      case ST_OUT: src = out; n = p.ntok * c.d_out; break;
+      default: return invalid("unknown stage");
+    }
+    if (dst_elems < n) return invalid("dst too small for this stage");
+    if (e->bf16) LAUNCH(ENC_K_OTHER, launch_to_f32<bf16_t>((const bf16_t*)src, n, dst, s));
+    else LAUNCH(ENC_K_OTHER, launch_to_f32<float>((const float*)src, n, dst, s));
+  }
+  return ENC_OK;
+}
+
+void free_all(encoder* e) {
+  if (!e) return;
+  hipSetDevice(e->device);
+  hipDeviceSynchronize();
+  encoder::Buf* bufs[] = {&e->mel_raw, &e->max_key, &e->wtab, &e->tpos, &e->act1, &e->act2,
+                          &e->tokA, &e->resid, &e->xn, &e->qkv, &e->attn, &e->hid, &e->hid2,
+                          &e->z, &e->dbg};
+  for (auto* b : bufs)
+    if (b->p) hipFree(b->p);
+  if (e->wdev) hipFree(e->wdev);
+  if (e->fdev) hipFree(e->fdev);
+  if (e->pinned) hipHostFree(e->pinned);
+  if (e->upload_done) hipEventDestroy(e->upload_done);
+  for (auto ev : e->event_pool) hipEventDestroy(ev);
+  delete e;
+}
+
+}  // namespace
+
+// ==========================================================================================
+// C ABI
+// ==========================================================================================
+extern "C" {
+
+const char* encoder_last_error(void) { return g_err.c_str(); }
+
+encoder_status encoder_validate_cfg(const encoder_cfg* cfg) { return check_cfg(cfg); }
+
+encoder_status encoder_weight_count(const encoder_cfg* cfg, int64_t* n_floats) {
+  encoder_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!n_floats) return invalid("n_floats is NULL");
+  int64_t n = 0;
+  for (int64_t v : blob_sizes(*cfg)) n += v;
+  *n_floats = n;
+  return ENC_OK;
+}
+
+encoder_status encoder_output_frames(const encoder_cfg* cfg, int64_t n_samples, int64_t* n_frames) {
+  encoder_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!n_frames) return invalid("n_frames is NULL");
+  if (n_samples <= cfg->n_fft / 2) return invalid("n_samples must exceed n_fft/2 = 200");
+  *n_frames = frames_out(*cfg, n_samples);
+  return ENC_OK;
+}
+
+encoder_status encoder_plan_windows(const encoder_cfg* cfg, int64_t n_samples, int32_t batch,
+                                    int32_t* table, int32_t max_windows, int32_t* n_windows) {
+  encoder_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!n_windows) return invalid("n_windows is NULL");
+  if (batch < 1) return invalid("batch must be >= 1");
+  if (n_samples <= cfg->n_fft / 2) return invalid("n_samples must exceed n_fft/2 = 200");
+  if (max_windows > 0 && !table) return invalid("table is NULL");
+  std::vector<Win> w;
+  plan_windows(*cfg, n_samples, batch, w);
+  *n_windows = (int32_t)w.size();
+  for (int32_t i = 0; i < std::min<int32_t>(max_windows, (int32_t)w.size()); ++i) {
+    int32_t* r = table + 7 * (int64_t)i;
+    r[0] = w[i].clip; r[1] = w[i].start; r[2] = w[i].L0; r[3] = w[i].L1;
+    r[4] = w[i].L2; r[5] = w[i].L3; r[6] = w[i].tok;
+  }
+  return ENC_OK;
+}
+
+encoder_status encoder_create(const float* weights, int64_t n_floats, const encoder_cfg* cfg,
+                              encoder** out) {
+  encoder_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!weights || !out) return invalid("weights and out must be non-NULL");
+  const encoder_cfg& c = *cfg;
+  const std::vector<int64_t> sizes = blob_sizes(c);
+  int64_t need = 0;
+  for (int64_t v : sizes) need += v;
+  if (n_floats != need)
+    return invalid("weight blob has " + std::to_string(n_floats) + " floats, config needs " +
+                   std::to_string(need));
+  if (getenv("ENCODER_FAIL_ALLOC")) {
+    set_error("allocation refused (ENCODER_FAIL_ALLOC is set)");
+    return ENC_E_OUT_OF_MEMORY;
+  }
+  int dev = 0;
+  AE_HIP(hipGetDevice(&dev));
+
+  encoder* e = new encoder();
+  e->cfg = c;
+  if (e->cfg.max_tokens_per_pass == 0) e->cfg.max_tokens_per_pass = 8192;
+  e->device = dev;
+  e->bf16 = c.dtype == ENC_BF16;
+  e->esz = e->bf16 ? 2 : 4;
+
+  const int64_t C = c.conv_channels, d = c.d_model, F = c.d_ffn, O = c.d_out, A = c.d_adapter;
+  const int W = c.window_tokens;
+  // blob offsets
+  std::vector<const float*> src;
+  {
+    const float* p = weights;
+    for (int64_t v : sizes) {
+      src.push_back(p);
+      p += v;
+    }
+  }
+  // ---- layout of the dtype weight buffer (element offsets, 128-element aligned)
+  int64_t woff = 0;
+  auto wslot = [&](int64_t n) {
+    const int64_t o = woff;
+    woff += (n + 127) & ~int64_t(127);
+    return o;
+  };
+  const int64_t o_conv2 = wslot(C * 9 * C), o_conv3 = wslot(C * 9 * C), o_co = wslot(d * 16 * C);
+  std::vector<int64_t> o_qkv, o_o, o_1, o_2;
+  for (int l = 0; l < c.n_layers; ++l) {
+    o_qkv.push_back(wslot(3 * d * d));
+    o_o.push_back(wslot(d * d));
+    o_1.push_back(wslot(F * d));
+    o_2.push_back(wslot(d * F));
+  }
+  const int64_t o_p1 = wslot(d * d), o_p2 = wslot(O * d), o_gu = wslot(2 * A * O), o_dn = wslot(O * A);
+  // ---- float32 parameter buffer
+  int64_t foff = 0;
+  auto fslot = [&](int64_t n) {
+    const int64_t o = foff;
+    foff += (n + 63) & ~int64_t(63);
+    return o;
+  };
+  const int64_t f_c1w = fslot(C * 9), f_c1b = fslot(C), f_c2b = fslot(C), f_c3b = fslot(C);
+  std::vector<int64_t> f_bqkv, f_bo, f_b1, f_b2, f_l1g, f_l1b, f_l2g, f_l2b;
+  for (int l = 0; l < c.n_layers; ++l) {
+    f_bqkv.push_back(fslot(3 * d));
+    f_bo.push_back(fslot(d));
+    f_b1.push_back(fslot(F));
+    f_b2.push_back(fslot(d));
+    f_l1g.push_back(fslot(d));
+    f_l1b.push_back(fslot(d));
+    f_l2g.push_back(fslot(d));
+    f_l2b.push_back(fslot(d));
+  }
+  const int64_t f_lpg = fslot(d), f_lpb = fslot(d), f_p1b = fslot(d), f_p2b = fslot(O);
+  const int64_t f_pe = fslot((int64_t)W * d), f_tw = fslot(800), f_win = fslot(400);
+  const int64_t f_fbw = fslot(128 * 16), f_fbs = fslot(128), f_fbl = fslot(128);
+
+  std::vector<float> fh((size_t)foff, 0.0f);
+  const size_t es = e->esz;
+  std::vector<uint8_t> wh((size_t)(woff * (int64_t)es));
+  auto put = [&](int64_t dst_el, int64_t idx, float v) {
+    if (es == 2) reinterpret_cast<bf16_t*>(wh.data())[dst_el + idx] = f32_to_bf16(v);
+    else reinterpret_cast<float*>(wh.data())[dst_el + idx] = v;
+  };
+  auto copy_plain = [&](int64_t dst_el, const float* s, int64_t n) {
+    parallel_for(n, [&](int64_t a, int64_t b) {
+      for (int64_t i = a; i < b; ++i) put(dst_el, i, s[i]);
+    });
+  };
+  auto fcopy = [&](int64_t dst_el, const float* s, int64_t n) {
+    std::memcpy(fh.data() + dst_el, s, n * sizeof(float));
+  };
+  // conv1: [C][9] float32 as stored
+  fcopy(f_c1w, src[0], C * 9);
+  fcopy(f_c1b, src[1], C);
+  // conv2/conv3: [co][ci][a][b] -> [co][a*3+b][ci]
+  for (int which = 0; which < 2; ++which) {
+    const float* s = src[2 + 2 * which];
+    const int64_t o = which == 0 ? o_conv2 : o_conv3;
+    parallel_for(C, [&](int64_t a0, int64_t a1) {
+      for (int64_t co = a0; co < a1; ++co)
+        for (int64_t ci = 0; ci < C; ++ci)
+          for (int t = 0; t < 9; ++t) put(o, (co * 9 + t) * C + ci, s[(co * C + ci) * 9 + t]);
+    });
+    fcopy(which == 0 ? f_c2b : f_c3b, src[3 + 2 * which], C);
+  }
+  // conv_out: column c*16+f -> f*C+c
+  parallel_for(d, [&](int64_t a0, int64_t a1) {
+    for (int64_t n = a0; n < a1; ++n)
+      for (int64_t ch = 0; ch < C; ++ch)
+        for (int f = 0; f < 16; ++f) put(o_co, n * 16 * C + f * C + ch, src[6][n * 16 * C + ch * 16 + f]);
+  });
+  for (int l = 0; l < c.n_layers; ++l) {
+    const float* const* s = src.data() + 7 + 16 * l;
+    // s: ln1g ln1b qw qb kw kb vw vb ow ob ln2g ln2b fc1w fc1b fc2w fc2b
+    fcopy(f_l1g[l], s[0], d);
+    fcopy(f_l1b[l], s[1], d);
+    copy_plain(o_qkv[l], s[2], d * d);
+    copy_plain(o_qkv[l] + d * d, s[4], d * d);
+    copy_plain(o_qkv[l] + 2 * d * d, s[6], d * d);
+    fcopy(f_bqkv[l], s[3], d);
+    fcopy(f_bqkv[l] + d, s[5], d);
+    fcopy(f_bqkv[l] + 2 * d, s[7], d);
+    copy_plain(o_o[l], s[8], d * d);
+    fcopy(f_bo[l], s[9], d);
+    fcopy(f_l2g[l], s[10], d);
+    fcopy(f_l2b[l], s[11], d);
+    copy_plain(o_1[l], s[12], F * d);
+    fcopy(f_b1[l], s[13], F);
+    copy_plain(o_2[l], s[14], d * F);
+    fcopy(f_b2[l], s[15], d);
+  }
+  const float* const* h = src.data() + 7 + 16 * c.n_layers;
+  // h: lnpg lnpb p1w p1b p2w p2b gate up down
+  fcopy(f_lpg, h[0], d);
+  fcopy(f_lpb, h[1], d);
+  copy_plain(o_p1, h[2], d * d);
+  fcopy(f_p1b, h[3], d);
+  copy_plain(o_p2, h[4], O * d);
+  fcopy(f_p2b, h[5], O);
+  // gate/up interleaved in groups of 32 rows: [gate 32 | up 32] per 64 rows
+  parallel_for(A, [&](int64_t a0, int64_t a1) {
+    for (int64_t j = a0; j < a1; ++j) {
+      const int64_t rg = 64 * (j / 32) + (j % 32);
+      for (int64_t k = 0; k < O; ++k) {
+        put(o_gu, rg * O + k, h[6][j * O + k]);
+        put(o_gu, (rg + 32) * O + k, h[7][j * O + k]);
+      }
+    }
+  });
+  copy_plain(o_dn, h[8], O * A);
+  // tables
+  {
+    std::vector<float> pe = pe_table(W, (int)d);
+    fcopy(f_pe, pe.data(), (int64_t)pe.size());
+    std::vector<float> tw, wn, fw;
+    std::vector<int32_t> fs, fl;
+    mel_host_tables(tw, wn, fs, fl, fw);
+    fcopy(f_tw, tw.data(), 800);
+    fcopy(f_win, wn.data(), 400);
+    fcopy(f_fbw, fw.data(), 128 * 16);
+    std::memcpy(fh.data() + f_fbs, fs.data(), 128 * 4);
+    std::memcpy(fh.data() + f_fbl, fl.data(), 128 * 4);
+  }
+
+  hipError_t err = hipMalloc(&e->wdev, woff * (int64_t)es);
+  if (err == hipSuccess) err = hipMalloc((void**)&e->fdev, foff * 4);
+  if (err == hipSuccess) err = hipMemcpy(e->wdev, wh.data(), woff * (int64_t)es, hipMemcpyHostToDevice);
+  if (err == hipSuccess) err = hipMemcpy(e->fdev, fh.data(), foff * 4, hipMemcpyHostToDevice);
+  if (err == hipSuccess) err = hipEventCreateWithFlags(&e->upload_done, hipEventDisableTiming);
+  if (err == hipSuccess) err = hipEventRecord(e->upload_done, nullptr);
+  if (err != hipSuccess) {
+    encoder_status r = hip_fail(err, "encoder_create");
+    free_all(e);
+    return r;
+  }
+  e->wbytes = woff * (int64_t)es;
+  e->fbytes = foff * 4;
+  auto W_ = [&](int64_t o) { return (void*)((uint8_t*)e->wdev + o * (int64_t)es); };
+  auto F_ = [&](int64_t o) { return e->fdev + o; };
+  e->conv1_w = F_(f_c1w); e->conv1_b = F_(f_c1b); e->conv2_b = F_(f_c2b); e->conv3_b = F_(f_c3b);
+  e->conv2_w = W_(o_conv2); e->conv3_w = W_(o_conv3); e->conv_out_w = W_(o_co);
+  for (int l = 0; l < c.n_layers; ++l) {
+    LayerW L;
+    L.wqkv = W_(o_qkv[l]); L.wo = W_(o_o[l]); L.w1 = W_(o_1[l]); L.w2 = W_(o_2[l]);
+    L.bqkv = F_(f_bqkv[l]); L.bo = F_(f_bo[l]); L.b1 = F_(f_b1[l]); L.b2 = F_(f_b2[l]);
+    L.ln1g = F_(f_l1g[l]); L.ln1b = F_(f_l1b[l]); L.ln2g = F_(f_l2g[l]); L.ln2b = F_(f_l2b[l]);
+    e->layers.push_back(L);
+  }
+  e->lnp_g = F_(f_lpg); e->lnp_b = F_(f_lpb); e->proj1_b = F_(f_p1b); e->proj2_b = F_(f_p2b);
+  e->proj1_w = W_(o_p1); e->proj2_w = W_(o_p2); e->gateup_w = W_(o_gu); e->down_w = W_(o_dn);
+  e->pe = F_(f_pe);
+  e->mel.twiddle = F_(f_tw);
+  e->mel.window = F_(f_win);
+  e->mel.fb_w = F_(f_fbw);
+  e->mel.fb_start = reinterpret_cast<const int32_t*>(F_(f_fbs));
+  e->mel.fb_len = reinterpret_cast<const int32_t*>(F_(f_fbl));
+  *out = e;
+  return ENC_OK;
+}
+
+void encoder_destroy(encoder* e) { free_all(e); }
+
+encoder_status encoder_memory_stats(const encoder* e, int64_t* weight_bytes, int64_t* workspace_bytes) {
+  if (!e) return invalid("encoder handle is NULL");
+  if (weight_bytes) *weight_bytes = e->wbytes + e->fbytes;
+  if (workspace_bytes) *workspace_bytes = e->ws_peak;
+  return ENC_OK;
+}
+
+encoder_status encoder_forward(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+                               void* out, void* stream) {
+  encoder_status st = check_forward_args(e, pcm, n_samples, batch, out);
+  if (st) return st;
+  return forward_impl(e, pcm, n_samples, batch, out, (hipStream_t)stream, 0);
+}
+
+encoder_status encoder_forward_long(encoder* e, const float* pcm, int64_t n_samples,
+                                    int32_t pieces_per_pass, void* out, void* stream) {
+  encoder_status st = check_forward_args(e, pcm, n_samples, 1, out);
+  if (st) return st;
+  if (pieces_per_pass < 1) return invalid("pieces_per_pass must be >= 1");
+  const int64_t pw = e->cfg.piece_tokens / e->cfg.window_tokens;  // windows per piece
+  if ((int64_t)pieces_per_pass * e->cfg.piece_tokens > max_tokens(e->cfg) ||
+      (int64_t)pieces_per_pass * pw > max_windows(e->cfg))
+    return invalid("pieces_per_pass * piece_tokens exceeds max_tokens_per_pass");
+  return forward_impl(e, pcm, n_samples, 1, out, (hipStream_t)stream, pw * pieces_per_pass);
+}
+
+encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+                               float* mel, void* stream) {
+  encoder_status st = check_forward_args(e, pcm, n_samples, batch, mel);
+  if (st) return st;
+  AE_HIP(hipSetDevice(e->device));
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t T = n_samples / e->cfg.hop;
+  if ((st = ensure(e, e->mel_raw, (int64_t)batch * T * 128 * 4))) return st;
+  if ((st = ensure(e, e->max_key, (int64_t)batch * 4))) return st;
+  if ((st = run_mel(e, pcm, n_samples, batch, s))) return st;
+  LAUNCH(ENC_K_OTHER, launch_mel_normalize((const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
+                                           T, batch, mel, s));
+  return ENC_OK;
+}
+
+encoder_status encoder_debug_stage(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+                                   int32_t stage, int32_t layer, float* dst, int64_t dst_elems,
+                                   void* stream) {
+  encoder_status st = check_forward_args(e, pcm, n_samples, batch, dst);
+  if (st) return st;
+  if (stage < ST_MEL || stage > ST_OUT) return invalid("unknown stage");
+  if (stage == ST_LAYER && (layer < 0 || layer >= e->cfg.n_layers)) return invalid("layer out of range");
+  if (stage == ST_MEL && dst_elems < (int64_t)batch * (n_samples / e->cfg.hop) * 128)
+    return invalid("dst too small for this stage");
+  const int64_t F = frames_out(e->cfg, n_samples) * batch;
+  if (F > max_tokens(e->cfg)) return invalid("debug stages need a single pass");
+  if ((st = ensure(e, e->dbg, F * e->cfg.d_out * (int64_t)e->esz))) return st;
+  return forward_impl(e, pcm, n_samples, batch, e->dbg.p, (hipStream_t)stream, 0, stage, layer,
+                      dst, dst_elems);
+}
+
+encoder_status encoder_timing_enable(encoder* e, int32_t enable) {
+  if (!e) return invalid("encoder handle is NULL");
+  e->timing = enable != 0;
+  return ENC_OK;
+}
+
+encoder_status encoder_timing_read(encoder* e, double* ms, int64_t* launches, int32_t reset) {
+  if (!e) return invalid("encoder handle is NULL");
+  AE_HIP(hipSetDevice(e->device));
+  if (ms) std::fill(ms, ms + ENC_K_COUNT, 0.0);
+  if (launches) std::fill(launches, launches + ENC_K_COUNT, int64_t(0));
+  for (const TimedLaunch& t : e->timed) {
+    AE_HIP(hipEventSynchronize(t.b));
+    float v = 0.0f;
+    AE_HIP(hipEventElapsedTime(&v, t.a, t.b));
+    if (ms) ms[t.kid] += v;
+    if (launches) launches[t.kid] += 1;
+  }
+  if (reset) {
+    e->timed.clear();
+    e->event_next = 0;
+  }
+  return ENC_OK;
+}
+
+encoder_status encoder_op_linear(const void* A, const void* W, const float* bias, void* C,
+                                 int64_t M, int32_t N, int32_t K, int32_t epi, int32_t dtype,
+                                 void* stream) {
+  if (!A || !W || !C) return invalid("A, W and C must be non-NULL");
+  if (M < 0 || N <= 0 || K <= 0 || K % 8) return invalid("need M >= 0, N > 0, K > 0, K % 8 == 0");
+  if (epi < 0 || epi > 3) return invalid("epi must be 0..3");
+  if (epi == 3 && N % 64) return invalid("SwiGLU needs N % 64 == 0");
+  if (dtype != ENC_BF16 && dtype != ENC_F32) return invalid("bad dtype");
+  hipStream_t s = (hipStream_t)stream;
+  static const int map[4] = {EPI_BIAS, EPI_BIAS_GELU, EPI_RESADD, EPI_SWIGLU};
+  const int64_t ldc = epi == 3 ? N / 2 : N;
+  LinearArgs a{A, K, W, bias, C, ldc, M, N, K, nullptr, nullptr};
+  hipError_t err;
+  if (dtype == ENC_BF16) {
+    err = launch_linear<bf16_t>(a, map[epi], ENC_K_OTHER, s);
+  } else if (epi == 3) {
+    float* tmp = nullptr;
+    AE_HIP(hipMallocAsync((void**)&tmp, M * N * 4, s));
+    LinearArgs t = a;
+    t.C = tmp;
+    t.ldc = N;
+    err = launch_linear<float>(t, EPI_BIAS, ENC_K_OTHER, s);
+    if (err == hipSuccess) err = launch_swiglu_split<float>(tmp, M, N, (float*)C, s);
+    hipFreeAsync(tmp, s);
+  } else {
+    err = launch_linear<float>(a, map[epi], ENC_K_OTHER, s);
+  }
+  if (err != hipSuccess) return hip_fail(err, "encoder_op_linear");
+  return ENC_OK;
+}
+
+encoder_status encoder_op_attention(const void* qkv, const int32_t* windows, int32_t n_windows,
+                                    int32_t n_heads, int64_t ntok, void* out, int32_t dtype,
+                                    void* stream) {
+  if (!qkv || !windows || !out) return invalid("qkv, windows and out must be non-NULL");
+  if (n_windows < 0 || n_heads <= 0 || ntok < 0) return invalid("bad sizes");
+  if (dtype != ENC_BF16 && dtype != ENC_F32) return invalid("bad dtype");
+  {
+    std::vector<int32_t> h((size_t)n_windows * 2);
+    if (n_windows) AE_HIP(hipMemcpy(h.data(), windows, h.size() * 4, hipMemcpyDeviceToHost));
+    for (int32_t i = 0; i < n_windows; ++i)
+      if (h[2 * i + 1] < 1 || h[2 * i + 1] > 128 || h[2 * i] < 0 || h[2 * i] + h[2 * i + 1] > ntok)
+        return invalid("window " + std::to_string(i) + " is empty, longer than 128 or outside ntok");
+  }
+  hipError_t err;
+  if (dtype == ENC_BF16)
+    err = launch_attention<bf16_t>((const bf16_t*)qkv, nullptr, windows, n_windows, n_heads,
+                                   n_heads * 64, (bf16_t*)out, (hipStream_t)stream);
+  else
+    err = launch_attention<float>((const float*)qkv, nullptr, windows, n_windows, n_heads,
+                                  n_heads * 64, (float*)out, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "encoder_op_attention");
+  return ENC_OK;
+}
+
+encoder_status encoder_op_layernorm(const float* x, const float* gamma, const float* beta, void* y,
+                                    int64_t M, int32_t D, float eps, int32_t dtype, void* stream) {
+  if (!x || !gamma || !beta || !y) return invalid("x, gamma, beta and y must be non-NULL");
+  if (M < 0 || D <= 0 || D % 64) return invalid("need M >= 0 and D % 64 == 0");
+  if (dtype != ENC_BF16 && dtype != ENC_F32) return invalid("bad dtype");
+  hipError_t err;
+  if (dtype == ENC_BF16)
+    err = launch_layernorm<bf16_t>(x, gamma, beta, (bf16_t*)y, M, D, eps, (hipStream_t)stream);
+  else
+    err = launch_layernorm<float>(x, gamma, beta, (float*)y, M, D, eps, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "encoder_op_layernorm");
+  return ENC_OK;
+}
+
+}  // extern "C"

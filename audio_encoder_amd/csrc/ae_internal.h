@@ -1,0 +1,144 @@
+// Internal declarations shared by the library's translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/audio_encoder.h"
+
+namespace ae {
+
+// ------------------------------------------------------------------------------------------
+// storage types
+// ------------------------------------------------------------------------------------------
+typedef uint16_t bf16_t;  // bf16 bit pattern
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__host__ __device__ inline float bf16_to_f32(bf16_t h) {
+  union { uint32_t u; float f; } c;
+  c.u = (uint32_t)h << 16;
+  return c.f;
+}
+__host__ __device__ inline bf16_t f32_to_bf16(float f) {  // round to nearest even
+  union { uint32_t u; float f; } c;
+  c.f = f;
+  if ((c.u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((c.u >> 16) | ((c.u & 0xffff) ? 0x40 : 0));
+  c.u += 0x7fffu + ((c.u >> 16) & 1u);
+  return (bf16_t)(c.u >> 16);
+}
+
+template <typename T> struct StoreT;
+template <> struct StoreT<float> {
+  __device__ static inline void put(float* p, float v) { *p = v; }
+};
+template <> struct StoreT<bf16_t> {
+  __device__ static inline void put(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+__device__ inline float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ inline float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// ------------------------------------------------------------------------------------------
+// window plan (one entry per attention window; all fields int32)
+// ------------------------------------------------------------------------------------------
+struct Win {
+  int32_t clip;   // clip (row of the log-mel buffer) the window belongs to
+  int32_t start;  // first mel frame within the clip
+  int32_t L0, L1, L2, L3;  // valid lengths: frames, after conv1, conv2, conv3 (= tokens)
+  int32_t tok;    // first token of the window within its pass
+  int32_t pad;
+};
+
+// Geometry of one pass over a group of windows.
+struct PassGeom {
+  const Win* wins;     // device, n_win entries
+  int32_t n_win;
+  int32_t W;           // window tokens; window frames = 8W, L1max = 4W, L2max = 2W, L3max = W
+  int64_t n_tok;
+  const int32_t* tok_pos;  // device, n_tok entries: position of each token within its window
+};
+
+// ------------------------------------------------------------------------------------------
+// error plumbing
+// ------------------------------------------------------------------------------------------
+void set_error(const std::string& msg);
+encoder_status hip_fail(hipError_t err, const char* what);
+
+#define AE_HIP(call)                                              \
+  do {                                                            \
+    hipError_t _e = (call);                                       \
+    if (_e != hipSuccess) return ::ae::hip_fail(_e, #call);       \
+  } while (0)
+
+// ------------------------------------------------------------------------------------------
+// kernel launchers (each returns hipSuccess or the launch error)
+// ------------------------------------------------------------------------------------------
+struct MelTables {
+  const float* twiddle;   // [400][2] cos, sin of 2*pi*j/400
+  const float* window;    // [400] periodic Hann
+  const int32_t* fb_start;  // [128] first bin of each mel filter
+  const int32_t* fb_len;    // [128] taps (<= 16)
+  const float* fb_w;        // [128][16] weights
+};
+
+// raw log10 mel of [nclip, n_samples] pcm -> mel [nclip, T, 128]; per-clip max into
+// max_key[clip] (ordered-uint encoding; must be cleared by launch_clear_u32 first)
+hipError_t launch_log_mel(const float* pcm, int64_t n_samples, int32_t nclip, const MelTables& t,
+                          float* mel, uint32_t* max_key, hipStream_t s);
+hipError_t launch_clear_u32(uint32_t* p, int64_t n, hipStream_t s);
+// normalised mel from raw + max keys (in place or out of place)
+hipError_t launch_mel_normalize(const float* raw, const uint32_t* max_key, int64_t T,
+                                int32_t nclip, float* out, hipStream_t s);
+
+// conv1: raw mel + max -> act1 [n_win][4W][64][C]
+template <typename T>
+hipError_t launch_conv1(const PassGeom& g, const float* mel, int64_t T_frames, const uint32_t* max_key,
+                        const float* w, const float* b, int32_t C, T* act1, hipStream_t s);
+
+// GEMM epilogue kinds
+enum Epi : int {
+  EPI_BIAS = 0,        // C = acc + bias (dtype)
+  EPI_BIAS_GELU = 1,   // C = gelu(acc + bias) (dtype)
+  EPI_RESADD = 2,      // Cf32 += acc + bias
+  EPI_SWIGLU = 3,      // C[:, n/2] = silu(gate) * up over 32-interleaved columns (dtype)
+  EPI_PE = 4,          // Cf32 = acc + pe[pos(row)]
+  EPI_STORE_F32 = 5    // Cf32 = acc + bias
+};
+
+struct LinearArgs {
+  const void* A; int64_t lda;
+  const void* W;            // [N, K]
+  const float* bias;        // [N] or null
+  void* C; int64_t ldc;
+  int64_t M; int32_t N; int32_t K;
+  // EPI_PE: pe table [window tokens][N] and each row's position within its window
+  const float* pe; const int32_t* tok_pos;
+};
+template <typename T>
+hipError_t launch_linear(const LinearArgs& a, int epi, int tag, hipStream_t s);
+
+// implicit-GEMM conv (conv2: level 2, conv3: level 3).  in: [n_win][Lin_max][Fin][C],
+// out: level 2 -> [n_win][2W][32][C]; level 3 -> [n_tok][16][C]
+template <typename T>
+hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T* wpk,
+                             const float* bias, int32_t C, T* out, hipStream_t s);
+
+template <typename T>
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, T* y, int64_t M,
+                            int32_t D, float eps, hipStream_t s);
+
+template <typename T>
+hipError_t launch_attention(const T* qkv, const Win* wins, const int32_t* win2, int32_t n_win,
+                            int32_t n_heads, int32_t d, T* out, hipStream_t s);
+
+template <typename T>
+hipError_t launch_swiglu_split(const T* gu, int64_t M, int32_t N2, T* out, hipStream_t s);
+
+template <typename T>
+hipError_t launch_to_f32(const T* src, int64_t n, float* dst, hipStream_t s);
+
+}  // namespace ae

@@ -66,10 +66,13 @@ def weight_count(cfg: dict) -> int:
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returned as float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    x = np.array(x, dtype=np.float32, copy=True)
+    u = x.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)  # finite values only: no carry out of the exponent
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return x
 
 
 def make_weights(cfg: dict, seed: int = 0) -> np.ndarray:

@@ -1,0 +1,223 @@
+"""Throughput of the audio-tower forward pass on one MI355X.
+
+One step = one forward pass of the whole path (log-mel -> conv stack -> 32 windowed layers ->
+head -> SwiGLU adapter) over one batch of synthetic PCM already resident in HBM.  Default
+workload: the full-size bf16 tower on 16 clips of 30 s (6000 tokens per step).
+
+Prints ONE JSON line: audio-seconds encoded per second, TFLOP/s and % of the bf16 MFMA peak,
+the roofline of the dominant kernel (timed live with HIP events on the forward's stream) and
+the float64 CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    "c2": "16 x 30 s clips (mixed pink noise / tones / chords / harmonic bursts, peak 0.5), "
+          "full-size tower, bf16",
+    "c1": "1 x 30 s clip (pink noise + harmonic bursts, peak 0.5), full-size tower, bf16",
+    "c3": "512 s stream as 8 x 64 s pieces in one pass, full-size tower, bf16",
+    "c4": "60 min recording as 57 sequential 64 s pieces, full-size tower, bf16",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def work_model(cfg: dict, n_samples: int, batch: int) -> dict:
+    """Algorithmic work per step for each kernel role: FLOPs (2 per MAC over valid positions and
+    in-window attention only) or HBM bytes for the bandwidth-bound roles."""
+    from audio_encoder_amd import binding as B
+    tab = B.encoder_plan_windows(cfg, n_samples, batch)
+    C, d, F, O, A = (cfg[k] for k in ("conv_channels", "d_model", "d_ffn", "d_out", "d_adapter"))
+    Lh = cfg["n_layers"]
+    L1, L2, L3 = (tab[:, i].astype(float) for i in (3, 4, 5))
+    ntok = L3.sum()
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    w = {
+        "conv1": 2 * (L1 * 64).sum() * C * 9,
+        "conv2": 2 * (L2 * 32).sum() * C * C * 9,
+        "conv3": 2 * (L3 * 16).sum() * C * C * 9,
+        "conv_out": 2 * ntok * d * 16 * C,
+        "qkv": 2 * ntok * 3 * d * d * Lh,
+        "attention": 2 * 2 * (L3 ** 2).sum() * d * Lh,
+        "o_proj": 2 * ntok * d * d * Lh,
+        "ffn1": 2 * ntok * F * d * Lh,
+        "ffn2": 2 * ntok * d * F * Lh,
+        "proj1": 2 * ntok * d * d,
+        "proj2": 2 * ntok * O * d,
+        "gate_up": 2 * ntok * 2 * A * O,
+        "down": 2 * ntok * O * A,
+    }
+    flops = float(sum(w.values()))
+    T = n_samples // 160
+    bytes_ = {
+        "mel": batch * (4.0 * n_samples + 512.0 * T),
+        "layernorm": (2 * Lh + 1) * ntok * d * (4 + es),
+    }
+    return {"flops": w, "total_flops": flops, "bytes": bytes_, "ntok": int(ntok)}
+
+
+def make_input(workload: str):
+    from audio_encoder_amd import synth as S
+    if workload == "c2":
+        return S.mixed_batch(range(101, 117)), 480.0
+    if workload == "c1":
+        return S.pink_plus_bursts(seed=1)[None], 30.0
+    if workload == "c3":
+        return S.long_stream_512s()[None], 512.0
+    if workload == "c4":
+        return S.hour_stream()[None], 3600.0
+    raise ValueError(workload)
+
+
+def cpu_baseline(pcm0, weights, cfg, max_windows: int = 2) -> dict:
+    """The float64 oracle on the first `max_windows` 8 s windows of clip 0 (about 10-30 s of
+    CPU work), scaled to audio-seconds per second."""
+    import numpy as np
+
+    import oracle as O
+    Wt = O.unpack_weights(weights, O.FULL)
+    t0 = time.perf_counter()
+    mel = O.log_mel(pcm0)
+    W = cfg["window_tokens"]
+    plan = O.window_plan(mel.shape[0], W)[:max_windows]
+    frames = 0
+    for w in plan:
+        O.encode_mel(mel[w["start"]:w["start"] + w["L0"]], Wt, O.FULL)
+        frames += w["L0"]
+    dt = time.perf_counter() - t0
+    audio_s = frames * 160 / 16000.0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": audio_s / dt, "unit": "audio-s/s", "cores": cores, "kind": "oracle",
+            "sample": f"clip 0, first {len(plan)} windows ({audio_s:.0f} s of audio), "
+                      f"float64 NumPy, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roofline-steps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); windows are independent, "
+              "so several GPUs would each run this same step on their own share of clips.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from audio_encoder_amd import binding as B
+    from audio_encoder_amd import synth as S
+
+    cfg = dict(B.FULL)
+    log("generating weights and input")
+    weights = S.make_weights(cfg, seed=0)
+    pcm_np, audio_s = make_input(args.workload)
+    enc = B.Encoder(weights, cfg)
+    pcm = torch.from_numpy(pcm_np).cuda()
+    n_samples = pcm.shape[1]
+    long_mode = args.workload in ("c3", "c4")
+    ppp = 8 if args.workload == "c3" else 1
+    wm = work_model(cfg, n_samples, pcm.shape[0])
+    F = enc.output_frames(n_samples)
+    out = torch.empty((pcm.shape[0], F, cfg["d_out"]), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        if long_mode:
+            enc.forward_long(pcm[0], pieces_per_pass=ppp, out=out[0])
+        else:
+            enc.forward(pcm, out=out)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = wm["total_flops"] / (ms * 1e-3) / 1e12
+    log(f"{ms:.3f} ms/step, {audio_s / (ms * 1e-3):.0f} audio-s/s, {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak); wall {t_wall:.2f} s")
+
+    # per-kernel timing on the forward's own stream
+    enc.timing_enable(True)
+    enc.timing_read(reset=True)
+    for _ in range(args.roofline_steps):
+        step()
+    tm = enc.timing_read(reset=True)
+    enc.timing_enable(False)
+    R = args.roofline_steps
+    stage_ms = {k: round(v[0] / R, 4) for k, v in tm.items() if v[1]}
+    dom = max((k for k in tm if k in wm["flops"]), key=lambda k: tm[k][0])
+    dom_ms, dom_n = tm[dom]
+    avg_ms = dom_ms / dom_n
+    per_launch = wm["flops"][dom] / (dom_n / R)
+    achieved = per_launch / (avg_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "avg_launch_ms": round(avg_ms, 5), "launches_per_step": dom_n // R,
+            "traffic": None}
+    for k, v in stage_ms.items():
+        log(f"  {k:10s} {v:8.3f} ms/step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(pcm_np[0], weights, cfg)
+        log(f"oracle: {cpu['value']:.2f} audio-s/s on {cpu['cores']} cores")
+
+    wbytes, ws = enc.memory_stats()
+    line = {
+        "metric": "audio-seconds encoded/sec (bf16, 1 GPU) + % of bf16 MFMA peak",
+        "value": round(audio_s / (ms * 1e-3), 1),
+        "unit": "audio-s/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload], "clips": int(pcm.shape[0]),
+                   "samples_per_clip": int(n_samples), "tokens_per_step": wm["ntok"],
+                   "audio_seconds_per_step": audio_s},
+        "tflops": round(tflops, 2),
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stage_ms": stage_ms,
+        "hbm_bytes": {"weights": wbytes, "workspace_high_water": ws},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

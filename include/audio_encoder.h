@@ -1,0 +1,203 @@
+/*
+ * audio_encoder.h - C ABI of the MI355X (gfx950) audio-tower library.
+ *
+ * The library computes the audio tower described on the "cstr/MOSS-Transcribe-preview-2B-GGUF"
+ * card (section "Architecture"): 16 kHz mono PCM -> 128-bin Whisper-style log-mel (n_fft 400,
+ * hop 160) -> 3 x Conv2D 3x3 stride 2 with GELU (1 -> C -> C -> C) -> conv_out (16*C -> d,
+ * no bias) + sinusoidal positions -> pre-LN Transformer layers with windowed (block-diagonal)
+ * self-attention -> ln_post -> proj1 -> GELU -> proj2 -> SwiGLU adapter.  It emits 12.5
+ * embeddings per second of audio ("SILVERTHRONE/Ossicle-4B" card, "Model Overview").  The
+ * long-audio entry point encodes a recording in 64 s pieces whose log-mel equals the whole-clip
+ * log-mel (Ossicle card, "Long Audio").
+ *
+ * Conventions (all readings of points the cards leave open):
+ *  - The encoder is window-local.  An attention window of W tokens covers 8*W mel frames.  Each
+ *    window is convolved with zero padding at its own time edges, and its sinusoidal positions
+ *    restart at 0.  The last window of a clip holds the remaining frames.
+ *  - The log-mel has T = n_samples / 160 frames: centred reflect-padded frames, a periodic Hann
+ *    window and the power spectrum; the trailing STFT frame is dropped (Transcribe card,
+ *    "Non-obvious gotchas", item 2).  The filterbank is Slaney-normalised.  The mel is
+ *    log10(max(., 1e-10)), clamped at (max - 8) and mapped to (x + 4) / 4.  The max runs over
+ *    one clip, or over the whole recording in long-audio mode.
+ *  - GELU is the exact erf form; LayerNorm uses eps = cfg.ln_eps with a biased variance.
+ *    Attention has biases on q, k, v, o and scale 1/sqrt(head_dim).  The adapter has no biases
+ *    and applies SiLU to the gate branch.
+ *
+ * Errors: every call returns an encoder_status; no C++ exception crosses the ABI.  On failure,
+ * encoder_last_error() returns a thread-local message.  A call that fails validation enqueues
+ * no GPU work.
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default stream).  Forward calls
+ * are asynchronous on that stream, and device faults surface at the caller's next
+ * synchronisation.  One forward may be in flight per handle (the workspace is shared).
+ */
+#ifndef AUDIO_ENCODER_H
+#define AUDIO_ENCODER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define ENC_API __attribute__((visibility("default")))
+#else
+#define ENC_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ENC_OK = 0,
+  ENC_E_INVALID_ARG = -1,   /* null pointer, bad size or inconsistent config; nothing enqueued */
+  ENC_E_OUT_OF_MEMORY = -2, /* a device or pinned-host allocation failed                         */
+  ENC_E_DEVICE = -3,        /* a HIP runtime call failed; message in encoder_last_error()       */
+  ENC_E_UNSUPPORTED = -4,   /* valid request this build does not handle (e.g. sample_rate != 16 kHz) */
+  ENC_E_INTERNAL = -5
+} encoder_status;
+
+typedef enum { ENC_BF16 = 0, ENC_F32 = 1 } encoder_dtype;
+
+/* Model and runtime configuration.  Full-size tower: 16000,400,160,128 | 480 | 1280,32,20,64,5120 |
+ * 100 | 2048,8192 | 800 | ENC_BF16 | 1e-5.  Dimension constraints (checked by
+ * encoder_validate_cfg): n_heads*head_dim == d_model, head_dim == 64, conv_channels % 32 == 0,
+ * d_model, d_ffn, d_out and d_adapter multiples of 64, 1 <= window_tokens <= 128,
+ * piece_tokens a multiple of window_tokens. */
+typedef struct {
+  int32_t sample_rate;    /* must be 16000 (no resampling)                                  */
+  int32_t n_fft;          /* 400                                                            */
+  int32_t hop;            /* 160                                                            */
+  int32_t n_mels;         /* 128                                                            */
+  int32_t conv_channels;  /* C: conv1..conv3 output channels                                */
+  int32_t d_model;        /* Transformer width d                                            */
+  int32_t n_layers;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t d_ffn;
+  int32_t window_tokens;  /* W: attention window (tokens); a window covers 8*W mel frames   */
+  int32_t d_out;          /* proj2 output and adapter in/out width                          */
+  int32_t d_adapter;      /* SwiGLU hidden width                                            */
+  int32_t piece_tokens;   /* long-audio piece length in tokens (800 = 64 s)                 */
+  int32_t dtype;          /* encoder_dtype: weights, GEMM operands and output storage      */
+  float ln_eps;
+  int64_t max_tokens_per_pass; /* bounds the activation workspace; larger inputs run in several
+                                  window-aligned passes.  0 selects 8192.                    */
+} encoder_cfg;
+
+typedef struct encoder encoder; /* opaque handle */
+
+/* ---- host-only calls (no GPU work) ----------------------------------------------------- */
+
+/* Checks the dimension constraints above.  ENC_OK, ENC_E_INVALID_ARG or ENC_E_UNSUPPORTED. */
+ENC_API encoder_status encoder_validate_cfg(const encoder_cfg* cfg);
+
+/* Number of float32 values the weight blob for `cfg` must hold.  Blob order (each tensor
+ * row-major, PyTorch [out, in] layout): conv1.w[C,1,3,3] conv1.b[C] conv2.w[C,C,3,3] conv2.b
+ * conv3.w conv3.b conv_out.w[d,16C] (column c*16+f: channel-major flatten); per layer: ln1.g[d]
+ * ln1.b q.w[d,d] q.b k.w k.b v.w v.b o.w o.b ln2.g ln2.b fc1.w[ffn,d] fc1.b fc2.w[d,ffn] fc2.b;
+ * then ln_post.g ln_post.b proj1.w[d,d] proj1.b proj2.w[dout,d] proj2.b gate.w[da,dout]
+ * up.w[da,dout] down.w[dout,da].  Conv taps: [out][in][freq][time]. */
+ENC_API encoder_status encoder_weight_count(const encoder_cfg* cfg, int64_t* n_floats);
+
+/* Embeddings per clip: the sum over windows of the 3 x stride-2 ceil chain of each window's
+ * frame count = ceil((n_samples/160)/8) (12.5 Hz).  n_samples must exceed n_fft/2. */
+ENC_API encoder_status encoder_output_frames(const encoder_cfg* cfg, int64_t n_samples, int64_t* n_frames);
+
+/* The window plan of a [batch, n_samples] call: for each window, 7 int32 values
+ * {clip, first mel frame within the clip, L0 (frames), L1, L2, L3 (valid lengths after each
+ * stride-2 conv; L3 = tokens), first output token (row of the [batch*F, d_out] output)}.
+ * Writes min(n_windows, max_windows) entries to `table` (may be NULL when max_windows is 0)
+ * and the total count to *n_windows. */
+ENC_API encoder_status encoder_plan_windows(const encoder_cfg* cfg, int64_t n_samples, int32_t batch,
+                                    int32_t* table, int32_t max_windows, int32_t* n_windows);
+
+/* ---- handle lifecycle -------------------------------------------------------------------- */
+
+/* Packs the host float32 weight blob (n_floats values, order above) for the current HIP device:
+ * bf16 weights for ENC_BF16 (round-to-nearest-even), float32 for ENC_F32.  The caller keeps
+ * ownership of `weights` and may free it when the call returns.  The handle owns the packed
+ * weights, tables and workspace.  Synchronous. */
+ENC_API encoder_status encoder_create(const float* weights, int64_t n_floats, const encoder_cfg* cfg,
+                              encoder** out);
+ENC_API void encoder_destroy(encoder* e);
+
+/* Bytes of packed weights and tables, and the workspace high-water mark so far. */
+ENC_API encoder_status encoder_memory_stats(const encoder* e, int64_t* weight_bytes,
+                                    int64_t* workspace_bytes);
+
+/* ---- forward passes ------------------------------------------------------------------------ */
+
+/* Whole-clip path.  pcm: device float32 [batch, n_samples] (independent equal-length clips; each
+ * is normalised by its own log-mel maximum).  out: device [batch, F, d_out] with F from
+ * encoder_output_frames, bf16 for ENC_BF16 and float32 for ENC_F32.  n_samples > n_fft/2,
+ * batch >= 1.  Inputs above max_tokens_per_pass run in several window-aligned passes. */
+ENC_API encoder_status encoder_forward(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+                               void* out, void* stream);
+
+/* Long-audio path for one recording (Ossicle card, "Long Audio").  The log-mel and its maximum
+ * are computed over the whole recording, which is then encoded in pieces of piece_tokens tokens
+ * (8*piece_tokens frames), pieces_per_pass pieces per pass.  The last piece may be partial.
+ * Output rows are written in time order: out [F, d_out].  Equals encoder_forward(batch = 1) up to
+ * summation order. */
+ENC_API encoder_status encoder_forward_long(encoder* e, const float* pcm, int64_t n_samples,
+                                    int32_t pieces_per_pass, void* out, void* stream);
+
+/* Normalised log-mel only: mel device float32 [batch, n_samples/160, 128]. */
+ENC_API encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+                               float* mel, void* stream);
+
+/* Stage-wise check point: runs the whole-clip path up to `stage` and writes that stage's output
+ * as float32 to dst (dst_elems values available).  Single pass only (batch*F <=
+ * max_tokens_per_pass).  Stages and layouts (nw = windows, ntok = batch*F):
+ *   0 log-mel [batch, T, 128]      1 conv1 [nw, 4W, 64, C]   2 conv2 [nw, 2W, 32, C]
+ *   3 conv3 [ntok, 16, C]          4 conv_out + positions [ntok, d]
+ *   5 residual after layer `layer` [ntok, d]     6 head (proj2) [ntok, d_out]
+ *   7 adapter output [ntok, d_out]
+ * Conv stages are padded per window; positions at or beyond a window's valid length are
+ * undefined.  Conv channels are innermost (c fastest, then frequency, then time). */
+ENC_API encoder_status encoder_debug_stage(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+                                   int32_t stage, int32_t layer, float* dst, int64_t dst_elems,
+                                   void* stream);
+
+/* ---- per-kernel timing (HIP events on the forward's stream) -------------------------------- */
+
+enum {
+  ENC_K_MEL = 0, ENC_K_CONV1, ENC_K_CONV2, ENC_K_CONV3, ENC_K_CONV_OUT, ENC_K_LN, ENC_K_QKV,
+  ENC_K_ATTN, ENC_K_OPROJ, ENC_K_FFN1, ENC_K_FFN2, ENC_K_PROJ1, ENC_K_PROJ2, ENC_K_GATE_UP,
+  ENC_K_DOWN, ENC_K_OTHER, ENC_K_COUNT
+};
+/* When enabled, forward calls bracket each kernel launch with events.  encoder_timing_read
+ * synchronises on the recorded events and returns, per ENC_K_* id, the summed milliseconds and
+ * the launch count since the last reset (arrays of ENC_K_COUNT entries). */
+ENC_API encoder_status encoder_timing_enable(encoder* e, int32_t enable);
+ENC_API encoder_status encoder_timing_read(encoder* e, double* ms, int64_t* launches, int32_t reset);
+
+/* ---- single-kernel entry points (kernel-level tests) --------------------------------------- */
+
+/* C = epi(A . W^T).  A device [M, K] row-major, W device [N, K] row-major, both bf16 (dtype
+ * ENC_BF16) or float32 (ENC_F32).  bias: device float32 [N] or NULL.  K % 64 == 0.
+ * epi 0: C[M,N] = acc + bias, stored in dtype.   epi 1: C = GELU(acc + bias), stored in dtype.
+ * epi 2: C[M,N] float32 += acc + bias (residual update).
+ * epi 3: SwiGLU over 32-column interleaved gate/up rows of W (rows 64j..64j+31 gate, 64j+32..64j+63
+ *        up, N % 64 == 0): C[M, N/2] = SiLU(gate) * up, stored in dtype. */
+ENC_API encoder_status encoder_op_linear(const void* A, const void* W, const float* bias, void* C,
+                                 int64_t M, int32_t N, int32_t K, int32_t epi, int32_t dtype,
+                                 void* stream);
+
+/* Windowed attention.  qkv device [ntok, 3*n_heads*64] (q | k | v, head h = columns 64h..64h+63
+ * of each part), windows device int32 [n_windows, 2] = {first token, length <= 128}.  out device
+ * [ntok, n_heads*64].  Softmax in float32. */
+ENC_API encoder_status encoder_op_attention(const void* qkv, const int32_t* windows, int32_t n_windows,
+                                    int32_t n_heads, int64_t ntok, void* out, int32_t dtype,
+                                    void* stream);
+
+/* LayerNorm of float32 rows x [M, D] -> y [M, D] in dtype; D % 256 == 0 or D % 64 == 0. */
+ENC_API encoder_status encoder_op_layernorm(const float* x, const float* gamma, const float* beta,
+                                    void* y, int64_t M, int32_t D, float eps, int32_t dtype,
+                                    void* stream);
+
+ENC_API const char* encoder_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AUDIO_ENCODER_H */

@@ -241,7 +241,8 @@ def conv2d_s2(x: np.ndarray, w: np.ndarray, b: np.ndarray) -> np.ndarray:
     for a in range(3):
         for bb in range(3):
             patch = xp[:, a:a + 2 * Ho:2, bb:bb + 2 * To:2].reshape(Cin, Ho * To)
-            y += (w[:, :, a, bb] @ patch).reshape(-1, Ho, To)
+            tap = np.ascontiguousarray(w[:, :, a, bb])  # contiguous, so matmul uses BLAS
+            y += (tap @ patch).reshape(-1, Ho, To)
     return y
 
 

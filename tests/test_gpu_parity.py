@@ -1,0 +1,385 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle on the same seeded
+inputs.  Kernel-level cases cover ragged tails and every epilogue; stage-wise cases compare every
+architectural boundary (log-mel, conv1..3, conv_out + positions, layers, head, adapter) the
+way the model cards describe their own parity checks; full-size cases use the 30 s batch,
+the 64 s piece stream and the hour-long recording, with the oracle evaluated on sampled windows
+(the encoder is window-local, so a window's oracle output needs only that window's log-mel).
+
+Tolerances: log-mel max |diff| <= 1e-3; full-size bf16 output per-frame cosine >= 0.999 and
+relative L2 <= 2e-2; the fp32 tiny configuration and the integer window maps are held much
+tighter (see each test).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from audio_encoder_amd import binding as B
+from audio_encoder_amd import synth as S
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def frame_metrics(got, ref):
+    got = np.asarray(got, dtype=np.float64).reshape(-1, got.shape[-1])
+    ref = np.asarray(ref, dtype=np.float64).reshape(-1, ref.shape[-1])
+    num = (got * ref).sum(1)
+    den = np.linalg.norm(got, axis=1) * np.linalg.norm(ref, axis=1)
+    cos = num / np.maximum(den, 1e-300)
+    rel = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
+    return float(cos.min()), float(rel.max())
+
+
+def bf16_round(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def to_dev(a, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dtype)
+
+
+# =============================================================================================
+# kernel level
+# =============================================================================================
+@pytest.mark.parametrize("D", [256, 1280, 384])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_op_layernorm(D, dtype):
+    rng = np.random.default_rng(D)
+    M = 37
+    x = (rng.standard_normal((M, D)) * 3 + 0.5).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(D)).astype(np.float32)
+    y = torch.empty((M, D), dtype=dtype, device=DEV)
+    B.op_layernorm(to_dev(x), to_dev(g), to_dev(b), y)
+    got = y.float().cpu().numpy()
+    ref = O.layer_norm(x.astype(np.float64), g, b)
+    tol = 1e-5 if dtype == torch.float32 else 8e-3
+    assert np.abs(got - ref).max() <= tol * np.abs(ref).max()
+
+
+LINEAR_SHAPES = [(1, 64, 64), (130, 200, 72), (300, 3840, 1280), (257, 1280, 5120),
+                 (129, 1024, 4320), (64, 128, 8)]
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_SHAPES)
+@pytest.mark.parametrize("epi", [0, 1, 2, 3])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_op_linear(M, N, K, epi, dtype):
+    if epi == 3 and N % 64:
+        pytest.skip("SwiGLU needs N % 64 == 0")
+    rng = np.random.default_rng(M * 7 + N + K + epi)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    W = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        A, W = bf16_round(A), bf16_round(W)
+    acc = A.astype(np.float64) @ W.astype(np.float64).T
+    if epi == 3:
+        Nh = N // 2
+        cols = np.arange(Nh)
+        g = acc[:, 64 * (cols // 32) + cols % 32]
+        u = acc[:, 64 * (cols // 32) + 32 + cols % 32]
+        ref = O.silu(g) * u
+        C = torch.zeros((M, Nh), dtype=dtype, device=DEV)
+        B.op_linear(to_dev(A, dtype), to_dev(W, dtype), None, C, 3)
+    elif epi == 2:
+        C0 = rng.standard_normal((M, N)).astype(np.float32)
+        ref = C0 + acc + bias
+        C = to_dev(C0)
+        B.op_linear(to_dev(A, dtype), to_dev(W, dtype), to_dev(bias), C, 2)
+    else:
+        ref = acc + bias
+        if epi == 1:
+            ref = O.gelu(ref)
+        C = torch.zeros((M, N), dtype=dtype, device=DEV)
+        B.op_linear(to_dev(A, dtype), to_dev(W, dtype), to_dev(bias), C, epi)
+    got = C.float().cpu().numpy()
+    scale = np.sqrt(np.mean(ref ** 2)) + 1e-30
+    err = np.abs(got - ref)
+    if dtype == torch.float32 or epi == 2:
+        assert err.max() <= 2e-5 * scale * max(1.0, np.sqrt(K / 64)), err.max()
+    else:  # one bf16 rounding of the output
+        assert np.all(err <= 2 ** -8 * np.abs(ref) + 1e-4 * scale), err.max()
+
+
+def attention_case(lengths, d, rng):
+    ntok = int(sum(lengths))
+    qkv = rng.standard_normal((ntok, 3 * d)).astype(np.float32)
+    wins = np.zeros((len(lengths), 2), dtype=np.int32)
+    t = 0
+    for i, n in enumerate(lengths):
+        wins[i] = (t, n)
+        t += n
+    return qkv, wins
+
+
+def oracle_attention(qkv, wins, d, nh):
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    out = np.zeros((qkv.shape[0], d))
+    for t0, n in wins:
+        out[t0:t0 + n] = O.window_attention(q[t0:t0 + n], k[t0:t0 + n], v[t0:t0 + n], nh)
+    return out
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_op_attention(dtype):
+    rng = np.random.default_rng(11)
+    nh, d = 4, 256
+    qkv, wins = attention_case([1, 7, 25, 64, 100, 128, 100, 75, 33], d, rng)
+    if dtype == torch.bfloat16:
+        qkv = bf16_round(qkv)
+    out = torch.zeros((qkv.shape[0], d), dtype=dtype, device=DEV)
+    B.op_attention(to_dev(qkv, dtype), to_dev(wins, torch.int32), nh, out)
+    got = out.float().cpu().numpy()
+    ref = oracle_attention(qkv.astype(np.float64), wins, d, nh)
+    if dtype == torch.float32:
+        assert np.abs(got - ref).max() < 1e-5
+    else:
+        cos, rel = frame_metrics(got.reshape(-1, 64), ref.reshape(-1, 64))
+        assert cos > 0.9999 and rel < 1.5e-2, (cos, rel)
+
+
+def test_op_attention_index_probes():
+    # Q = K = 0: uniform weights over each window's valid keys, so V = window id returns the id
+    # and V = position in window returns (n - 1) / 2 (exact after bf16 rounding here)
+    nh, d = 2, 128
+    lengths = [100, 100, 75, 1, 2, 128, 9]
+    ntok = sum(lengths)
+    for probe in ("window", "position"):
+        qkv = np.zeros((ntok, 3 * d), dtype=np.float32)
+        wins = np.zeros((len(lengths), 2), dtype=np.int32)
+        t = 0
+        for i, n in enumerate(lengths):
+            wins[i] = (t, n)
+            qkv[t:t + n, 2 * d:] = (i + 1) if probe == "window" else np.arange(n)[:, None]
+            t += n
+        out = torch.zeros((ntok, d), dtype=torch.bfloat16, device=DEV)
+        B.op_attention(to_dev(qkv, torch.bfloat16), to_dev(wins, torch.int32), nh, out)
+        got = out.float().cpu().numpy()
+        for i, (t0, n) in enumerate(wins):
+            want = (i + 1) if probe == "window" else (n - 1) / 2.0
+            assert np.all(got[t0:t0 + n] == bf16_round(np.float32(want))), (probe, i, n)
+
+
+# =============================================================================================
+# log-mel
+# =============================================================================================
+@pytest.fixture(scope="module")
+def tiny():
+    w = S.make_weights(B.TINY, seed=0)
+    return B.Encoder(w, B.TINY), O.unpack_weights(w, O.TINY)
+
+
+MEL_CASES = {
+    "three_sines_4s": lambda: S.three_sines(),
+    "pink_bursts_30s": lambda: S.pink_plus_bursts(),
+    "pure_tone_clamp": lambda: S.pure_tone_bin(25, 0.3, 48000),
+    "silence": lambda: np.zeros(16000, dtype=np.float32),
+    "shortest_201": lambda: S.pink_plus_bursts(seed=4, n=201),
+    "ragged_30s_plus": lambda: S.pink_plus_bursts(seed=5, n=480000 + 159),
+}
+
+
+@pytest.mark.parametrize("case", list(MEL_CASES))
+def test_log_mel_matches_oracle(tiny, case):
+    enc, _ = tiny
+    x = MEL_CASES[case]()
+    got = enc.log_mel(to_dev(x[None])).cpu().numpy()[0]
+    ref = O.log_mel(x)
+    assert got.shape == ref.shape
+    assert np.abs(got - ref).max() <= 1e-3, np.abs(got - ref).max()
+
+
+def test_log_mel_batch_uses_per_clip_max(tiny):
+    enc, _ = tiny
+    xs = np.stack([S.three_sines(seed=1), 0.01 * S.three_sines(seed=2),
+                   S.pure_tone_bin(40, 0.5, 64000)])
+    got = enc.log_mel(to_dev(xs)).cpu().numpy()
+    for b in range(3):
+        assert np.abs(got[b] - O.log_mel(xs[b])).max() <= 1e-3
+
+
+# =============================================================================================
+# tiny fp32 tower, stage by stage
+# =============================================================================================
+def window_stage(stages, key, plan, layout):
+    """Oracle conv activations [C, F, L] per window -> the library's padded channels-last
+    layout, valid positions only."""
+    return [(w, stages[key][i]) for i, w in enumerate(plan)]
+
+
+@pytest.mark.parametrize("n,batch", [(64000, 1), (53920, 1), (129760, 3), (201, 2)])
+def test_tiny_stagewise(tiny, n, batch):
+    enc, Wt = tiny
+    xs = np.stack([S.mixed_clip(100 + b, n) if n > 1000 else S.pink_plus_bursts(seed=b, n=n)
+                   for b in range(batch)])
+    if n == 64000 and batch == 1:
+        xs = S.three_sines()[None]
+    pcm = to_dev(xs)
+    W = 25
+    outs = {k: enc.debug_stage(pcm, k).cpu().numpy()
+            for k in (B.STAGE_CONV1, B.STAGE_CONV2, B.STAGE_CONV3, B.STAGE_EMBED, B.STAGE_HEAD)}
+    outs["layer1"] = enc.debug_stage(pcm, B.STAGE_LAYER, 1).cpu().numpy()
+    final = enc.forward(pcm).cpu().numpy()
+    F = O.n_output_frames(n, W)
+    win = 0
+    for b in range(batch):
+        st = {}
+        mel = O.log_mel(xs[b])
+        ref = O.encode_mel(mel, Wt, O.TINY, st)
+        plan = O.window_plan(mel.shape[0], W)
+        for i, w in enumerate(plan):
+            for lvl, key, L in ((1, "conv1", w["L1"]), (2, "conv2", w["L2"])):
+                g = outs[B.STAGE_CONV1 if lvl == 1 else B.STAGE_CONV2][win + i][:L]  # [t, f, c]
+                r = st[key][i].transpose(2, 1, 0)  # [t, f, c]
+                assert np.abs(g - r).max() <= 1e-5 * max(1.0, np.abs(r).max()), (key, b, i)
+            g3 = outs[B.STAGE_CONV3][b * F + w["tok"]: b * F + w["tok"] + w["L3"]]
+            r3 = st["conv3"][i].transpose(2, 1, 0)
+            assert np.abs(g3 - r3).max() <= 1e-5
+        win += len(plan)
+        sl = slice(b * F, (b + 1) * F)
+        for key, r in (("embed", st["embed"]), ("layer1", st["layer1"]), ("head", st["head"])):
+            g = outs[{"embed": B.STAGE_EMBED, "layer1": "layer1", "head": B.STAGE_HEAD}[key]][sl]
+            assert np.abs(g - r).max() <= 2e-4 * np.abs(r).max(), key
+        cos, rel = frame_metrics(final[b], ref)
+        assert cos >= 0.99999 and rel <= 1e-3, (cos, rel)
+
+
+def test_tiny_long_mode_equals_whole_clip(tiny):
+    enc, Wt = tiny
+    x = S.segment_stream(12, 150.0)
+    pcm = to_dev(x)
+    whole = enc.forward(pcm[None]).cpu().numpy()[0]
+    for ppp in (1, 2):
+        pieces = enc.forward_long(pcm, pieces_per_pass=ppp).cpu().numpy()
+        assert np.array_equal(whole, pieces)
+    ref = O.encode_long(x, Wt, O.TINY)
+    cos, rel = frame_metrics(whole, ref)
+    assert cos >= 0.99999 and rel <= 1e-3
+
+
+def test_tiny_deterministic(tiny):
+    enc, _ = tiny
+    pcm = to_dev(S.mixed_batch([1, 2], 64000))
+    a = enc.forward(pcm).cpu().numpy()
+    b = enc.forward(pcm).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+# =============================================================================================
+# full-size tower (bf16)
+# =============================================================================================
+@pytest.fixture(scope="module")
+def full():
+    log("generating full-size weights")
+    w = S.make_weights(B.FULL, seed=0)
+    log("creating encoder")
+    enc = B.Encoder(w, B.FULL)
+    Wt = O.unpack_weights(w, O.FULL)
+    del w
+    return enc, Wt
+
+
+def oracle_windows(x, Wt, cfg, idx, stages=None):
+    """Oracle output of the windows `idx` of one clip (log-mel normalised over the clip)."""
+    mel = O.log_mel(x)
+    plan = O.window_plan(mel.shape[0], cfg["window_tokens"])
+    res = []
+    for i in idx:
+        w = plan[i]
+        st = {} if stages is not None else None
+        y = O.encode_mel(mel[w["start"]:w["start"] + w["L0"]], Wt, cfg, st)
+        res.append((w["tok"], y, st))
+    return res, plan
+
+
+def check_bf16(got, ref, what):
+    cos, rel = frame_metrics(got, ref)
+    log(f"{what}: min cos {cos:.6f}  max rel-L2 {rel:.4e}")
+    assert cos >= 0.999 and rel <= 2e-2, (what, cos, rel)
+    return cos, rel
+
+
+def test_full_c1_stagewise(full):
+    enc, Wt = full
+    x = S.pink_plus_bursts(seed=1)
+    pcm = to_dev(x[None])
+    y = enc.forward(pcm)
+    torch.cuda.synchronize()
+    assert y.shape == (1, 375, 2048) and y.dtype == torch.bfloat16
+    got = y.float().cpu().numpy()[0]
+    assert np.isfinite(got).all()
+    embed = enc.debug_stage(pcm, B.STAGE_EMBED).cpu().numpy()
+    l0 = enc.debug_stage(pcm, B.STAGE_LAYER, 0).cpu().numpy()
+    l31 = enc.debug_stage(pcm, B.STAGE_LAYER, 31).cpu().numpy()
+    head = enc.debug_stage(pcm, B.STAGE_HEAD).cpu().numpy()
+    c3 = enc.debug_stage(pcm, B.STAGE_CONV3).cpu().numpy()
+    res, plan = oracle_windows(x, Wt, O.FULL, [0, 3], stages=True)
+    for tok, yref, st in res:
+        n = yref.shape[0]
+        sl = slice(tok, tok + n)
+        check_bf16(c3[sl].reshape(n, -1), st["conv3"][0].transpose(2, 1, 0).reshape(n, -1), "conv3")
+        check_bf16(embed[sl], st["embed"], "conv_out+pos")
+        check_bf16(l0[sl], st["layer0"], "layer 0")
+        check_bf16(l31[sl], st["layer31"], "layer 31")
+        check_bf16(head[sl], st["head"], "head")
+        check_bf16(got[sl], yref, "adapter out")
+
+
+def test_full_c2_batch_sampled_windows(full):
+    enc, Wt = full
+    xs = S.mixed_batch(range(101, 117))
+    y = enc.forward(to_dev(xs))
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy()
+    assert got.shape == (16, 375, 2048) and np.isfinite(got).all()
+    for b, wi in ((0, 0), (7, 3), (15, 2)):
+        res, _ = oracle_windows(xs[b], Wt, O.FULL, [wi])
+        tok, yref, _ = res[0]
+        check_bf16(got[b, tok:tok + yref.shape[0]], yref, f"clip {b} window {wi}")
+    # determinism
+    y2 = enc.forward(to_dev(xs))
+    assert torch.equal(y, y2)
+
+
+def test_full_c3_pieces_equal_whole(full):
+    enc, Wt = full
+    x = S.long_stream_512s()
+    pcm = to_dev(x)
+    whole = enc.forward(pcm[None])[0]
+    pieces = enc.forward_long(pcm, pieces_per_pass=8)
+    torch.cuda.synchronize()
+    assert pieces.shape == (6400, 2048)
+    # windows are independent units, so the piece path reproduces the whole-clip path exactly
+    assert torch.equal(whole, pieces)
+    got = pieces.float().cpu().numpy()
+    for wi in (0, 37, 63):
+        res, _ = oracle_windows(x, Wt, O.FULL, [wi])
+        tok, yref, _ = res[0]
+        check_bf16(got[tok:tok + yref.shape[0]], yref, f"stream window {wi}")
+
+
+def test_full_c4_hour_stream(full):
+    enc, Wt = full
+    x = S.hour_stream()
+    pcm = to_dev(x)
+    torch.cuda.reset_peak_memory_stats()
+    y = enc.forward_long(pcm, pieces_per_pass=1)
+    torch.cuda.synchronize()
+    assert y.shape == (45000, 2048)
+    got = y.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    wbytes, ws = enc.memory_stats()
+    log(f"hour stream: weights {wbytes / 1e9:.2f} GB, workspace high-water {ws / 1e9:.2f} GB")
+    for wi in (0, 225, 449):
+        res, _ = oracle_windows(x, Wt, O.FULL, [wi])
+        tok, yref, _ = res[0]
+        check_bf16(got[tok:tok + yref.shape[0]], yref, f"hour window {wi}")

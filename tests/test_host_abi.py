@@ -1,0 +1,110 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every function
+include/audio_encoder.h declares, validates configurations, and its integer window plan equals
+the oracle's window plan exactly."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from audio_encoder_amd import binding as B
+from audio_encoder_amd import synth as S
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "audio_encoder.h")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"ENC_API\s+[\w\s\*]+?\b(encoder_\w+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("encoder_create", "encoder_forward", "encoder_forward_long", "encoder_log_mel",
+              "encoder_destroy", "encoder_output_frames", "encoder_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    L = B.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) == set(B._SIGS)
+
+
+def oracle_cfg(cfg):
+    return {k: cfg[k] for k in O.FULL}
+
+
+def test_product_presets_match_oracle_presets():
+    assert oracle_cfg(B.FULL) == O.FULL
+    assert oracle_cfg(B.TINY) == O.TINY
+
+
+@pytest.mark.parametrize("cfg", [B.FULL, B.TINY])
+def test_weight_count_matches_blob_layout(cfg):
+    assert B.encoder_weight_count(cfg) == S.weight_count(cfg)
+
+
+def test_validate_cfg():
+    assert B.encoder_validate_cfg(B.FULL) == B.ENC_OK
+    assert B.encoder_validate_cfg(B.TINY) == B.ENC_OK
+    bad = [dict(B.FULL, n_heads=19), dict(B.FULL, head_dim=32, n_heads=40),
+           dict(B.FULL, conv_channels=100), dict(B.FULL, window_tokens=129),
+           dict(B.FULL, window_tokens=0), dict(B.FULL, piece_tokens=850),
+           dict(B.FULL, d_ffn=5000), dict(B.FULL, n_fft=512), dict(B.FULL, ln_eps=0.0),
+           dict(B.FULL, dtype=7), dict(B.FULL, max_tokens_per_pass=50)]
+    for c in bad:
+        assert B.encoder_validate_cfg(c) == B.ENC_E_INVALID_ARG, c
+    assert B.encoder_validate_cfg(dict(B.FULL, sample_rate=44100)) == B.ENC_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("n", [201, 16000, 64000, 480000, 1024000, 2560000, 57600000, 480160,
+                               127999, 128001])
+def test_output_frames_match_oracle(n):
+    assert B.encoder_output_frames(B.FULL, n) == O.n_output_frames(n, 100)
+    assert B.encoder_output_frames(B.TINY, n) == O.n_output_frames(n, 25)
+
+
+def test_output_frames_rejects_short_input():
+    with pytest.raises(B.EncoderError):
+        B.encoder_output_frames(B.FULL, 200)
+
+
+@pytest.mark.parametrize("cfg,W", [(B.FULL, 100), (B.TINY, 25)])
+@pytest.mark.parametrize("n,batch", [(480000, 16), (64000, 1), (8192000, 1), (57600000, 1),
+                                     (129760, 3), (201, 2)])
+def test_window_plan_is_bit_exact_with_oracle(cfg, W, n, batch):
+    got = B.encoder_plan_windows(cfg, n, batch)
+    T = O.n_mel_frames(n)
+    F = O.n_output_frames(n, W)
+    rows = []
+    for b in range(batch):
+        for w in O.window_plan(T, W):
+            rows.append([b, w["start"], w["L0"], w["L1"], w["L2"], w["L3"], b * F + w["tok"]])
+    assert np.array_equal(got, np.array(rows, dtype=np.int32).reshape(-1, 7))
+
+
+def test_plan_of_hour_stream_has_45000_tokens():
+    tab = B.encoder_plan_windows(B.FULL, 57_600_000, 1)
+    assert len(tab) == 450 and tab[:, 5].sum() == 45000
+    # 64 s pieces are 8 whole windows each: every 8th window starts a piece
+    assert np.all(tab[::8, 1] % 6400 == 0)
+
+
+def test_create_rejects_bad_blob_without_touching_the_gpu():
+    import ctypes
+    c = B.make_cfg(B.TINY)
+    h = ctypes.c_void_p()
+    w = np.zeros(10, dtype=np.float32)
+    st = B.lib().encoder_create(w.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), 10,
+                                ctypes.byref(c), ctypes.byref(h))
+    assert st == B.ENC_E_INVALID_ARG
+    assert b"config needs" in B.lib().encoder_last_error()
+
+
+def test_forward_argument_checks():
+    L = B.lib()
+    assert L.encoder_forward(None, None, 1000, 1, None, None) == B.ENC_E_INVALID_ARG
+    assert L.encoder_op_linear(None, None, None, None, 1, 1, 1, 0, 0, None) == B.ENC_E_INVALID_ARG
