@@ -4,13 +4,15 @@
 // no score outside a window is ever formed.  Scores are scaled by 1/sqrt(64), keys past the
 // window's valid length are masked, and the softmax runs in fp32.
 //
-// bf16 path (windows of up to 128 tokens): four waves, each owning 32 query rows.
-//   S = Q K^T  : 4 key blocks x 4 K-steps of v_mfma_f32_32x32x16_bf16 (Q fragments straight
-//                from HBM, K staged in LDS with XOR-swizzled 16-byte chunks)
-//   softmax    : row max and row sum with cross-lane shuffles inside each 32-lane half (a
-//                32x32 MFMA result row is spread over the 32 lanes of one half)
-//   O = P V    : P goes through LDS to become an A operand; V is staged transposed so each
-//                lane reads 8 consecutive keys of one feature as a B operand.
+// bf16 path (windows of up to 128 tokens): four waves, each owning 32 queries.
+//   S^T = K Q^T : 4 key blocks x 4 K-steps of v_mfma_f32_32x32x16_bf16.  K is staged in LDS
+//                 (XOR-swizzled 16-byte chunks); Q fragments come straight from HBM.  In the
+//                 transposed product each lane owns one query column, so the softmax max and
+//                 sum run over its own registers plus a single exchange with lane ^ 32.
+//   O^T = V^T P^T: the unnormalised probabilities are packed to bf16 in registers and reordered
+//                 into the B-operand layout with one lane ^ 32 exchange per K-step (no LDS round
+//                 trip); V is staged transposed so each lane reads 8 consecutive keys of one
+//                 feature.  The 1/sum scale is applied to O in fp32.
 // fp32 path: one thread per query row with an online softmax over the window's keys.
 #include <algorithm>
 
@@ -31,119 +33,137 @@ constexpr int VTS = QMAX + 8;  // row stride (elements) of the transposed V and 
 __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict__ qkv, WinRef wr,
                                                         int32_t n_heads, int32_t d,
                                                         bf16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[QMAX * HD];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[HD * VTS];
-  __shared__ __attribute__((aligned(16))) bf16_t Ps[4][32 * VTS];
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[QMAX * HD];   // [key][64], chunk-swizzled
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[HD * VTS];    // [feature][key]
 
   const int w = blockIdx.x / n_heads;
   const int h = blockIdx.x - w * n_heads;
   const int tok0 = wr.p[(int64_t)w * wr.stride + wr.tok_off];
   const int n = wr.p[(int64_t)w * wr.stride + wr.len_off];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
   const int64_t ld = 3 * (int64_t)d;
   const bf16_t* base = qkv + (int64_t)tok0 * ld + h * HD;
 
-  // stage K (row-major, swizzled) and V (transposed)
+  // K rows (16-byte chunks, swizzled) and V transposed: each thread takes 4 consecutive keys
+  // of one 8-feature chunk and writes 4 keys x 8 features as eight 8-byte rows of Vt
   {
     const int c = tid & 7;
+    const int r0 = (tid >> 3) * 4;
+    uint32_t vw[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i;
+      const int r = r0 + i;
       uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = make_uint4(0u, 0u, 0u, 0u);
       if (r < n) {
         kv = *reinterpret_cast<const uint4*>(base + (int64_t)r * ld + d + c * 8);
         vv = *reinterpret_cast<const uint4*>(base + (int64_t)r * ld + 2 * d + c * 8);
       }
       *reinterpret_cast<uint4*>(&Ks[r * HD + ((c ^ (r & 7)) * 8)]) = kv;
-      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+      vw[i][0] = vv.x; vw[i][1] = vv.y; vw[i][2] = vv.z; vw[i][3] = vv.w;
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(c * 8 + 2 * e) * VTS + r] = (bf16_t)(vw[e] & 0xffffu);
-        Vt[(c * 8 + 2 * e + 1) * VTS + r] = (bf16_t)(vw[e] >> 16);
-      }
+    for (int e = 0; e < 8; ++e) {  // feature c*8+e: keys r0..r0+3
+      const int sh = (e & 1) * 16;
+      const uint32_t k01 = ((vw[0][e >> 1] >> sh) & 0xffffu) | (((vw[1][e >> 1] >> sh) & 0xffffu) << 16);
+      const uint32_t k23 = ((vw[2][e >> 1] >> sh) & 0xffffu) | (((vw[3][e >> 1] >> sh) & 0xffffu) << 16);
+      *reinterpret_cast<uint2*>(&Vt[(c * 8 + e) * VTS + r0]) = make_uint2(k01, k23);
     }
   }
-  // Q fragments of this wave's 32 rows: lane -> row lane%32, 8 features per K-step
-  const int q0 = wv * 32;
-  const int qr = q0 + (lane & 31);
+  // Q as the B operand of S^T = K Q^T: lane -> query column l32, 8 features per K-step
+  const int q = wv * 32 + l32;
   bf16x8_t qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (qr < n) v = *reinterpret_cast<const uint4*>(base + (int64_t)qr * ld + ks * 16 + (lane >> 5) * 8);
+    if (q < n) v = *reinterpret_cast<const uint4*>(base + (int64_t)q * ld + ks * 16 + half * 8);
     qf[ks] = __builtin_bit_cast(bf16x8_t, v);
   }
   __syncthreads();
 
+  // S^T blocks: rows = keys 32*kb + 8*(v/4) + 4*half + v%4, column = this lane's query
   f32x16_t S[4];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
+  for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) S[jb][v] = 0.0f;
-    const int key = jb * 32 + (lane & 31);
+    for (int v = 0; v < 16; ++v) S[kb][v] = 0.0f;
+    const int key = kb * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int ch = ks * 2 + (lane >> 5);
+      const int ch = ks * 2 + half;
       const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[key * HD + ((ch ^ (key & 7)) * 8)]);
-      S[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf, S[jb], 0, 0, 0);
+      S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[kb], 0, 0, 0);
     }
   }
-
-  // softmax over keys; lane holds key column lane%32 of each block for 16 rows
-  const float scale = 0.125f;  // 1/sqrt(64)
+  // softmax over keys for this lane's query: registers, then the other 32-lane half
+  float m = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float m = -INFINITY;
+  for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      const int key = jb * 32 + (lane & 31);
-      const float s = key < n ? S[jb][v] * scale : -INFINITY;
-      S[jb][v] = s;
-      m = fmaxf(m, s);
+    for (int v = 0; v < 16; ++v) {
+      const int key = kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      const float sv = key < n ? S[kb][v] * 0.125f : -INFINITY;  // 1/sqrt(64)
+      S[kb][v] = sv;
+      m = fmaxf(m, sv);
     }
+  m = fmaxf(m, __shfl_xor(m, 32));
+  float sum = 0.0f;
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float sum = 0.0f;
+  for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      const float e = __expf(S[jb][v] - m);
-      S[jb][v] = e;
+    for (int v = 0; v < 16; ++v) {
+      const float e = __expf(S[kb][v] - m);
+      S[kb][v] = e;
       sum += e;
     }
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) sum += __shfl_xor(sum, o);
-    const float inv = 1.0f / sum;
-    const int prow = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-      Ps[wv][prow * VTS + jb * 32 + (lane & 31)] = f32_to_bf16(S[jb][v] * inv);
-  }
-  __syncthreads();
+  sum += __shfl_xor(sum, 32);
+  const float inv = 1.0f / sum;
 
-  // O = P V
-  f32x16_t O[2];
+  // P^T as the B operand of O^T = V^T P^T: K-step s covers keys 16s..16s+15; lane half hh needs
+  // keys 16s + 8hh .. +8.  Its own registers hold keys 8g + 4*half + (0..3) (g = 2(s%2) + hh for
+  // the own part); the other four come from lane ^ 32.
+  bf16x8_t pf[8];
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int s = 0; s < 8; ++s) {
+    const int kb = s >> 1;
+    const int g_own = 2 * (s & 1) + half;        // group whose own half this lane keeps
+    const int g_send = 2 * (s & 1) + (1 - half);  // group the partner needs from this lane
+    uint32_t own0 = 0, own1 = 0, snd0 = 0, snd1 = 0;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) O[db][v] = 0.0f;
-#pragma unroll
-  for (int ks = 0; ks < QMAX / 16; ++ks) {
-    const int kk = ks * 16 + (lane >> 5) * 8;
-    const bf16x8_t pf = *reinterpret_cast<const bf16x8_t*>(&Ps[wv][(lane & 31) * VTS + kk]);
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const int dim = db * 32 + (lane & 31);
-      const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&Vt[dim * VTS + kk]);
-      O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, vf, O[db], 0, 0, 0);
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t a0 = (uint32_t)f32_to_bf16(S[kb][4 * g + 0]) | ((uint32_t)f32_to_bf16(S[kb][4 * g + 1]) << 16);
+      const uint32_t a1 = (uint32_t)f32_to_bf16(S[kb][4 * g + 2]) | ((uint32_t)f32_to_bf16(S[kb][4 * g + 3]) << 16);
+      if (g == g_own) { own0 = a0; own1 = a1; }
+      if (g == g_send) { snd0 = a0; snd1 = a1; }
     }
+    const uint32_t rc0 = (uint32_t)__shfl_xor((int)snd0, 32);
+    const uint32_t rc1 = (uint32_t)__shfl_xor((int)snd1, 32);
+    // keys 8g..8g+3 come from the half-0 lane, 8g+4..8g+7 from the half-1 lane
+    const uint4 pk = half == 0 ? make_uint4(own0, own1, rc0, rc1) : make_uint4(rc0, rc1, own0, own1);
+    pf[s] = __builtin_bit_cast(bf16x8_t, pk);
   }
+
+  // O^T blocks: rows = features 32*db + 8*(v/4) + 4*half + v%4, column = this lane's query
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int row = q0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    if (row >= n) continue;
-    bf16_t* o = out + (int64_t)(tok0 + row) * d + h * HD;
+  for (int db = 0; db < 2; ++db) {
+    f32x16_t O;
 #pragma unroll
-    for (int db = 0; db < 2; ++db) o[db * 32 + (lane & 31)] = f32_to_bf16(O[db][v]);
+    for (int v = 0; v < 16; ++v) O[v] = 0.0f;
+    const int feat = db * 32 + l32;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&Vt[feat * VTS + s * 16 + half * 8]);
+      O = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], O, 0, 0, 0);
+    }
+    if (q < n) {
+      bf16_t* o = out + (int64_t)(tok0 + q) * d + h * HD + db * 32 + 4 * half;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = (uint32_t)f32_to_bf16(O[4 * g] * inv) | ((uint32_t)f32_to_bf16(O[4 * g + 1] * inv) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(O[4 * g + 2] * inv) | ((uint32_t)f32_to_bf16(O[4 * g + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(o + 8 * g) = make_uint2(lo, hi);
+      }
+    }
   }
 }
 

@@ -3,17 +3,23 @@
 //
 // The image of one window is [128 mel bins (frequency), L0 frames (time)], zero outside.  The
 // kernel reads the raw log10 mel and applies the Whisper normalisation (max(L, max - 8) + 4) / 4
-// on load, so the normalised mel is never written to HBM.  Each thread produces 8 consecutive
-// output channels of one (time, frequency) position and writes them as one 16-byte store into
-// the channels-last activation [window][4W time][64 freq][C], which is the layout the implicit
-// GEMM of conv2 reads.  With one input channel this layer has K = 9 and no MFMA shape fits;
-// it is bound by its HBM writes.
+// on load, so the normalised mel is never written to HBM.  The output is the channels-last
+// activation [window][4W time][64 freq][C] that the implicit GEMM of conv2 reads.
+//
+// With one input channel the layer has K = 9: no MFMA shape fits and it is bound by its HBM
+// writes (2*C bytes per output position).  A workgroup owns RT consecutive output time steps of
+// one window.  It stages the 2*RT+1 normalised mel frames those steps touch in LDS (zero rows and
+// columns for the padding).  Each thread keeps the 9 taps and the bias of its 8 output channels
+// in registers and emits 16-byte stores; CG = C/8 consecutive threads write one contiguous
+// C-channel position.
 #include <algorithm>
 
 #include "ae_internal.h"
 
 namespace ae {
 namespace {
+
+constexpr int RT = 4;  // output time steps per workgroup
 
 __device__ inline float key_to_float_c(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
@@ -37,55 +43,67 @@ template <> struct Pack8<float> {
   }
 };
 
+// blockDim.x = CG * FQ; thread -> channel group cg = tid % CG, frequency phase fq = tid / CG
 template <typename T>
-__global__ __launch_bounds__(256) void conv1_kernel(const Win* __restrict__ wins, int32_t n_win,
-                                                    int32_t W, const float* __restrict__ mel,
+__global__ __launch_bounds__(256) void conv1_kernel(const Win* __restrict__ wins, int32_t W,
+                                                    const float* __restrict__ mel,
                                                     int64_t T_frames,
                                                     const uint32_t* __restrict__ max_key,
                                                     const float* __restrict__ wt,
                                                     const float* __restrict__ bias, int32_t C,
                                                     T* __restrict__ act1) {
-  extern __shared__ float sw[];  // [C][10]: 9 taps + bias
-  for (int i = threadIdx.x; i < C * 9; i += blockDim.x) sw[(i / 9) * 10 + (i % 9)] = wt[i];
-  for (int i = threadIdx.x; i < C; i += blockDim.x) sw[i * 10 + 9] = bias[i];
-  __syncthreads();
+  __shared__ float xs[2 * RT + 1][130];  // frames 2*t1_0-1 .. 2*(t1_0+RT-1)+1, freq -1..128
+  const int CG = C >> 3;
+  const int FQ = blockDim.x / CG;
+  const int tid = threadIdx.x;
+  const int cg = tid % CG, fq = tid / CG;
+  const int L1max = 4 * W;
+  const int nrb = (L1max + RT - 1) / RT;
+  const int w = blockIdx.x / nrb;
+  const int t1_0 = (blockIdx.x - w * nrb) * RT;
+  const Win wn = wins[w];
+  if (t1_0 >= wn.L1) return;
 
-  const int CG = C / 8;
-  const int64_t L1max = 4 * (int64_t)W;
-  const int64_t total = (int64_t)n_win * L1max * 64 * CG;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int cg = (int)(i % CG);
-    int64_t r = i / CG;
-    const int f1 = (int)(r % 64);
-    r /= 64;
-    const int t1 = (int)(r % L1max);
-    const int wi = (int)(r / L1max);
-    const Win wn = wins[wi];
-    if (t1 >= wn.L1) continue;
-    const float lo = key_to_float_c(max_key[wn.clip]) - 8.0f;
-    const float* mrow = mel + ((int64_t)wn.clip * T_frames + wn.start) * 128;
-    float xv[9];
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-#pragma unroll
-      for (int b = 0; b < 3; ++b) {
-        const int f = 2 * f1 + a - 1;  // frequency tap
-        const int t = 2 * t1 + b - 1;  // time tap
-        const bool ok = f >= 0 && f < 128 && t >= 0 && t < wn.L0;
-        xv[a * 3 + b] = ok ? (fmaxf(mrow[(int64_t)t * 128 + f], lo) + 4.0f) * 0.25f : 0.0f;
-      }
-    }
-    float o[8];
+  const float lo = key_to_float_c(max_key[wn.clip]) - 8.0f;
+  const float* mrow = mel + ((int64_t)wn.clip * T_frames + wn.start) * 128;
+  for (int i = tid; i < (2 * RT + 1) * 130; i += blockDim.x) {
+    const int r = i / 130, c = i - r * 130;
+    const int t = 2 * t1_0 - 1 + r, f = c - 1;
+    float v = 0.0f;
+    if (t >= 0 && t < wn.L0 && f >= 0 && f < 128) v = (fmaxf(mrow[t * 128 + f], lo) + 4.0f) * 0.25f;
+    xs[r][c] = v;
+  }
+  float wr[8][9], br[8];
+  if (fq < FQ) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float* wc = sw + (cg * 8 + c) * 10;
-      float acc = wc[9];
+      br[c] = bias[cg * 8 + c];
 #pragma unroll
-      for (int q = 0; q < 9; ++q) acc = fmaf(wc[q], xv[q], acc);
-      o[c] = gelu_erf(acc);
+      for (int q = 0; q < 9; ++q) wr[c][q] = wt[(cg * 8 + c) * 9 + q];
     }
-    Pack8<T>::store(act1 + (((int64_t)wi * L1max + t1) * 64 + f1) * C + cg * 8, o);
+  }
+  __syncthreads();
+  if (fq >= FQ) return;
+
+  const int rows = min(RT, wn.L1 - t1_0);
+  for (int r = 0; r < rows; ++r) {
+    T* orow = act1 + (((int64_t)w * L1max + t1_0 + r) * 64) * C + cg * 8;
+    for (int f1 = fq; f1 < 64; f1 += FQ) {
+      float xv[9];
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b) xv[a * 3 + b] = xs[2 * r + b][2 * f1 + a];  // (freq a, time b)
+      float o[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float acc = br[c];
+#pragma unroll
+        for (int q = 0; q < 9; ++q) acc = fmaf(wr[c][q], xv[q], acc);
+        o[c] = gelu_erf(acc);
+      }
+      Pack8<T>::store(orow + (int64_t)f1 * C, o);
+    }
   }
 }
 
@@ -95,10 +113,15 @@ template <typename T>
 hipError_t launch_conv1(const PassGeom& g, const float* mel, int64_t T_frames,
                         const uint32_t* max_key, const float* w, const float* b, int32_t C,
                         T* act1, hipStream_t s) {
-  const int64_t total = (int64_t)g.n_win * 4 * g.W * 64 * (C / 8);
-  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 1 << 16));
-  hipLaunchKernelGGL(conv1_kernel<T>, dim3(blocks), dim3(256), C * 10 * sizeof(float), s, g.wins,
-                     g.n_win, g.W, mel, T_frames, max_key, w, b, C, act1);
+  const int CG = C / 8;
+  const int FQ = std::max(1, std::min(64, 256 / CG));
+  const int threads = CG * FQ;
+  if (threads > 256 || threads < 1) return hipErrorInvalidValue;
+  const int nrb = (4 * g.W + RT - 1) / RT;
+  const int64_t blocks = (int64_t)g.n_win * nrb;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(conv1_kernel<T>, dim3((unsigned)blocks), dim3(threads), 0, s, g.wins, g.W,
+                     mel, T_frames, max_key, w, b, C, act1);
   return hipGetLastError();
 }
 

@@ -38,57 +38,90 @@ struct ALinear {
   int32_t K;
   struct Row { const T* p; };
   struct KC { int k; bool ok; };
-  __device__ bool tile_live(int64_t m0) const { return m0 < M; }
+  __device__ bool tile_live(int64_t m0, int) const { return m0 < M; }
   __device__ Row row(int64_t r) const { return Row{r < M ? A + r * lda : nullptr}; }
   __device__ KC kc(int k) const { return KC{k, k < K}; }
   __device__ const T* ptr(const Row& x, const KC& c) const {
     return (x.p && c.ok) ? x.p + c.k : nullptr;
   }
+  // byte-offset form for buffer loads: rows past M read as zero (offset beyond the range)
+  struct BRow { uint32_t off; };
+  __device__ BRow brow(int64_t r) const {
+    return BRow{r < M ? (uint32_t)(r * lda * (int64_t)sizeof(T)) : 0x80000000u};
+  }
+  __device__ uint32_t boff(const BRow& x, const KC& c) const {
+    return c.ok ? x.off + (uint32_t)(c.k * (int)sizeof(T)) : 0x80000000u;
+  }
+  __device__ int64_t bytes() const { return M * lda * (int64_t)sizeof(T); }
+  __device__ const void* base() const { return A; }
 };
 
-// im2col view for a 3x3 stride-2 pad-1 conv: output row r of window w covers
-// (t_out, f_out) = (loc / Fout, loc % Fout) with loc = r - w * rows_per_win.
+// im2col view for a 3x3 stride-2 pad-1 conv.  GEMM row r is output position
+// (window w, time t, freq f) with r = w * rows_per_win + t * Fout + f (rows_per_win = Lout_max *
+// Fout, so tiles may straddle windows).  Per row the loader keeps the element offset of tap
+// (freq 0, time 0) and a 9-bit mask of the taps that fall inside the window's valid image.
 template <typename T>
 struct AConv {
   const T* in;
   const Win* wins;
   int32_t C, Fin, Fout, Lin_max, level, rows_per_win, K;
-  struct Row { const T* base; int t2, f2, Lin; };
-  struct KC { int ci, da, db; bool ok; };
-  __device__ bool tile_live(int64_t m0) const {
-    const int w = (int)(m0 / rows_per_win);
-    const int loc = (int)(m0 - (int64_t)w * rows_per_win);
-    const Win wn = wins[w];
-    return loc / Fout < (level == 2 ? wn.L2 : wn.L3);
+  int64_t m_rows;
+  struct Row { int32_t off; int32_t mask; };
+  struct KC { int32_t toff; int32_t bit; bool ok; };
+  __device__ int lout(const Win& wn) const { return level == 2 ? wn.L2 : wn.L3; }
+  __device__ bool row_valid(int64_t r) const {
+    if (r >= m_rows) return false;
+    const int w = (int)(r / rows_per_win);
+    const int t = (int)(r - (int64_t)w * rows_per_win) / Fout;
+    return t < lout(wins[w]);
+  }
+  __device__ bool tile_live(int64_t m0, int bm) const {
+    const int64_t last = min(m0 + bm - 1, m_rows - 1);
+    if (m0 / rows_per_win != last / rows_per_win) return true;  // straddles two windows
+    return row_valid(m0);
   }
   __device__ Row row(int64_t r) const {
+    Row x{0, 0};
+    if (r >= m_rows) return x;
     const int w = (int)(r / rows_per_win);
     const int loc = (int)(r - (int64_t)w * rows_per_win);
     const int t = loc / Fout, f = loc - (loc / Fout) * Fout;
     const Win wn = wins[w];
-    Row x;
-    if (t >= (level == 2 ? wn.L2 : wn.L3)) { x.base = nullptr; x.t2 = x.f2 = x.Lin = 0; return x; }
-    x.base = in + (int64_t)w * Lin_max * Fin * C;
-    x.t2 = 2 * t - 1;
-    x.f2 = 2 * f - 1;
-    x.Lin = level == 2 ? wn.L1 : wn.L2;
+    if (t >= lout(wn)) return x;
+    const int Lin = level == 2 ? wn.L1 : wn.L2;
+    int m = 0;
+#pragma unroll
+    for (int da = 0; da < 3; ++da)
+#pragma unroll
+      for (int db = 0; db < 3; ++db) {
+        const int ti = 2 * t - 1 + db, fi = 2 * f - 1 + da;
+        if (ti >= 0 && ti < Lin && fi >= 0 && fi < Fin) m |= 1 << (da * 3 + db);
+      }
+    x.mask = m;
+    x.off = ((w * Lin_max + (2 * t - 1)) * Fin + (2 * f - 1)) * C;
     return x;
   }
   __device__ KC kc(int k) const {
     KC c;
     c.ok = k < K;
     const int tap = k / C;
-    c.ci = k - tap * C;
-    c.da = tap / 3;          // frequency tap
-    c.db = tap - 3 * c.da;   // time tap
+    const int ci = k - tap * C;
+    const int da = tap / 3, db = tap - 3 * (tap / 3);  // frequency tap, time tap
+    c.bit = 1 << tap;
+    c.toff = (db * Fin + da) * C + ci;
     return c;
   }
   __device__ const T* ptr(const Row& x, const KC& c) const {
-    if (!x.base || !c.ok) return nullptr;
-    const int t = x.t2 + c.db, f = x.f2 + c.da;
-    if (t < 0 || t >= x.Lin || f < 0 || f >= Fin) return nullptr;
-    return x.base + ((int64_t)t * Fin + f) * C + c.ci;
+    return (c.ok && (x.mask & c.bit)) ? in + (x.off + c.toff) : nullptr;
   }
+  using BRow = Row;
+  __device__ BRow brow(int64_t r) const { return row(r); }
+  __device__ uint32_t boff(const BRow& x, const KC& c) const {
+    return (c.ok && (x.mask & c.bit)) ? (uint32_t)((x.off + c.toff) * (int)sizeof(T)) : 0x80000000u;
+  }
+  __device__ int64_t bytes() const { return (int64_t)wins_bytes; }
+  __device__ const void* base() const { return in; }
+  int64_t wins_bytes;  // bytes of the input activation
 };
 
 // ============================================================================================
@@ -102,7 +135,9 @@ struct OLinear {
 struct OConv {
   const Win* wins;
   int32_t rows_per_win, Fout, C, level, Lout_max;
+  int64_t m_rows;
   __device__ int64_t off(int64_t r) const {
+    if (r >= m_rows) return -1;
     const int w = (int)(r / rows_per_win);
     const int loc = (int)(r - (int64_t)w * rows_per_win);
     const int t = loc / Fout, f = loc - (loc / Fout) * Fout;
@@ -118,6 +153,21 @@ struct EpiP {
   void* C;
   const float* pe;
   const int32_t* tok_pos;
+};
+
+template <typename T> struct Store4x;
+template <> struct Store4x<bf16_t> {
+  __device__ static inline void put(bf16_t* p, float a, float b, float c, float d) {
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    o.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+    *reinterpret_cast<uint2*>(p) = o;
+  }
+};
+template <> struct Store4x<float> {
+  __device__ static inline void put(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  }
 };
 
 template <int EPI, typename OT>
@@ -138,128 +188,306 @@ __device__ inline void epi_store(const EpiP& ep, int64_t off, int64_t row, int c
 // ============================================================================================
 // bf16 MFMA kernel
 // ============================================================================================
-constexpr int BM = 128, BN = 128, BK = 64, NTHR = 256;
+constexpr int BK = 64, NTHR = 256;
 
 __device__ inline uint4 ld16(const bf16_t* p) {
   return p ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Block tile BM x BN, WGM x WGN waves, each owning (BM/WGM) x (BN/WGN) as TM x TN blocks of
+// 32x32 MFMA output.
+template <int BM_, int BN_, int WGM_, int WGN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int NW = WGM * WGN, NT = 64 * NW;  // waves, threads
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static constexpr int RS = NT / 8;                    // rows covered by one loader pass
+  static constexpr int AR = BM / RS, BR = BN / RS;     // 16-byte chunks per thread per K step
+  static_assert(TM * 32 == WTM && TN * 32 == WTN && AR * RS == BM && BR * RS == BN, "tile");
+};
+using TileL = Tile<256, 256, 2, 2>;   // 4 waves, wave tile 128 x 128
+using TileL8 = Tile<256, 256, 2, 4>;  // 8 waves, wave tile 128 x 64 (two waves per SIMD)
+using TileL8b = Tile<256, 256, 4, 2>; // 8 waves, wave tile 64 x 128
+using TileM = Tile<256, 128, 2, 2>;   // 4 waves, wave tile 128 x 64
+using TileM8 = Tile<256, 128, 4, 2>;  // 8 waves, wave tile 64 x 64
+using TileC = Tile<256, 160, 4, 1>;   // 4 waves, wave tile 64 x 160 (480-channel convs)
+
+// Workgroups are dispatched round-robin over the 8 XCDs; remap so that consecutive logical
+// tiles (same A rows, neighbouring B columns) run on the same XCD and share its L2.
+__device__ inline int64_t xcd_remap(int64_t bid, int64_t G) {
+  const int64_t per = G / 8, rem = G % 8;
+  const int64_t x = bid % 8, i = bid / 8;
+  return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// LDS tile rows are 128 bytes (BK = 64 bf16).  The 16-byte chunk index is XORed with
+// (row >> 1) & 7 so that 16 consecutive rows at one logical chunk cover all 64 banks
+// (row parity selects the bank half, the XOR spreads the 8 chunk slots).
+__device__ __host__ constexpr int swz(int r) { return (r >> 1) & 7; }
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  // raw buffer: stride 0, range check against `bytes`; dword3 0x00020000 (32-bit data format)
+  const int n = (int)min<int64_t>(bytes, 0x7fffffff);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+
 // TAG only names the call site (one kernel symbol per role, so profiles separate them)
-template <class AS, class OM, int EPI, typename OT, int TAG>
-__global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(AS as, const bf16_t* __restrict__ Bw,
+#ifndef AE_GEMM_SCHED
+#define AE_GEMM_SCHED 3
+#endif
+
+// SCHED bit 0: software-pipeline the K loop across the barrier (the last K-step's MFMAs run
+// after the barrier, covering the LDS reads of the next tile's first K-step).  SCHED bit 1:
+// order each K-step as [LDS reads of the next K-step][MFMAs of this one] for the scheduler.
+template <class TL, class AS, class OM, int EPI, typename OT, int TAG, int SCHED = AE_GEMM_SCHED>
+__global__ __launch_bounds__(TL::NT) void gemm_bf16_kernel(AS as, const bf16_t* __restrict__ Bw,
                                                          int32_t N, int32_t K, OM om, EpiP ep,
                                                          int32_t n_tiles, int32_t pe_ld) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
+  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN, AR = TL::AR, BR = TL::BR;
+  constexpr int WTN = TL::WTN;
+  constexpr int SMEM = 2 * (BM + BN) * BK;  // bf16 elements: double-buffered A and B tiles
+  // epilogue staging: SR rows of each wave's tile at a time (32, or 16 when 32 do not fit)
+  constexpr int SR = (TL::NW * 32 * (WTN + 4) * 4 <= SMEM * 2) ? 32 : 16;
+  static_assert(TL::NW * SR * (WTN + 4) * 4 <= SMEM * 2, "epilogue staging must fit in the tiles");
+  __shared__ __attribute__((aligned(16))) bf16_t smem[SMEM];
+  bf16_t* const sA = smem;                 // [2][BM * BK]
+  bf16_t* const sB = smem + 2 * BM * BK;   // [2][BN * BK]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
   const int wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
-  const int64_t mt = blockIdx.x / n_tiles;
-  const int nt = blockIdx.x - (int)(mt * n_tiles);
+  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
+  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t mt = tile / n_tiles;
+  const int nt = (int)(tile - mt * n_tiles);
   const int64_t m0 = mt * BM;
   const int n0 = nt * BN;
-  if (!as.tile_live(m0)) return;
+  if (!as.tile_live(m0, BM)) return;
 
-  // loader mapping: 16-byte chunk c of rows lr + 32*i
+  // global -> register loader: 16-byte chunk c of rows lr + 32*i, via buffer loads whose
+  // out-of-range offsets return zero (ragged M/N tails, conv padding taps)
   const int c = tid & 7;
   const int lr = tid >> 3;
-  typename AS::Row arow[4];
-  const bf16_t* brow[4];
+  constexpr int RS = TL::RS;
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
+  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
+  typename AS::BRow arow[AR];
+  uint32_t boffr[BR];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    arow[i] = as.row(m0 + lr + 32 * i);
-    const int n = n0 + lr + 32 * i;
-    brow[i] = n < N ? Bw + (int64_t)n * K : nullptr;
+  for (int i = 0; i < AR; ++i) arow[i] = as.brow(m0 + lr + RS * i);
+#pragma unroll
+  for (int i = 0; i < BR; ++i) {
+    const int n = n0 + lr + RS * i;
+    boffr[i] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
   }
-  uint4 ra[4], rb[4];
-  auto gload = [&](int kt) {
+  u32x4_t ra[2][AR], rb[2][BR];  // register sets (the second one only with two-deep prefetch)
+  auto gload = [&](int kt, int set) {
     const int k = kt * BK + c * 8;
     const auto kc = as.kc(k);
     const bool kok = k < K;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ld16(as.ptr(arow[i], kc));
-      rb[i] = ld16((brow[i] && kok) ? brow[i] + k : nullptr);
+    for (int i = 0; i < AR; ++i)
+      ra[set][i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, (int)as.boff(arow[i], kc), 0, 0);
+#pragma unroll
+    for (int i = 0; i < BR; ++i) {
+      const uint32_t off = (kok && boffr[i] != 0x80000000u) ? boffr[i] + (uint32_t)k * 2u : 0x80000000u;
+      rb[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, (int)off, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, int set) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = lr + 32 * i;
-      const int pc = c ^ (r & 7);
-      *reinterpret_cast<uint4*>(&sA[buf][r * BK + pc * 8]) = ra[i];
-      *reinterpret_cast<uint4*>(&sB[buf][r * BK + pc * 8]) = rb[i];
+    for (int i = 0; i < AR; ++i) {
+      const int r = lr + RS * i;
+      *reinterpret_cast<u32x4_t*>(&sA[buf * BM * BK + r * BK + ((c ^ swz(r)) * 8)]) = ra[set][i];
+    }
+#pragma unroll
+    for (int i = 0; i < BR; ++i) {
+      const int r = lr + RS * i;
+      *reinterpret_cast<u32x4_t*>(&sB[buf * BN * BK + r * BK + ((c ^ swz(r)) * 8)]) = rb[set][i];
     }
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+  // MFMA operand rows of this lane (the swizzle key depends on row % 16 = l32 % 16 only)
+  const int arow0 = wm * TL::WTM + l32;
+  const int brow0 = wn * TL::WTN + l32;
+  const int sw = swz(l32);
+  bf16x8_t af[2][TM], bfr[2][TN];
+  auto fload = [&](int buf, int ks, int slot) {
+    const bf16_t* pa = sA + buf * BM * BK + arow0 * BK;
+    const bf16_t* pb = sB + buf * BN * BK + brow0 * BK;
+    const int ch = ((ks * 2 + half) ^ sw) * 8;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[slot][i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * BK + ch);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[slot][j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * BK + ch);
+  };
+
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][i], bfr[slot][j], acc[i][j],
+                                                            0, 0, 0);
+  };
+  constexpr int KS = BK / 16;
   const int nk = (K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  if constexpr ((SCHED & 5) == 0) {
+    gload(0, 0);
+    sstore(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) gload(kt + 1, 0);
+      fload(cur, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t af[2], bfr[2];
-      const int ch = ks * 2 + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[cur][r * BK + ((ch ^ (r & 7)) * 8)]);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) fload(cur, ks + 1, (ks + 1) & 1);
+        mfmas(ks & 1);
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + j * 32 + (lane & 31);
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&sB[cur][r * BK + ((ch ^ (r & 7)) * 8)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      if (kt + 1 < nk) sstore(cur ^ 1, 0);
+      __syncthreads();
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
+  } else if constexpr ((SCHED & 4) == 0) {
+    gload(0, 0);
+    sstore(0, 0);
+    __syncthreads();
+    fload(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) gload(kt + 1, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+          fload(cur, ks + 1, (ks + 1) & 1);
+        } else if (more) {
+          sstore(cur ^ 1, 0);
+          __syncthreads();
+          fload(cur ^ 1, 0, 0);
+        }
+        if constexpr (SCHED & 2) {
+          __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // DS reads (next K-step)
+          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);  // MFMAs (this K-step)
+        }
+        mfmas(ks & 1);
+      }
+    }
+    __syncthreads();  // the epilogue reuses the tile buffers as staging
+  } else {
+    // two-deep register prefetch: tile t lives in register set t & 1 from its load (issued two
+    // tiles ahead) until its LDS store at the end of tile t - 1
+    gload(0, 0);
+    sstore(0, 0);
+    __syncthreads();
+    if (nk > 1) gload(1, 1);
+    fload(0, 0, 0);
+    auto iter = [&](int kt, auto parity) {
+      constexpr int P = decltype(parity)::value;  // kt & 1
+      const bool more = kt + 1 < nk;
+      if (kt + 2 < nk) gload(kt + 2, P);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+          fload(P, ks + 1, (ks + 1) & 1);
+        } else if (more) {
+          sstore(1 - P, 1 - P);
+          __syncthreads();
+          fload(1 - P, 0, 0);
+        }
+        if constexpr (SCHED & 2) {
+          __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+        }
+        mfmas(ks & 1);
+      }
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      iter(kt, std::integral_constant<int, 0>());
+      if (kt + 1 < nk) iter(kt + 1, std::integral_constant<int, 1>());
+    }
     __syncthreads();
   }
 
-  // epilogue: element v of a 32x32 block sits at row 8*(v/4) + 4*(lane/32) + v%4, col lane%32
+  // epilogue through LDS: each wave writes SR rows of its accumulators row-major, then reads
+  // them back four columns per lane for 16-byte (fp32) / 8-byte (bf16) stores
+  constexpr int LDW = WTN + 4;
+  float* stg = reinterpret_cast<float*>(smem) + wv * SR * LDW;
+  const int wcol = n0 + wn * TL::WTN;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const int64_t off = om.off(row);
-      if (off < 0) continue;
-      if constexpr (EPI == EPI_SWIGLU) {
-        if (n0 + wn * 64 >= N) continue;  // this wave's gate|up column pair lies past N
-        const int col = (n0 + wn * 64) / 2 + (lane & 31);
-        const float g = acc[i][0][v], u = acc[i][1][v];
-        StoreT<OT>::put(reinterpret_cast<OT*>(ep.C) + off + col, silu(g) * u);
-      } else {
+  for (int hs = 0; hs < 32 / SR; ++hs) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-          if (col >= N) continue;
-          if constexpr (EPI == EPI_PE) {
-            reinterpret_cast<float*>(ep.C)[off + col] =
-                acc[i][j][v] + ep.pe[(int64_t)ep.tok_pos[row] * pe_ld + col];
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
+        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
+      }
+    __syncthreads();
+    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int Q = WTN / 8;  // 4-wide outputs per row
+      for (int idx = lane; idx < SR * Q; idx += 64) {
+        const int r = idx / Q, q4 = idx - (idx / Q) * Q;
+        const int p = (4 * q4) / 32, jj = (4 * q4) % 32;
+        if (wcol + 64 * p >= N) continue;
+        const int64_t off = om.off(rbase + r);
+        if (off < 0) continue;
+        const float4 g = *reinterpret_cast<const float4*>(stg + r * LDW + 64 * p + jj);
+        const float4 u = *reinterpret_cast<const float4*>(stg + r * LDW + 64 * p + 32 + jj);
+        const int col = (wcol + 64 * p) / 2 + jj;
+        OT* dst = reinterpret_cast<OT*>(ep.C) + off + col;
+        Store4x<OT>::put(dst, silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w);
+      }
+    } else {
+      constexpr int Q = WTN / 4;
+      for (int idx = lane; idx < SR * Q; idx += 64) {
+        const int r = idx / Q, q4 = idx - (idx / Q) * Q;
+        const int col = wcol + 4 * q4;
+        if (col >= N) continue;
+        const int64_t row = rbase + r;
+        const int64_t off = om.off(row);
+        if (off < 0) continue;
+        float4 a = *reinterpret_cast<const float4*>(stg + r * LDW + 4 * q4);
+        if constexpr (EPI == EPI_PE) {
+          const float4 pe = *reinterpret_cast<const float4*>(ep.pe + (int64_t)ep.tok_pos[row] * pe_ld + col);
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col) =
+              make_float4(a.x + pe.x, a.y + pe.y, a.z + pe.z, a.w + pe.w);
+        } else {
+          if (ep.bias) {
+            const float4 b = *reinterpret_cast<const float4*>(ep.bias + col);
+            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+          }
+          if constexpr (EPI == EPI_RESADD) {
+            float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col);
+            const float4 o = *p;
+            *p = make_float4(o.x + a.x, o.y + a.y, o.z + a.z, o.w + a.w);
+          } else if constexpr (EPI == EPI_STORE_F32) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col) = a;
           } else {
-            epi_store<EPI, OT>(ep, off, row, col, acc[i][j][v]);
+            if constexpr (EPI == EPI_BIAS_GELU) {
+              a.x = gelu_erf(a.x); a.y = gelu_erf(a.y); a.z = gelu_erf(a.z); a.w = gelu_erf(a.w);
+            }
+            Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off + col, a.x, a.y, a.z, a.w);
           }
         }
       }
     }
+    __syncthreads();
+  }
   }
 }
 
@@ -280,7 +508,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(AS as, const float* __res
   const int nt = blockIdx.x - (int)(mt * n_tiles);
   const int64_t m0 = mt * FBM;
   const int n0 = nt * FBN;
-  if (!as.tile_live(m0)) return;
+  if (!as.tile_live(m0, FBM)) return;
 
   // loader: 4 consecutive k of one row per thread
   const int lrow = tid >> 2;
@@ -340,15 +568,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(AS as, const float* __res
 // ============================================================================================
 // dispatch
 // ============================================================================================
-template <typename T, class AS, class OM, int EPI, int TAG>
+template <typename T, class TL, class AS, class OM, int EPI, int TAG>
 hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, const EpiP& ep,
                int64_t m_rows, int32_t pe_ld, hipStream_t s) {
   if constexpr (std::is_same<T, bf16_t>::value) {
-    const int n_tiles = (N + BN - 1) / BN;
-    const int64_t m_tiles = (m_rows + BM - 1) / BM;
+    const int n_tiles = (N + TL::BN - 1) / TL::BN;
+    const int64_t m_tiles = (m_rows + TL::BM - 1) / TL::BM;
     if (m_tiles * n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_bf16_kernel<AS, OM, EPI, bf16_t, TAG>), dim3((unsigned)(m_tiles * n_tiles)),
-                       dim3(NTHR), 0, s, as, Bw, N, K, om, ep, n_tiles, pe_ld);
+    hipLaunchKernelGGL((gemm_bf16_kernel<TL, AS, OM, EPI, bf16_t, TAG>),
+                       dim3((unsigned)(m_tiles * n_tiles)), dim3(TL::NT), 0, s, as, Bw, N, K, om, ep,
+                       n_tiles, pe_ld);
   } else {
     if constexpr (EPI == EPI_SWIGLU) {
       return hipErrorInvalidValue;  // the fp32 path applies SwiGLU in a separate kernel
@@ -363,13 +592,28 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
   return hipGetLastError();
 }
 
+// Estimated time of a GEMM on the 256 CUs: whole rounds of tiles times the tile's cost; the
+// 256x256 tile does twice the work of 256x128 at about 1.2x the throughput per tile.
+inline bool use_wide_tile(int64_t M, int64_t N) {
+  const int64_t mt = (M + 255) / 256;
+  const int64_t rl = (mt * ((N + 255) / 256) + 255) / 256;
+  const int64_t rm = (mt * ((N + 127) / 128) + 255) / 256;
+  return rl * 10 <= rm * 6;  // rl * (2 / 1.2) <= rm
+}
+
+// Tile choice (measured on MI355X): eight waves per workgroup so that each SIMD holds two
+// waves and one issues MFMAs while the other waits on its loads: the 256x256 tile (wave tile
+// 128x64) or the 256x128 tile (wave tile 64x64), whichever use_wide_tile estimates faster.
 template <typename T, int TAG, int EPI>
 hipError_t lin(const LinearArgs& a, hipStream_t s) {
   ALinear<T> as{reinterpret_cast<const T*>(a.A), a.lda, a.M, a.K};
   OLinear om{a.M, a.ldc};
   EpiP ep{a.bias, a.C, a.pe, a.tok_pos};
-  return run<T, ALinear<T>, OLinear, EPI, TAG>(as, reinterpret_cast<const T*>(a.W), a.N, a.K, om,
-                                               ep, a.M, EPI == EPI_PE ? a.N : 0, s);
+  const T* Bw = reinterpret_cast<const T*>(a.W);
+  const int pe_ld = EPI == EPI_PE ? a.N : 0;
+  if (use_wide_tile(a.M, a.N))
+    return run<T, TileL8, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+  return run<T, TileM8, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
 }
 
 }  // namespace
@@ -406,20 +650,21 @@ hipError_t launch_linear(const LinearArgs& a, int epi, int tag, hipStream_t s) {
 template <typename T>
 hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T* wpk,
                              const float* bias, int32_t C, T* out, hipStream_t s) {
-  constexpr int TM = std::is_same<T, bf16_t>::value ? BM : FBM;
   const int Fin = level == 2 ? 64 : 32;
   const int Fout = Fin / 2;
   const int Lin_max = level == 2 ? 4 * g.W : 2 * g.W;
   const int Lout_max = Lin_max / 2;
-  const int rows = Lout_max * Fout;
-  const int rows_per_win = ((rows + TM - 1) / TM) * TM;
-  AConv<T> as{in, g.wins, C, Fin, Fout, Lin_max, level, rows_per_win, 9 * C};
-  OConv om{g.wins, rows_per_win, Fout, C, level, Lout_max};
-  EpiP ep{bias, out, nullptr, nullptr};
+  const int rows_per_win = Lout_max * Fout;
   const int64_t m_rows = (int64_t)g.n_win * rows_per_win;
+  if ((int64_t)g.n_win * Lin_max * Fin * C >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  AConv<T> as{in, g.wins, C, Fin, Fout, Lin_max, level, rows_per_win, 9 * C, m_rows,
+              (int64_t)g.n_win * Lin_max * Fin * C * (int64_t)sizeof(T)};
+  OConv om{g.wins, rows_per_win, Fout, C, level, Lout_max, m_rows};
+  EpiP ep{bias, out, nullptr, nullptr};
+  // 480 output channels: two 256-wide column tiles (the second one 224 wide)
   if (level == 2)
-    return run<T, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV2>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
-  return run<T, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV3>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
+    return run<T, TileL8, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV2>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
+  return run<T, TileL8, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV3>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
 }
 
 template hipError_t launch_linear<bf16_t>(const LinearArgs&, int, int, hipStream_t);

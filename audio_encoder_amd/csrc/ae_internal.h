@@ -39,7 +39,21 @@ template <> struct StoreT<bf16_t> {
   __device__ static inline void put(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
-__device__ inline float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// Exact-form GELU x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)).  erfc(z) for z >= 0 is evaluated
+// with Abramowitz & Stegun's formula 7.1.26 (|error in erf| <= 1.5e-7): erfc(z) ~ t (a1 + t (a2 +
+// t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z).  The negative branch uses erfc directly,
+// so the left tail keeps its relative accuracy instead of cancelling 1 + erf.
+__device__ inline float gelu_erf(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __frcp_rn(fmaf(0.3275911f, z, 1.0f));
+  float p = fmaf(t, 1.061405429f, -1.453152027f);
+  p = fmaf(t, p, 1.421413741f);
+  p = fmaf(t, p, -0.284496736f);
+  p = fmaf(t, p, 0.254829592f);
+  const float erfc_z = p * t * __expf(-z * z);
+  const float hx = 0.5f * x;
+  return x >= 0.0f ? fmaf(-hx, erfc_z, x) : hx * erfc_z;
+}
 __device__ inline float silu(float x) { return x / (1.0f + expf(-x)); }
 
 // ------------------------------------------------------------------------------------------
