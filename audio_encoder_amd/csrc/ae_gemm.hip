@@ -188,30 +188,42 @@ __device__ inline void epi_store(const EpiP& ep, int64_t off, int64_t row, int c
 // ============================================================================================
 // bf16 MFMA kernel
 // ============================================================================================
-constexpr int BK = 64, NTHR = 256;
+constexpr int NTHR = 256;
 
 __device__ inline uint4 ld16(const bf16_t* p) {
   return p ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Block tile BM x BN, WGM x WGN waves, each owning (BM/WGM) x (BN/WGN) as TM x TN blocks of
-// 32x32 MFMA output.
-template <int BM_, int BN_, int WGM_, int WGN_>
+// Block tile BM x BN x BK, WGM x WGN waves, each owning (BM/WGM) x (BN/WGN) as TM x TN blocks
+// of 32x32 MFMA output.  MINB workgroups are meant to share a CU (occupancy hint).  NPF register
+// sets form a ring of K tiles in flight from HBM/L2, so a tile's loads are issued NPF tiles
+// before it is written to LDS (the global load latency exceeds one tile of MFMA work).
+template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int MINB_ = 1, int NPF_ = 1>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_, MINB = MINB_;
+  static constexpr int NPF = NPF_;  // K tiles in flight between global load and LDS store
   static constexpr int NW = WGM * WGN, NT = 64 * NW;  // waves, threads
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  static constexpr int RS = NT / 8;                    // rows covered by one loader pass
-  static constexpr int AR = BM / RS, BR = BN / RS;     // 16-byte chunks per thread per K step
+  static constexpr int CPR = BK / 8;                   // 16-byte chunks per tile row
+  static constexpr int RS = NT / CPR;                  // rows covered by one loader pass
+  static constexpr int AR = BM / RS, BR = BN / RS;     // chunks per thread per K step
   static_assert(TM * 32 == WTM && TN * 32 == WTN && AR * RS == BM && BR * RS == BN, "tile");
+  static_assert(BK == 32 || BK == 64, "BK");
 };
 using TileL = Tile<256, 256, 2, 2>;   // 4 waves, wave tile 128 x 128
 using TileL8 = Tile<256, 256, 2, 4>;  // 8 waves, wave tile 128 x 64 (two waves per SIMD)
 using TileL8b = Tile<256, 256, 4, 2>; // 8 waves, wave tile 64 x 128
 using TileM = Tile<256, 128, 2, 2>;   // 4 waves, wave tile 128 x 64
 using TileM8 = Tile<256, 128, 4, 2>;  // 8 waves, wave tile 64 x 64
-using TileC = Tile<256, 160, 4, 1>;   // 4 waves, wave tile 64 x 160 (480-channel convs)
+using TileMk = Tile<256, 128, 2, 2, 32, 2>;  // 4 waves, BK 32, two workgroups per CU
+using TileSk = Tile<128, 128, 2, 2, 32, 3>;  // 4 waves, BK 32, three workgroups per CU
+using TileS = Tile<128, 128, 2, 2, 64, 2>;   // 4 waves, BK 64, two workgroups per CU
+using TileSk3 = Tile<128, 128, 2, 2, 32, 3, 3>;  // + 3 tiles in flight
+using TileSk2 = Tile<128, 128, 2, 2, 32, 3, 2>;
+using TileMk3 = Tile<256, 128, 2, 2, 32, 2, 3>;
+using TileM83 = Tile<256, 128, 4, 2, 32, 1, 3>;  // 8 waves, BK 32
+using TileL83 = Tile<256, 256, 2, 4, 32, 1, 2>;  // 8 waves, BK 32, 2 in flight
 
 // Workgroups are dispatched round-robin over the 8 XCDs; remap so that consecutive logical
 // tiles (same A rows, neighbouring B columns) run on the same XCD and share its L2.
@@ -223,10 +235,69 @@ __device__ inline int64_t xcd_remap(int64_t bid, int64_t G) {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// LDS tile rows are 128 bytes (BK = 64 bf16).  The 16-byte chunk index is XORed with
-// (row >> 1) & 7 so that 16 consecutive rows at one logical chunk cover all 64 banks
-// (row parity selects the bank half, the XOR spreads the 8 chunk slots).
-__device__ __host__ constexpr int swz(int r) { return (r >> 1) & 7; }
+// Epilogue of SR staged accumulator rows (row-major, stride LDW floats) of one wave: rows
+// rbase.., columns wcol..wcol+WTN-1.  Each lane handles 4 consecutive columns per step.
+template <int EPI, typename OT, int WTN, int SR, class OM>
+__device__ inline void epilogue_rows(const float* stg, int LDW, int64_t rbase, int wcol, int N,
+                                     const OM& om, const EpiP& ep, int pe_ld, int lane) {
+    if constexpr (EPI == EPI_SWIGLU) {
+    constexpr int Q = WTN / 8;  // 4-wide outputs per row
+    for (int idx = lane; idx < SR * Q; idx += 64) {
+      const int r = idx / Q, q4 = idx - (idx / Q) * Q;
+      const int p = (4 * q4) / 32, jj = (4 * q4) % 32;
+      if (wcol + 64 * p >= N) continue;
+      const int64_t off = om.off(rbase + r);
+      if (off < 0) continue;
+      const float4 g = *reinterpret_cast<const float4*>(stg + r * LDW + 64 * p + jj);
+      const float4 u = *reinterpret_cast<const float4*>(stg + r * LDW + 64 * p + 32 + jj);
+      const int col = (wcol + 64 * p) / 2 + jj;
+      OT* dst = reinterpret_cast<OT*>(ep.C) + off + col;
+      Store4x<OT>::put(dst, silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w);
+    }
+  } else {
+    constexpr int Q = WTN / 4;
+    for (int idx = lane; idx < SR * Q; idx += 64) {
+      const int r = idx / Q, q4 = idx - (idx / Q) * Q;
+      const int col = wcol + 4 * q4;
+      if (col >= N) continue;
+      const int64_t row = rbase + r;
+      const int64_t off = om.off(row);
+      if (off < 0) continue;
+      float4 a = *reinterpret_cast<const float4*>(stg + r * LDW + 4 * q4);
+      if constexpr (EPI == EPI_PE) {
+        const float4 pe = *reinterpret_cast<const float4*>(ep.pe + (int64_t)ep.tok_pos[row] * pe_ld + col);
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col) =
+            make_float4(a.x + pe.x, a.y + pe.y, a.z + pe.z, a.w + pe.w);
+      } else {
+        if (ep.bias) {
+          const float4 b = *reinterpret_cast<const float4*>(ep.bias + col);
+          a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+        }
+        if constexpr (EPI == EPI_RESADD) {
+          float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col);
+          const float4 o = *p;
+          *p = make_float4(o.x + a.x, o.y + a.y, o.z + a.z, o.w + a.w);
+        } else if constexpr (EPI == EPI_STORE_F32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col) = a;
+        } else {
+          if constexpr (EPI == EPI_BIAS_GELU) {
+            a.x = gelu_erf(a.x); a.y = gelu_erf(a.y); a.z = gelu_erf(a.z); a.w = gelu_erf(a.w);
+          }
+          Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off + col, a.x, a.y, a.z, a.w);
+        }
+      }
+    }
+  }
+}
+
+
+
+// LDS tile rows are BK*2 bytes.  The 16-byte chunk index is XORed with a row hash so that 16
+// consecutive rows at one logical chunk cover all 64 banks: for 128-byte rows (BK 64) the row
+// parity selects the bank half and (row >> 1) & 7 spreads the 8 chunk slots; for 64-byte rows
+// (BK 32) row % 4 selects the bank quarter and (row >> 2) & 3 spreads the 4 slots.
+template <int BK>
+__device__ __host__ constexpr int swz(int r) { return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3; }
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
   // raw buffer: stride 0, range check against `bytes`; dword3 0x00020000 (32-bit data format)
@@ -235,6 +306,12 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes)
 }
 
 // TAG only names the call site (one kernel symbol per role, so profiles separate them)
+#ifndef AE_GEMM_CPOL
+#define AE_GEMM_CPOL 0  // cache policy bits of the tile loads
+#endif
+#ifndef AE_GEMM_GROUP_M
+#define AE_GEMM_GROUP_M 8
+#endif
 #ifndef AE_GEMM_SCHED
 #define AE_GEMM_SCHED 3
 #endif
@@ -243,11 +320,11 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes)
 // after the barrier, covering the LDS reads of the next tile's first K-step).  SCHED bit 1:
 // order each K-step as [LDS reads of the next K-step][MFMAs of this one] for the scheduler.
 template <class TL, class AS, class OM, int EPI, typename OT, int TAG, int SCHED = AE_GEMM_SCHED>
-__global__ __launch_bounds__(TL::NT) void gemm_bf16_kernel(AS as, const bf16_t* __restrict__ Bw,
+__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_bf16_kernel(AS as, const bf16_t* __restrict__ Bw,
                                                          int32_t N, int32_t K, OM om, EpiP ep,
-                                                         int32_t n_tiles, int32_t pe_ld) {
+                                                         int32_t n_tiles, int32_t pe_ld, int32_t gm) {
   constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN, AR = TL::AR, BR = TL::BR;
-  constexpr int WTN = TL::WTN;
+  constexpr int WTN = TL::WTN, BK = TL::BK, CPR = TL::CPR;
   constexpr int SMEM = 2 * (BM + BN) * BK;  // bf16 elements: double-buffered A and B tiles
   // epilogue staging: SR rows of each wave's tile at a time (32, or 16 when 32 do not fit)
   constexpr int SR = (TL::NW * 32 * (WTN + 4) * 4 <= SMEM * 2) ? 32 : 16;
@@ -260,17 +337,25 @@ __global__ __launch_bounds__(TL::NT) void gemm_bf16_kernel(AS as, const bf16_t* 
   const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
   const int wv = tid >> 6;
   const int wm = wv / TL::WGN, wn = wv % TL::WGN;
+  // tile order: XCD-contiguous ranges, then groups of `gm` M-tiles swept column by column so the
+  // tiles an XCD runs at once share a few A row-panels and B column-panels in its L2
   const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t mt = tile / n_tiles;
-  const int nt = (int)(tile - mt * n_tiles);
+  const int64_t m_tiles = gridDim.x / n_tiles;
+  const int64_t gsize = (int64_t)gm * n_tiles;
+  const int64_t g = tile / gsize;
+  const int64_t first_m = g * gm;
+  const int64_t gh = min<int64_t>(m_tiles - first_m, gm);
+  const int64_t in_g = tile - g * gsize;
+  const int64_t mt = first_m + in_g % gh;
+  const int nt = (int)(in_g / gh);
   const int64_t m0 = mt * BM;
   const int n0 = nt * BN;
   if (!as.tile_live(m0, BM)) return;
 
   // global -> register loader: 16-byte chunk c of rows lr + 32*i, via buffer loads whose
   // out-of-range offsets return zero (ragged M/N tails, conv padding taps)
-  const int c = tid & 7;
-  const int lr = tid >> 3;
+  const int c = tid % CPR;
+  const int lr = tid / CPR;
   constexpr int RS = TL::RS;
   const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
   const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
@@ -283,30 +368,31 @@ __global__ __launch_bounds__(TL::NT) void gemm_bf16_kernel(AS as, const bf16_t* 
     const int n = n0 + lr + RS * i;
     boffr[i] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
   }
-  u32x4_t ra[2][AR], rb[2][BR];  // register sets (the second one only with two-deep prefetch)
+  constexpr int NSET = TL::NPF > 2 ? TL::NPF : 2;
+  u32x4_t ra[NSET][AR], rb[NSET][BR];  // register sets
   auto gload = [&](int kt, int set) {
     const int k = kt * BK + c * 8;
     const auto kc = as.kc(k);
     const bool kok = k < K;
 #pragma unroll
     for (int i = 0; i < AR; ++i)
-      ra[set][i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, (int)as.boff(arow[i], kc), 0, 0);
+      ra[set][i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, (int)as.boff(arow[i], kc), 0, AE_GEMM_CPOL);
 #pragma unroll
     for (int i = 0; i < BR; ++i) {
       const uint32_t off = (kok && boffr[i] != 0x80000000u) ? boffr[i] + (uint32_t)k * 2u : 0x80000000u;
-      rb[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, (int)off, 0, 0);
+      rb[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, (int)off, 0, AE_GEMM_CPOL);
     }
   };
   auto sstore = [&](int buf, int set) {
 #pragma unroll
     for (int i = 0; i < AR; ++i) {
       const int r = lr + RS * i;
-      *reinterpret_cast<u32x4_t*>(&sA[buf * BM * BK + r * BK + ((c ^ swz(r)) * 8)]) = ra[set][i];
+      *reinterpret_cast<u32x4_t*>(&sA[buf * BM * BK + r * BK + ((c ^ swz<BK>(r)) * 8)]) = ra[set][i];
     }
 #pragma unroll
     for (int i = 0; i < BR; ++i) {
       const int r = lr + RS * i;
-      *reinterpret_cast<u32x4_t*>(&sB[buf * BN * BK + r * BK + ((c ^ swz(r)) * 8)]) = rb[set][i];
+      *reinterpret_cast<u32x4_t*>(&sB[buf * BN * BK + r * BK + ((c ^ swz<BK>(r)) * 8)]) = rb[set][i];
     }
   };
 
@@ -321,7 +407,7 @@ __global__ __launch_bounds__(TL::NT) void gemm_bf16_kernel(AS as, const bf16_t* 
   // MFMA operand rows of this lane (the swizzle key depends on row % 16 = l32 % 16 only)
   const int arow0 = wm * TL::WTM + l32;
   const int brow0 = wn * TL::WTN + l32;
-  const int sw = swz(l32);
+  const int sw = swz<BK>(l32);
   bf16x8_t af[2][TM], bfr[2][TN];
   auto fload = [&](int buf, int ks, int slot) {
     const bf16_t* pa = sA + buf * BM * BK + arow0 * BK;
@@ -343,7 +429,46 @@ __global__ __launch_bounds__(TL::NT) void gemm_bf16_kernel(AS as, const bf16_t* 
   };
   constexpr int KS = BK / 16;
   const int nk = (K + BK - 1) / BK;
-  if constexpr ((SCHED & 5) == 0) {
+  if constexpr (TL::NPF > 1) {
+    // register ring: tile t is loaded into set t % NPF right after that set's previous tile was
+    // written to LDS, i.e. NPF tiles of MFMA work before it is needed
+    constexpr int NPF = TL::NPF;
+#pragma unroll
+    for (int p = 0; p < NPF; ++p)
+      if (p < nk) gload(p, p);
+    sstore(0, 0);
+    if (NPF < nk) gload(NPF, 0);
+    __syncthreads();
+    fload(0, 0, 0);
+    auto iter = [&](int kt, auto ph) {
+      constexpr int P = decltype(ph)::value;  // kt % NPF
+      constexpr int PN = (P + 1) % NPF;       // set of tile kt + 1
+      const bool more = kt + 1 < nk;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+          fload(kt & 1, ks + 1, (ks + 1) & 1);
+        } else if (more) {
+          sstore((kt + 1) & 1, PN);
+          if (kt + 1 + NPF < nk) gload(kt + 1 + NPF, PN);
+          __syncthreads();
+          fload((kt + 1) & 1, 0, 0);
+        }
+        if constexpr (SCHED & 2) {
+          __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+        }
+        mfmas(ks & 1);
+      }
+    };
+    for (int kt = 0; kt < nk; kt += NPF) {
+      iter(kt, std::integral_constant<int, 0>());
+      if constexpr (NPF > 1) if (kt + 1 < nk) iter(kt + 1, std::integral_constant<int, 1 % NPF>());
+      if constexpr (NPF > 2) if (kt + 2 < nk) iter(kt + 2, std::integral_constant<int, 2 % NPF>());
+      if constexpr (NPF > 3) if (kt + 3 < nk) iter(kt + 3, std::integral_constant<int, 3 % NPF>());
+    }
+    __syncthreads();
+  } else if constexpr ((SCHED & 5) == 0) {
     gload(0, 0);
     sstore(0, 0);
     __syncthreads();
@@ -438,54 +563,151 @@ __global__ __launch_bounds__(TL::NT) void gemm_bf16_kernel(AS as, const bf16_t* 
       }
     __syncthreads();
     const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
-    if constexpr (EPI == EPI_SWIGLU) {
-      constexpr int Q = WTN / 8;  // 4-wide outputs per row
-      for (int idx = lane; idx < SR * Q; idx += 64) {
-        const int r = idx / Q, q4 = idx - (idx / Q) * Q;
-        const int p = (4 * q4) / 32, jj = (4 * q4) % 32;
-        if (wcol + 64 * p >= N) continue;
-        const int64_t off = om.off(rbase + r);
-        if (off < 0) continue;
-        const float4 g = *reinterpret_cast<const float4*>(stg + r * LDW + 64 * p + jj);
-        const float4 u = *reinterpret_cast<const float4*>(stg + r * LDW + 64 * p + 32 + jj);
-        const int col = (wcol + 64 * p) / 2 + jj;
-        OT* dst = reinterpret_cast<OT*>(ep.C) + off + col;
-        Store4x<OT>::put(dst, silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w);
-      }
-    } else {
-      constexpr int Q = WTN / 4;
-      for (int idx = lane; idx < SR * Q; idx += 64) {
-        const int r = idx / Q, q4 = idx - (idx / Q) * Q;
-        const int col = wcol + 4 * q4;
-        if (col >= N) continue;
-        const int64_t row = rbase + r;
-        const int64_t off = om.off(row);
-        if (off < 0) continue;
-        float4 a = *reinterpret_cast<const float4*>(stg + r * LDW + 4 * q4);
-        if constexpr (EPI == EPI_PE) {
-          const float4 pe = *reinterpret_cast<const float4*>(ep.pe + (int64_t)ep.tok_pos[row] * pe_ld + col);
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col) =
-              make_float4(a.x + pe.x, a.y + pe.y, a.z + pe.z, a.w + pe.w);
-        } else {
-          if (ep.bias) {
-            const float4 b = *reinterpret_cast<const float4*>(ep.bias + col);
-            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-          }
-          if constexpr (EPI == EPI_RESADD) {
-            float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col);
-            const float4 o = *p;
-            *p = make_float4(o.x + a.x, o.y + a.y, o.z + a.z, o.w + a.w);
-          } else if constexpr (EPI == EPI_STORE_F32) {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col) = a;
-          } else {
-            if constexpr (EPI == EPI_BIAS_GELU) {
-              a.x = gelu_erf(a.x); a.y = gelu_erf(a.y); a.z = gelu_erf(a.z); a.w = gelu_erf(a.w);
-            }
-            Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off + col, a.x, a.y, a.z, a.w);
-          }
-        }
-      }
+    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
+    __syncthreads();
+  }
+  }
+}
+
+// Direct-to-LDS variant: the tile loads are buffer_load_dwordx4 ... lds (gfx950 LDS DMA, 16
+// bytes per lane), so tile data never passes through VGPRs.  One LDS DMA instruction fills
+// 1 KB of LDS at (wave-uniform base + 16 * lane); each lane therefore fetches the global chunk
+// whose swizzled LDS slot is base + 16 * lane.  Per K tile:
+//   wait for this tile's DMA, barrier -> read all MFMA fragments of the tile into registers ->
+//   issue the DMA of the next tile into the other buffer -> MFMAs.
+// The DMA of tile kt+1 thus overlaps the MFMAs of tile kt, and the compiler's conservative
+// wait before LDS reads never falls between a DMA and the fragment reads it could delay.
+template <class TL, class AS, class OM, int EPI, typename OT, int TAG>
+__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const bf16_t* __restrict__ Bw,
+                                                                   int32_t N, int32_t K, OM om, EpiP ep,
+                                                                   int32_t n_tiles, int32_t pe_ld, int32_t gm) {
+  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
+  constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
+  constexpr int SMEM = 2 * (BM + BN) * BK;
+  constexpr int SR = (NW * 32 * (WTN + 4) * 4 <= SMEM * 2) ? 32 : 16;
+  static_assert(NW * SR * (WTN + 4) * 4 <= SMEM * 2, "epilogue staging must fit in the tiles");
+  constexpr int ROWS_PER_DMA = 1024 / (BK * 2);           // tile rows filled by one instruction
+  constexpr int ADMA = BM / ROWS_PER_DMA / NW;            // DMA instructions per wave per tile
+  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
+  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
+  constexpr int KS = BK / 16;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM];
+  bf16_t* const sA = smem;
+  bf16_t* const sB = smem + 2 * BM * BK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
+  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t m_tiles = gridDim.x / n_tiles;
+  const int64_t gsize = (int64_t)gm * n_tiles;
+  const int64_t g = tile / gsize;
+  const int64_t first_m = g * gm;
+  const int64_t gh = min<int64_t>(m_tiles - first_m, gm);
+  const int64_t in_g = tile - g * gsize;
+  const int64_t mt = first_m + in_g % gh;
+  const int nt = (int)(in_g / gh);
+  const int64_t m0 = mt * BM;
+  const int n0 = nt * BN;
+  if (!as.tile_live(m0, BM)) return;
+
+  // lane -> (tile row, logical chunk) of each DMA instruction of this wave
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
+  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
+  constexpr int CPR = BK / 8;
+  typename AS::BRow arow[ADMA];
+  int achunk[ADMA];
+  uint32_t boffr[BDMA];
+  int bchunk[BDMA];
+#pragma unroll
+  for (int j = 0; j < ADMA; ++j) {
+    const int r = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
+    achunk[j] = (lane % CPR) ^ swz<BK>(r);
+    arow[j] = as.brow(m0 + r);
+  }
+#pragma unroll
+  for (int j = 0; j < BDMA; ++j) {
+    const int r = (wv * BDMA + j) * ROWS_PER_DMA + lane / CPR;
+    bchunk[j] = (lane % CPR) ^ swz<BK>(r);
+    const int n = n0 + r;
+    boffr[j] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
+  }
+  auto dma = [&](int kt, int buf) {
+#pragma unroll
+    for (int j = 0; j < ADMA; ++j) {
+      const int k = kt * BK + achunk[j] * 8;
+      const uint32_t off = as.boff(arow[j], as.kc(k));
+      bf16_t* dst = sA + buf * BM * BK + (wv * ADMA + j) * ROWS_PER_DMA * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
     }
+#pragma unroll
+    for (int j = 0; j < BDMA; ++j) {
+      const int k = kt * BK + bchunk[j] * 8;
+      const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
+      bf16_t* dst = sB + buf * BN * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int arow0 = wm * TL::WTM + l32;
+  const int brow0 = wn * TL::WTN + l32;
+  const int sw = swz<BK>(l32);
+  bf16x8_t af[KS][TM], bfr[KS][TN];
+  const int nk = (K + BK - 1) / BK;
+  dma(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA of tile kt has landed
+    __syncthreads();                     // every wave's DMA landed; buffer cur^1 is free
+    const bf16_t* pa = sA + cur * BM * BK + arow0 * BK;
+    const bf16_t* pb = sB + cur * BN * BK + brow0 * BK;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch = ((ks * 2 + half) ^ sw) * 8;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[ks][i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * BK + ch);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[ks][j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * BK + ch);
+    }
+    if (kt + 1 < nk) dma(kt + 1, cur ^ 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+  }
+  __syncthreads();
+
+  constexpr int LDW = WTN + 4;
+  float* stg = reinterpret_cast<float*>(smem) + wv * SR * LDW;
+  const int wcol = n0 + wn * TL::WTN;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+  for (int hs = 0; hs < 32 / SR; ++hs) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
+        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
+      }
+    __syncthreads();
+    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
+    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
     __syncthreads();
   }
   }
@@ -575,9 +797,9 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
     const int n_tiles = (N + TL::BN - 1) / TL::BN;
     const int64_t m_tiles = (m_rows + TL::BM - 1) / TL::BM;
     if (m_tiles * n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_bf16_kernel<TL, AS, OM, EPI, bf16_t, TAG>),
+    hipLaunchKernelGGL((gemm_dtl_kernel<TL, AS, OM, EPI, bf16_t, TAG>),
                        dim3((unsigned)(m_tiles * n_tiles)), dim3(TL::NT), 0, s, as, Bw, N, K, om, ep,
-                       n_tiles, pe_ld);
+                       n_tiles, pe_ld, AE_GEMM_GROUP_M);
   } else {
     if constexpr (EPI == EPI_SWIGLU) {
       return hipErrorInvalidValue;  // the fp32 path applies SwiGLU in a separate kernel
@@ -592,18 +814,14 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
   return hipGetLastError();
 }
 
-// Estimated time of a GEMM on the 256 CUs: whole rounds of tiles times the tile's cost; the
-// 256x256 tile does twice the work of 256x128 at about 1.2x the throughput per tile.
-inline bool use_wide_tile(int64_t M, int64_t N) {
-  const int64_t mt = (M + 255) / 256;
-  const int64_t rl = (mt * ((N + 255) / 256) + 255) / 256;
-  const int64_t rm = (mt * ((N + 127) / 128) + 255) / 256;
-  return rl * 10 <= rm * 6;  // rl * (2 / 1.2) <= rm
-}
+// Tile choice (measured on MI355X with the shapes of the tower, M = 6000): the 256x256 tile
+// (8 waves, two per SIMD) for the wide projections (N >= 4096) and N = 2048 (long K), the
+// 128x128 tile with BK 32 and three workgroups per CU for N = 1280 and N = 3840, where 256x256
+// tiles leave part of the 256 CUs idle in the last round.
+using TileWide = Tile<256, 256, 2, 4, 64, 1>;
+using TileNarrow = Tile<128, 128, 2, 2, 32, 3>;
+inline bool use_wide_tile(int64_t /*M*/, int64_t N) { return N >= 4096 || N == 2048; }
 
-// Tile choice (measured on MI355X): eight waves per workgroup so that each SIMD holds two
-// waves and one issues MFMAs while the other waits on its loads: the 256x256 tile (wave tile
-// 128x64) or the 256x128 tile (wave tile 64x64), whichever use_wide_tile estimates faster.
 template <typename T, int TAG, int EPI>
 hipError_t lin(const LinearArgs& a, hipStream_t s) {
   ALinear<T> as{reinterpret_cast<const T*>(a.A), a.lda, a.M, a.K};
@@ -612,8 +830,8 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
   const T* Bw = reinterpret_cast<const T*>(a.W);
   const int pe_ld = EPI == EPI_PE ? a.N : 0;
   if (use_wide_tile(a.M, a.N))
-    return run<T, TileL8, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
-  return run<T, TileM8, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+    return run<T, TileWide, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+  return run<T, TileNarrow, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
 }
 
 }  // namespace
@@ -663,8 +881,8 @@ hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T*
   EpiP ep{bias, out, nullptr, nullptr};
   // 480 output channels: two 256-wide column tiles (the second one 224 wide)
   if (level == 2)
-    return run<T, TileL8, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV2>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
-  return run<T, TileL8, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV3>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
+    return run<T, TileWide, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV2>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
+  return run<T, TileWide, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV3>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
 }
 
 template hipError_t launch_linear<bf16_t>(const LinearArgs&, int, int, hipStream_t);
