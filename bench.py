@@ -83,27 +83,52 @@ def make_input(workload: str):
     raise ValueError(workload)
 
 
-def cpu_baseline(pcm0, weights, cfg, max_windows: int = 2) -> dict:
-    """The float64 oracle on the first `max_windows` 8 s windows of clip 0 (about 10-30 s of
-    CPU work), scaled to audio-seconds per second."""
+def measured_traffic(role: str, cfg_note: str = "full-size tower, 16 x 30 s clips"):
+    """HBM bytes per launch of `role` from the committed counter summary, or None when the
+    GEMM source changed since the counters were taken (or no summary exists)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_full_16x30s.json")
+    src = os.path.join(ROOT, "audio_encoder_amd", "csrc", "ae_gemm.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("gemm_source_sha256") != sha or role not in rec.get("per_launch", {}):
+        return None
+    t = rec["per_launch"][role]
+    return round(t["fetch_bytes"] + t["write_bytes"])
+
+
+def cpu_baseline(pcm, weights, cfg, max_windows: int = 12) -> dict:
+    """The float64 oracle on the first `max_windows` 8 s windows of the batch (clip by clip;
+    about 10-30 s of CPU work), scaled to audio-seconds per second."""
     import numpy as np
 
     import oracle as O
     Wt = O.unpack_weights(weights, O.FULL)
-    t0 = time.perf_counter()
-    mel = O.log_mel(pcm0)
     W = cfg["window_tokens"]
-    plan = O.window_plan(mel.shape[0], W)[:max_windows]
-    frames = 0
-    for w in plan:
-        O.encode_mel(mel[w["start"]:w["start"] + w["L0"]], Wt, O.FULL)
-        frames += w["L0"]
+    t0 = time.perf_counter()
+    frames = nwin = clips = 0
+    for clip in pcm:
+        mel = O.log_mel(clip)
+        clips += 1
+        for w in O.window_plan(mel.shape[0], W):
+            O.encode_mel(mel[w["start"]:w["start"] + w["L0"]], Wt, O.FULL)
+            frames += w["L0"]
+            nwin += 1
+            if nwin >= max_windows:
+                break
+        if nwin >= max_windows:
+            break
     dt = time.perf_counter() - t0
     audio_s = frames * 160 / 16000.0
     cores = len(os.sched_getaffinity(0))
     return {"value": audio_s / dt, "unit": "audio-s/s", "cores": cores, "kind": "oracle",
-            "sample": f"clip 0, first {len(plan)} windows ({audio_s:.0f} s of audio), "
-                      f"float64 NumPy, {dt:.1f} s wall"}
+            "sample": f"first {nwin} windows of the batch ({clips} clips, {audio_s:.0f} s of "
+                      f"audio), float64 NumPy, {dt:.1f} s wall"}
 
 
 def main():
@@ -114,6 +139,9 @@ def main():
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-steps", type=int, default=3)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after the run, launch one plain device copy of this many MiB (a "
+                         "known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); windows are independent, "
@@ -182,14 +210,15 @@ def main():
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "avg_launch_ms": round(avg_ms, 5), "launches_per_step": dom_n // R,
-            "traffic": None}
+            "traffic": measured_traffic(dom) if args.workload == "c2" else None,
+            "algorithmic_unit": "FLOP per launch", "algorithmic_per_launch": per_launch}
     for k, v in stage_ms.items():
         log(f"  {k:10s} {v:8.3f} ms/step")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        cpu = cpu_baseline(pcm_np[0], weights, cfg)
+        cpu = cpu_baseline(pcm_np, weights, cfg)
         log(f"oracle: {cpu['value']:.2f} audio-s/s on {cpu['cores']} cores")
 
     wbytes, ws = enc.memory_stats()
@@ -217,6 +246,14 @@ def main():
         "hbm_bytes": {"weights": wbytes, "workspace_high_water": ws},
     }
     print(json.dumps(line), flush=True)
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {4 * n} bytes read, {4 * n} bytes written")
 
 
 if __name__ == "__main__":
