@@ -713,6 +713,201 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
   }
 }
 
+// MFMA fragments of one K-step (BK = 32: 32-row blocks 2048 bytes apart) read from LDS by one
+// (outputs are early-clobber: no output may share a register with the address inputs)
+// inline-asm block that waits for its own reads before it ends, so the compiler never sees an
+// LDS read that could alias the in-flight LDS DMA of later stages (it would otherwise wait for
+// every outstanding DMA before each read).
+typedef __attribute__((address_space(3))) const void* lds_cptr;
+template <int TM, int TN> struct FragK32;
+template <> struct FragK32<2, 2> {
+  __device__ static inline void load(lds_cptr a, lds_cptr b, bf16x8_t* af, bf16x8_t* bf) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:2048\n\t"
+        "ds_read_b128 %2, %5\n\t"
+        "ds_read_b128 %3, %5 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(bf[0]), "=&v"(bf[1])
+        : "v"(a), "v"(b)
+        : "memory");
+  }
+};
+template <> struct FragK32<4, 2> {
+  __device__ static inline void load(lds_cptr a, lds_cptr b, bf16x8_t* af, bf16x8_t* bf) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %6 offset:2048\n\t"
+        "ds_read_b128 %2, %6 offset:4096\n\t"
+        "ds_read_b128 %3, %6 offset:6144\n\t"
+        "ds_read_b128 %4, %7\n\t"
+        "ds_read_b128 %5, %7 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bf[0]), "=&v"(bf[1])
+        : "v"(a), "v"(b)
+        : "memory");
+  }
+};
+template <> struct FragK32<2, 4> {
+  __device__ static inline void load(lds_cptr a, lds_cptr b, bf16x8_t* af, bf16x8_t* bf) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %6 offset:2048\n\t"
+        "ds_read_b128 %2, %7\n\t"
+        "ds_read_b128 %3, %7 offset:2048\n\t"
+        "ds_read_b128 %4, %7 offset:4096\n\t"
+        "ds_read_b128 %5, %7 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3])
+        : "v"(a), "v"(b)
+        : "memory");
+  }
+};
+
+// Ring-pipelined direct-to-LDS GEMM (BK = 32): NST LDS stages; the DMA of tile kt + NST - 1 is
+// issued right after the barrier of tile kt, so each tile's loads have NST - 1 tiles of MFMA
+// work to land.  Every iteration issues the same number of DMA instructions (tiles past the end
+// read as zero into a stage that is never read again), so "this tile has landed" is the fixed
+// wait vmcnt <= (NST - 2) * (DMA instructions per tile).
+template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG>
+__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ring_kernel(AS as, const bf16_t* __restrict__ Bw,
+                                                                    int32_t N, int32_t K, OM om, EpiP ep,
+                                                                    int32_t n_tiles, int32_t pe_ld, int32_t gm) {
+  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
+  constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
+  static_assert(BK == 32, "ring kernel uses BK = 32");
+  constexpr int STAGE = (BM + BN) * BK;                   // bf16 elements per stage
+  constexpr int SMEM = NST * STAGE;
+  constexpr int SR = (NW * 32 * (WTN + 4) * 4 <= SMEM * 2) ? 32 : 16;
+  static_assert(NW * SR * (WTN + 4) * 4 <= SMEM * 2, "epilogue staging must fit in the tiles");
+  constexpr int ROWS_PER_DMA = 1024 / (BK * 2);           // 16 rows of 64 bytes
+  constexpr int ADMA = BM / ROWS_PER_DMA / NW;
+  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
+  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
+  constexpr int NDMA = ADMA + BDMA;
+  constexpr int VMC = (NST - 2) * NDMA;
+  static_assert(VMC < 64, "vmcnt range");
+  constexpr int WAIT_TILE = (VMC & 15) | (7 << 4) | (15 << 8) | ((VMC >> 4) << 14);
+  constexpr int KS = BK / 16;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
+  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t m_tiles = gridDim.x / n_tiles;
+  const int64_t gsize = (int64_t)gm * n_tiles;
+  const int64_t g = tile / gsize;
+  const int64_t first_m = g * gm;
+  const int64_t gh = min<int64_t>(m_tiles - first_m, gm);
+  const int64_t in_g = tile - g * gsize;
+  const int64_t mt = first_m + in_g % gh;
+  const int nt = (int)(in_g / gh);
+  const int64_t m0 = mt * BM;
+  const int n0 = nt * BN;
+  if (!as.tile_live(m0, BM)) return;
+
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
+  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
+  constexpr int CPR = BK / 8;
+  typename AS::BRow arow[ADMA];
+  int achunk[ADMA];
+  uint32_t boffr[BDMA];
+  int bchunk[BDMA];
+#pragma unroll
+  for (int j = 0; j < ADMA; ++j) {
+    const int r = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
+    achunk[j] = (lane % CPR) ^ swz<BK>(r);
+    arow[j] = as.brow(m0 + r);
+  }
+#pragma unroll
+  for (int j = 0; j < BDMA; ++j) {
+    const int r = (wv * BDMA + j) * ROWS_PER_DMA + lane / CPR;
+    bchunk[j] = (lane % CPR) ^ swz<BK>(r);
+    const int n = n0 + r;
+    boffr[j] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
+  }
+  auto dma = [&](int kt, int stage) {
+    bf16_t* sa = smem + stage * STAGE;
+    bf16_t* sb = sa + BM * BK;
+#pragma unroll
+    for (int j = 0; j < ADMA; ++j) {
+      const int k = kt * BK + achunk[j] * 8;
+      const uint32_t off = as.boff(arow[j], as.kc(k));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra_rsrc, (__attribute__((address_space(3))) void*)(sa + (wv * ADMA + j) * ROWS_PER_DMA * BK),
+          16, (int)off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < BDMA; ++j) {
+      const int k = kt * BK + bchunk[j] * 8;
+      const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb_rsrc, (__attribute__((address_space(3))) void*)(sb + (wv * BDMA + j) * ROWS_PER_DMA * BK),
+          16, (int)off, 0, 0, 0);
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int arow0 = wm * TL::WTM + l32;
+  const int brow0 = wn * TL::WTN + l32;
+  const int sw = swz<BK>(l32);
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t) dma(t, t);
+  int stage = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_s_waitcnt(WAIT_TILE);  // this wave's DMA of tile kt has landed
+    __builtin_amdgcn_s_barrier();           // all waves: tile kt in LDS, tile kt-1 consumed
+    dma(kt + NST - 1, stage == 0 ? NST - 1 : stage - 1);
+    const bf16_t* sa = smem + stage * STAGE;
+    const bf16_t* sb = sa + BM * BK;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch = ((ks * 2 + half) ^ sw) * 8;
+      bf16x8_t af[TM], bfr[TN];
+      FragK32<TM, TN>::load((lds_cptr)(sa + arow0 * BK + ch), (lds_cptr)(sb + brow0 * BK + ch), af, bfr);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    stage = stage + 1 == NST ? 0 : stage + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the trailing zero-fill DMAs have landed
+  __syncthreads();
+
+  constexpr int LDW = WTN + 4;
+  float* stg = reinterpret_cast<float*>(smem) + wv * SR * LDW;
+  const int wcol = n0 + wn * TL::WTN;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+  for (int hs = 0; hs < 32 / SR; ++hs) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
+        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
+      }
+    __syncthreads();
+    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
+    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
+    __syncthreads();
+  }
+  }
+}
+
 // ============================================================================================
 // fp32 VALU kernel (tiny fp32 configuration; not a throughput path)
 // ============================================================================================
@@ -814,13 +1009,27 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
   return hipGetLastError();
 }
 
-// Tile choice (measured on MI355X with the shapes of the tower, M = 6000): the 256x256 tile
-// (8 waves, two per SIMD) for the wide projections (N >= 4096) and N = 2048 (long K), the
-// 128x128 tile with BK 32 and three workgroups per CU for N = 1280 and N = 3840, where 256x256
-// tiles leave part of the 256 CUs idle in the last round.
-using TileWide = Tile<256, 256, 2, 4, 64, 1>;
-using TileNarrow = Tile<128, 128, 2, 2, 32, 3>;
-inline bool use_wide_tile(int64_t /*M*/, int64_t N) { return N >= 4096 || N == 2048; }
+// Tile choice (measured on MI355X with the shapes of the tower, M = 6000): 256x128 tiles with
+// 8 waves (two per SIMD, BK 32) for the wide outputs (N >= 2048: FFN1, head proj2, adapter);
+// 128x128 tiles with BK 64 and two workgroups per CU for N = 1280 and N = 3840 (o-proj, FFN2,
+// conv_out, proj1, QKV), where the wider tile leaves CUs idle in the last round.
+using TileWide = Tile<256, 128, 4, 2, 32, 1>;
+using TileNarrow = Tile<128, 128, 2, 2, 64, 2>;
+inline bool use_wide_tile(int64_t /*M*/, int64_t N) { return N >= 2048 && N != 3840; }
+
+// conv2/conv3 (N = 480 output channels)
+#ifndef AE_CONV_TILE
+#define AE_CONV_TILE 0
+#endif
+#if AE_CONV_TILE == 0
+using TileConv = Tile<256, 128, 4, 2, 32, 1>;
+#elif AE_CONV_TILE == 1
+using TileConv = Tile<256, 256, 2, 4, 64, 1>;
+#elif AE_CONV_TILE == 2
+using TileConv = Tile<128, 128, 2, 2, 64, 2>;
+#else
+using TileConv = Tile<256, 160, 4, 1, 64, 1>;
+#endif
 
 template <typename T, int TAG, int EPI>
 hipError_t lin(const LinearArgs& a, hipStream_t s) {
@@ -879,10 +1088,9 @@ hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T*
               (int64_t)g.n_win * Lin_max * Fin * C * (int64_t)sizeof(T)};
   OConv om{g.wins, rows_per_win, Fout, C, level, Lout_max, m_rows};
   EpiP ep{bias, out, nullptr, nullptr};
-  // 480 output channels: two 256-wide column tiles (the second one 224 wide)
   if (level == 2)
-    return run<T, TileWide, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV2>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
-  return run<T, TileWide, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV3>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
+    return run<T, TileConv, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV2>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
+  return run<T, TileConv, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV3>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
 }
 
 template hipError_t launch_linear<bf16_t>(const LinearArgs&, int, int, hipStream_t);
