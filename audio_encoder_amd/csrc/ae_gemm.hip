@@ -227,10 +227,27 @@ using TileL83 = Tile<256, 256, 2, 4, 32, 1, 2>;  // 8 waves, BK 32, 2 in flight
 
 // Workgroups are dispatched round-robin over the 8 XCDs; remap so that consecutive logical
 // tiles (same A rows, neighbouring B columns) run on the same XCD and share its L2.
-__device__ inline int64_t xcd_remap(int64_t bid, int64_t G) {
-  const int64_t per = G / 8, rem = G % 8;
-  const int64_t x = bid % 8, i = bid / 8;
+__device__ inline int xcd_remap(int bid, int G) {
+  const int per = G / 8, rem = G % 8;
+  const int x = bid % 8, i = bid / 8;
   return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+}
+
+// (m tile, n tile) of this workgroup: XCD remap, then groups of gm m-tiles walked column by
+// column so that the workgroups resident at one time share A rows and B columns in L2.  All
+// 32-bit and wave-uniform (kept in scalar registers).
+struct TileCoord { int mt, nt; };
+__device__ inline TileCoord tile_coord(int n_tiles, int gm) {
+  const int G = gridDim.x;
+  const int tile = xcd_remap(blockIdx.x, G);
+  const int m_tiles = G / n_tiles;
+  const int gsize = gm * n_tiles;
+  const int g = tile / gsize;
+  const int first_m = g * gm;
+  const int gh = m_tiles - first_m < gm ? m_tiles - first_m : gm;
+  const int in_g = tile - g * gsize;
+  return TileCoord{__builtin_amdgcn_readfirstlane(first_m + in_g % gh),
+                   __builtin_amdgcn_readfirstlane(in_g / gh)};
 }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -301,7 +318,9 @@ __device__ __host__ constexpr int swz(int r) { return BK == 64 ? (r >> 1) & 7 : 
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
   // raw buffer: stride 0, range check against `bytes`; dword3 0x00020000 (32-bit data format)
-  const int n = (int)min<int64_t>(bytes, 0x7fffffff);
+  // integer clamp (a 64-bit min lowers to a vector f64 op here, which would drag the whole
+  // descriptor into vector registers and wrap every buffer load in a waterfall loop)
+  const int n = __builtin_amdgcn_readfirstlane(bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
 }
 
@@ -339,15 +358,9 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_bf16_kernel(AS as, cons
   const int wm = wv / TL::WGN, wn = wv % TL::WGN;
   // tile order: XCD-contiguous ranges, then groups of `gm` M-tiles swept column by column so the
   // tiles an XCD runs at once share a few A row-panels and B column-panels in its L2
-  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t m_tiles = gridDim.x / n_tiles;
-  const int64_t gsize = (int64_t)gm * n_tiles;
-  const int64_t g = tile / gsize;
-  const int64_t first_m = g * gm;
-  const int64_t gh = min<int64_t>(m_tiles - first_m, gm);
-  const int64_t in_g = tile - g * gsize;
-  const int64_t mt = first_m + in_g % gh;
-  const int nt = (int)(in_g / gh);
+  const TileCoord tc = tile_coord(n_tiles, gm);
+  const int64_t mt = tc.mt;
+  const int nt = tc.nt;
   const int64_t m0 = mt * BM;
   const int n0 = nt * BN;
   if (!as.tile_live(m0, BM)) return;
@@ -599,15 +612,9 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
   const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv / TL::WGN, wn = wv % TL::WGN;
-  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t m_tiles = gridDim.x / n_tiles;
-  const int64_t gsize = (int64_t)gm * n_tiles;
-  const int64_t g = tile / gsize;
-  const int64_t first_m = g * gm;
-  const int64_t gh = min<int64_t>(m_tiles - first_m, gm);
-  const int64_t in_g = tile - g * gsize;
-  const int64_t mt = first_m + in_g % gh;
-  const int nt = (int)(in_g / gh);
+  const TileCoord tc = tile_coord(n_tiles, gm);
+  const int64_t mt = tc.mt;
+  const int nt = tc.nt;
   const int64_t m0 = mt * BM;
   const int n0 = nt * BN;
   if (!as.tile_live(m0, BM)) return;
@@ -713,6 +720,862 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
   }
 }
 
+// Compiler-only barrier: no LDS access moves across it, and unlike __syncthreads() it adds
+// no release fence (which would wait for every LDS DMA in flight, deeper stages included).
+__device__ inline void cbar() { asm volatile("" ::: "memory"); }
+
+// s_waitcnt vmcnt(VM) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
+// vmcnt[5:4] in bits 15:14)
+template <int VM>
+__device__ inline void wait_vm_lds0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+
+// Direct-to-LDS kernel with an NST-stage ring (tile kt+NST-1 is in flight while tile kt is
+// multiplied).  Each stage is its own __shared__ array: the compiler then knows which DMA a
+// fragment read can depend on, waits for that one only, and is free to interleave the reads of
+// one K step with the MFMAs of the previous one.  Per K tile:
+//   wait until this wave's DMA of tile kt has landed and its LDS reads of the stage about to
+//   be refilled are done; barrier (all waves) -> DMA of tile kt+NST-1 into the stage read at
+//   kt-1 -> fragment reads and MFMAs of tile kt.
+template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG>
+__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_pipe_kernel(AS as, const bf16_t* __restrict__ Bw,
+                                                                    int32_t N, int32_t K, OM om, EpiP ep,
+                                                                    int32_t n_tiles, int32_t pe_ld, int32_t gm) {
+  static_assert(NST >= 2 && NST <= 4, "stages");
+  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
+  constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
+  constexpr int STG = (BM + BN) * BK;  // bf16 elements per stage: A tile, then B tile
+  constexpr int SR = (NW * 32 * (WTN + 4) * 4 <= STG * 2) ? 32
+                     : (NW * 16 * (WTN + 4) * 4 <= STG * 2) ? 16 : 8;
+  static_assert(NW * SR * (WTN + 4) * 4 <= STG * 2, "epilogue staging must fit in one stage");
+  constexpr int ROWS_PER_DMA = 1024 / (BK * 2);
+  constexpr int ADMA = BM / ROWS_PER_DMA / NW;
+  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
+  constexpr int P = ADMA + BDMA;  // DMA instructions per wave per K tile
+  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
+  static_assert(P * (NST - 2) < 64, "vmcnt range");
+  constexpr int KS = BK / 16;
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[STG];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[STG];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[NST > 2 ? STG : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t st3[NST > 3 ? STG : 8];
+  auto stage = [&](auto sc) -> bf16_t* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return st0;
+    else if constexpr (s == 1) return st1;
+    else if constexpr (s == 2) return st2;
+    else return st3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
+  const TileCoord tc = tile_coord(n_tiles, gm);
+  const int64_t mt = tc.mt;
+  const int nt = tc.nt;
+  const int64_t m0 = mt * BM;
+  const int n0 = nt * BN;
+  if (!as.tile_live(m0, BM)) return;
+
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
+  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
+  constexpr int CPR = BK / 8;
+  typename AS::BRow arow[ADMA];
+  int achunk[ADMA];
+  uint32_t boffr[BDMA];
+  int bchunk[BDMA];
+#pragma unroll
+  for (int j = 0; j < ADMA; ++j) {
+    const int r = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
+    achunk[j] = (lane % CPR) ^ swz<BK>(r);
+    arow[j] = as.brow(m0 + r);
+  }
+#pragma unroll
+  for (int j = 0; j < BDMA; ++j) {
+    const int r = (wv * BDMA + j) * ROWS_PER_DMA + lane / CPR;
+    bchunk[j] = (lane % CPR) ^ swz<BK>(r);
+    const int n = n0 + r;
+    boffr[j] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
+  }
+  auto dma = [&](int kt, bf16_t* st) {
+#pragma unroll
+    for (int j = 0; j < ADMA; ++j) {
+      const int k = kt * BK + achunk[j] * 8;
+      const uint32_t off = as.boff(arow[j], as.kc(k));
+      bf16_t* dst = st + (wv * ADMA + j) * ROWS_PER_DMA * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < BDMA; ++j) {
+      const int k = kt * BK + bchunk[j] * 8;
+      const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
+      bf16_t* dst = st + BM * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int arow0 = wm * TL::WTM + l32;
+  const int brow0 = wn * TL::WTN + l32;
+  const int sw = swz<BK>(l32);
+  auto compute = [&](const bf16_t* st) {
+    const bf16_t* pa = st + arow0 * BK;
+    const bf16_t* pb = st + BM * BK + brow0 * BK;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch = ((ks * 2 + half) ^ sw) * 8;
+      bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * BK + ch);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * BK + ch);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  dma(0, st0);
+  if constexpr (NST > 2) if (1 < nk) dma(1, st1);
+  if constexpr (NST > 3) if (2 < nk) dma(2, st2);
+  auto iter = [&](int kt, auto sc) {
+    constexpr int s = decltype(sc)::value;
+    const int after = min(NST - 2, nk - 1 - kt);  // tiles issued after tile kt
+    if constexpr (NST > 3) {
+      if (after >= 2) wait_vm_lds0<2 * P>();
+      else if (after == 1) wait_vm_lds0<P>();
+      else wait_vm_lds0<0>();
+    } else if constexpr (NST > 2) {
+      if (after >= 1) wait_vm_lds0<P>();
+      else wait_vm_lds0<0>();
+    } else {
+      wait_vm_lds0<0>();
+    }
+    cbar();
+    __builtin_amdgcn_s_barrier();
+    cbar();
+    if (kt + NST - 1 < nk) dma(kt + NST - 1, stage(std::integral_constant<int, (s + NST - 1) % NST>()));
+    compute(stage(std::integral_constant<int, s>()));
+  };
+  for (int kt = 0; kt < nk; kt += NST) {
+    iter(kt, std::integral_constant<int, 0>());
+    if (kt + 1 < nk) iter(kt + 1, std::integral_constant<int, 1>());
+    if constexpr (NST > 2) if (kt + 2 < nk) iter(kt + 2, std::integral_constant<int, 2>());
+    if constexpr (NST > 3) if (kt + 3 < nk) iter(kt + 3, std::integral_constant<int, 3>());
+  }
+  wait_vm_lds0<0>();
+  __syncthreads();
+
+  constexpr int LDW = WTN + 4;
+  float* stg = reinterpret_cast<float*>(st0) + wv * SR * LDW;
+  const int wcol = n0 + wn * TL::WTN;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+  for (int hs = 0; hs < 32 / SR; ++hs) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
+        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
+      }
+    __syncthreads();
+    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
+    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
+    __syncthreads();
+  }
+  }
+}
+
+// Epilogue straight from the accumulators of a wave (no LDS staging, no barriers).  The MFMAs
+// compute the transposed product (B fragment as the first operand), so lane l of a 32x32 block
+// holds output row l % 32 and, for register group g = v / 4, the four consecutive columns
+// 8 g + 4 (l / 32) .. +3: every lane stores 4-wide runs of its own row.
+template <int EPI, typename OT, int TM, int TN, class OM>
+__device__ __attribute__((always_inline)) inline void epilogue_direct(const f32x16_t (&acc)[TM][TN], int64_t mrow0, int ncol0,
+                                       int N, const OM& om, const EpiP& ep, int pe_ld, int lane) {
+  const int l32 = lane & 31, half = lane >> 5;
+  const bool vec = (N & 3) == 0;  // 4-wide runs are aligned and never straddle the end
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t row = mrow0 + i * 32 + l32;
+    const int64_t off = om.off(row);
+    if (off < 0) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      // gate and up columns alternate in blocks of 32 (N % 64 == 0): block pairs (j, j+1)
+#pragma unroll
+      for (int j = 0; j + 1 < TN; j += 2) {
+        if (ncol0 + j * 32 >= N) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = (ncol0 + j * 32) / 2 + 8 * g + 4 * half;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = silu(acc[i][j][4 * g + e]) * acc[i][j + 1][4 * g + e];
+          Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off + col, o[0], o[1], o[2], o[3]);
+        }
+      }
+    } else {
+      const float* perow = nullptr;
+      if constexpr (EPI == EPI_PE) perow = ep.pe + (int64_t)ep.tok_pos[row] * pe_ld;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = ncol0 + j * 32 + 8 * g + 4 * half;
+          if (col >= N) continue;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e];
+          if (vec) {
+            if constexpr (EPI == EPI_PE) {
+              const float4 pe = *reinterpret_cast<const float4*>(perow + col);
+              o[0] += pe.x; o[1] += pe.y; o[2] += pe.z; o[3] += pe.w;
+            } else if (ep.bias) {
+              const float4 b = *reinterpret_cast<const float4*>(ep.bias + col);
+              o[0] += b.x; o[1] += b.y; o[2] += b.z; o[3] += b.w;
+            }
+            if constexpr (EPI == EPI_RESADD) {
+              float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col);
+              const float4 c = *p;
+              *p = make_float4(c.x + o[0], c.y + o[1], c.z + o[2], c.w + o[3]);
+            } else if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_PE) {
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col) =
+                  make_float4(o[0], o[1], o[2], o[3]);
+            } else {
+              if constexpr (EPI == EPI_BIAS_GELU) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = gelu_erf(o[e]);
+              }
+              Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off + col, o[0], o[1], o[2], o[3]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (col + e >= N) break;
+              if constexpr (EPI == EPI_PE) {
+                reinterpret_cast<float*>(ep.C)[off + col + e] = o[e] + perow[col + e];
+              } else {
+                epi_store<EPI, OT>(ep, off, row, col + e, o[e]);
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int P, int NMAX>
+__device__ inline void wait_tiles(int n) {  // vmcnt(P * n) lgkmcnt(0), n in [0, NMAX]
+  if constexpr (NMAX >= 3) if (n >= 3) { wait_vm_lds0<3 * P>(); return; }
+  if constexpr (NMAX >= 2) if (n >= 2) { wait_vm_lds0<2 * P>(); return; }
+  if constexpr (NMAX >= 1) if (n >= 1) { wait_vm_lds0<P>(); return; }
+  wait_vm_lds0<0>();
+}
+
+// As gemm_pipe_kernel, with the MFMA fragments double-buffered in registers: the fragment
+// reads of K step ks+1 are issued before the MFMAs of step ks, and the barrier that publishes
+// tile kt+1 sits before the MFMAs of the last step of tile kt, so the matrix pipe is fed across
+// tile boundaries even with one wave per SIMD.
+//   prologue: DMA tiles 0..NST-1, wait for tile 0, barrier, read step 0.
+//   tile kt, step ks < KS-1: read step ks+1; MFMAs of step ks.
+//   tile kt, last step: wait for tile kt+1 (and for this wave's reads), barrier, DMA of tile
+//   kt+NST into the stage just drained, read step 0 of tile kt+1; MFMAs of the last step.
+template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG, bool DIRECT = true>
+__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_pipe2_kernel(AS as, const bf16_t* __restrict__ Bw,
+                                                                     int32_t N, int32_t K, OM om, EpiP ep,
+                                                                     int32_t n_tiles, int32_t pe_ld, int32_t gm) {
+  static_assert(NST >= 2 && NST <= 4, "stages");
+  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
+  constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
+  constexpr int STG = (BM + BN) * BK;
+  constexpr int SR = (NW * 32 * (WTN + 4) * 4 <= STG * 2) ? 32
+                     : (NW * 16 * (WTN + 4) * 4 <= STG * 2) ? 16 : 8;
+  static_assert(NW * SR * (WTN + 4) * 4 <= STG * 2, "epilogue staging must fit in one stage");
+  constexpr int ROWS_PER_DMA = 1024 / (BK * 2);
+  constexpr int ADMA = BM / ROWS_PER_DMA / NW;
+  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
+  constexpr int P = ADMA + BDMA;
+  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
+  static_assert(P * (NST - 1) < 64, "vmcnt range");
+  constexpr int KS = BK / 16;
+  static_assert(KS % 2 == 0, "fragment buffers alternate by step parity");
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[STG];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[STG];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[NST > 2 ? STG : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t st3[NST > 3 ? STG : 8];
+  auto stage = [&](auto sc) -> bf16_t* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return st0;
+    else if constexpr (s == 1) return st1;
+    else if constexpr (s == 2) return st2;
+    else return st3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
+  const TileCoord tc = tile_coord(n_tiles, gm);
+  const int64_t m0 = (int64_t)tc.mt * BM;
+  const int n0 = tc.nt * BN;
+  if (!as.tile_live(m0, BM)) return;
+
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
+  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
+  constexpr int CPR = BK / 8;
+  typename AS::BRow arow[ADMA];
+  int achunk[ADMA];
+  uint32_t boffr[BDMA];
+  int bchunk[BDMA];
+#pragma unroll
+  for (int j = 0; j < ADMA; ++j) {
+    const int r = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
+    achunk[j] = (lane % CPR) ^ swz<BK>(r);
+    arow[j] = as.brow(m0 + r);
+  }
+#pragma unroll
+  for (int j = 0; j < BDMA; ++j) {
+    const int r = (wv * BDMA + j) * ROWS_PER_DMA + lane / CPR;
+    bchunk[j] = (lane % CPR) ^ swz<BK>(r);
+    const int n = n0 + r;
+    boffr[j] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
+  }
+  auto dma = [&](int kt, bf16_t* st) {
+#pragma unroll
+    for (int j = 0; j < ADMA; ++j) {
+      const int k = kt * BK + achunk[j] * 8;
+      const uint32_t off = as.boff(arow[j], as.kc(k));
+      bf16_t* dst = st + (wv * ADMA + j) * ROWS_PER_DMA * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < BDMA; ++j) {
+      const int k = kt * BK + bchunk[j] * 8;
+      const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
+      bf16_t* dst = st + BM * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int aoff = (wm * TL::WTM + l32) * BK;
+  const int boff = BM * BK + (wn * TL::WTN + l32) * BK;
+  const int sw = swz<BK>(l32);
+  bf16x8_t fa[2][TM], fb[2][TN];
+  auto rd = [&](const bf16_t* st, int ks, int buf) {
+    const int ch = ((ks * 2 + half) ^ sw) * 8;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoff + i * 32 * BK + ch);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boff + j * 32 * BK + ch);
+  };
+  auto mm = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        if constexpr (DIRECT)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  };
+  auto barrier = [&]() {
+    cbar();
+    __builtin_amdgcn_s_barrier();
+    cbar();
+  };
+
+  // The K loop runs over a multiple of NST tiles, and tiles past the end of K are issued like
+  // any other: every offset is out of range, so they only write zeros into stages whose
+  // products add nothing.  The loop body is then free of branches and each wave always has the
+  // same number of DMAs in flight, so every wait below is a constant (the compiler's wait-count
+  // tracking merges the states of branches conservatively and would otherwise stall MFMAs on
+  // fragment reads they do not use).
+  const int nk = (K + BK * NST - 1) / (BK * NST) * NST;
+  dma(0, st0);
+  dma(1, st1);
+  if constexpr (NST > 2) dma(2, st2);
+  if constexpr (NST > 3) dma(3, st3);
+  wait_vm_lds0<P * (NST - 1)>();
+  barrier();
+  rd(st0, 0, 0);
+
+  auto tile_step = [&](int kt, auto sc) {
+    constexpr int s = decltype(sc)::value;
+    const bf16_t* cur = stage(sc);
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      rd(cur, ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs they overlap
+      mm(ks & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm_lds0<P * (NST - 2)>();
+    barrier();
+    dma(kt + NST, stage(sc));
+    rd(stage(std::integral_constant<int, (s + 1) % NST>()), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mm((KS - 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int kt = 0; kt < nk; kt += NST) {
+    tile_step(kt, std::integral_constant<int, 0>());
+    tile_step(kt + 1, std::integral_constant<int, 1>());
+    if constexpr (NST > 2) tile_step(kt + 2, std::integral_constant<int, 2>());
+    if constexpr (NST > 3) tile_step(kt + 3, std::integral_constant<int, 3>());
+  }
+  if constexpr (DIRECT) {
+    epilogue_direct<EPI, OT, TM, TN>(acc, m0 + wm * TL::WTM, n0 + wn * TL::WTN, N, om, ep, pe_ld, lane);
+    wait_vm_lds0<0>();  // the trailing out-of-range DMAs land before the LDS is released
+    return;
+  }
+  wait_vm_lds0<0>();
+  __syncthreads();
+
+  constexpr int LDW = WTN + 4;
+  float* stg = reinterpret_cast<float*>(st0) + wv * SR * LDW;
+  const int wcol = n0 + wn * TL::WTN;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+  for (int hs = 0; hs < 32 / SR; ++hs) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
+        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
+      }
+    __syncthreads();
+    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
+    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
+    __syncthreads();
+  }
+  }
+}
+
+// NST-stage direct-to-LDS kernel with the refill DMAs spread over the MFMAs.  One barrier per K
+// step, at its start: it publishes tile kt and frees the stage read in step kt-1, which is then
+// refilled with tile kt+NST-1 in KS slices, one slice issued between the MFMAs of each K
+// sub-step (issuing a whole tile's DMAs at once backs up the load queue and stalls the issuing
+// waves, MFMAs included).  Fragment reads of sub-step ks+1 are issued before the MFMAs of ks.
+template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG, bool DIRECT = false>
+__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const bf16_t* __restrict__ Bw,
+                                                                   int32_t N, int32_t K, OM om, EpiP ep,
+                                                                   int32_t n_tiles, int32_t pe_ld, int32_t gm) {
+  static_assert(NST >= 3 && NST <= 4, "stages: the last refill slice needs a step of slack");
+  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
+  constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
+  constexpr int STG = (BM + BN) * BK;
+  constexpr int SR = (NW * 32 * (WTN + 4) * 4 <= STG * 2) ? 32
+                     : (NW * 16 * (WTN + 4) * 4 <= STG * 2) ? 16 : 8;
+  static_assert(NW * SR * (WTN + 4) * 4 <= STG * 2, "epilogue staging must fit in one stage");
+  constexpr int ROWS_PER_DMA = 1024 / (BK * 2);
+  constexpr int ADMA = BM / ROWS_PER_DMA / NW;
+  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
+  constexpr int P = ADMA + BDMA;
+  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
+  static_assert(P * (NST - 1) < 64, "vmcnt range");
+  constexpr int KS = BK / 16;
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[STG];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[STG];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[STG];
+  __shared__ __attribute__((aligned(1024))) bf16_t st3[NST > 3 ? STG : 8];
+  auto stage = [&](auto sc) -> bf16_t* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return st0;
+    else if constexpr (s == 1) return st1;
+    else if constexpr (s == 2) return st2;
+    else return st3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
+  const TileCoord tc = tile_coord(n_tiles, gm);
+  const int64_t m0 = (int64_t)tc.mt * BM;
+  const int n0 = tc.nt * BN;
+  if (!as.tile_live(m0, BM)) return;
+
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
+  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
+  constexpr int CPR = BK / 8;
+  typename AS::BRow arow[ADMA];
+  int achunk[ADMA];
+  uint32_t boffr[BDMA];
+  int bchunk[BDMA];
+#pragma unroll
+  for (int j = 0; j < ADMA; ++j) {
+    const int r = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
+    achunk[j] = (lane % CPR) ^ swz<BK>(r);
+    arow[j] = as.brow(m0 + r);
+  }
+#pragma unroll
+  for (int j = 0; j < BDMA; ++j) {
+    const int r = (wv * BDMA + j) * ROWS_PER_DMA + lane / CPR;
+    bchunk[j] = (lane % CPR) ^ swz<BK>(r);
+    const int n = n0 + r;
+    boffr[j] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
+  }
+  // DMA instructions [lo, hi) of tile kt (A rows first, then B rows)
+  auto dma_part = [&](int kt, bf16_t* st, int lo, int hi) {
+#pragma unroll
+    for (int j = 0; j < ADMA; ++j) {
+      if (j < lo || j >= hi) continue;
+      const int k = kt * BK + achunk[j] * 8;
+      const uint32_t off = as.boff(arow[j], as.kc(k));
+      bf16_t* dst = st + (wv * ADMA + j) * ROWS_PER_DMA * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < BDMA; ++j) {
+      if (ADMA + j < lo || ADMA + j >= hi) continue;
+      const int k = kt * BK + bchunk[j] * 8;
+      const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
+      bf16_t* dst = st + BM * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int aoff = (wm * TL::WTM + l32) * BK;
+  const int boff = BM * BK + (wn * TL::WTN + l32) * BK;
+  const int sw = swz<BK>(l32);
+  bf16x8_t fa[2][TM], fb[2][TN];
+  auto rd = [&](const bf16_t* st, int ks, int buf) {
+    const int ch = ((ks * 2 + half) ^ sw) * 8;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoff + i * 32 * BK + ch);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boff + j * 32 * BK + ch);
+  };
+  auto mm = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (DIRECT)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+      }
+  };
+  auto barrier = [&]() {
+    cbar();
+    __builtin_amdgcn_s_barrier();
+    cbar();
+  };
+
+  // As in gemm_pipe2_kernel: a multiple of NST steps, with out-of-range tiles past the end of K
+  // (zero fill), so every wait is a constant.
+  const int nk = (K + BK * NST - 1) / (BK * NST) * NST;
+  dma_part(0, st0, 0, P);
+  dma_part(1, st1, 0, P);
+  if constexpr (NST > 3) dma_part(2, st2, 0, P);
+
+  auto step = [&](int kt, auto sc) {
+    constexpr int s = decltype(sc)::value;
+    constexpr int sf = (s + NST - 1) % NST;  // stage freed by this step's barrier
+    wait_vm_lds0<P * (NST - 2)>();           // tile kt landed; tiles kt+1 .. kt+NST-2 in flight
+    barrier();
+    const bf16_t* cur = stage(sc);
+    bf16_t* nxt = stage(std::integral_constant<int, sf>());
+    rd(cur, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) rd(cur, ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      dma_part(kt + NST - 1, nxt, ks * P / KS, (ks + 1) * P / KS);
+      mm(ks & 1);
+      // alternate refill DMAs and MFMAs
+#pragma unroll
+      for (int d = ks * P / KS; d < (ks + 1) * P / KS; ++d) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int kt = 0; kt < nk; kt += NST) {
+    step(kt, std::integral_constant<int, 0>());
+    step(kt + 1, std::integral_constant<int, 1>());
+    step(kt + 2, std::integral_constant<int, 2>());
+    if constexpr (NST > 3) step(kt + 3, std::integral_constant<int, 3>());
+  }
+  if constexpr (DIRECT) {
+    epilogue_direct<EPI, OT, TM, TN>(acc, m0 + wm * TL::WTM, n0 + wn * TL::WTN, N, om, ep, pe_ld, lane);
+    wait_vm_lds0<0>();  // the trailing out-of-range DMAs land before the LDS is released
+    return;
+  }
+  wait_vm_lds0<0>();
+  __syncthreads();
+
+  constexpr int LDW = WTN + 4;
+  float* stg = reinterpret_cast<float*>(st0) + wv * SR * LDW;
+  const int wcol = n0 + wn * TL::WTN;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+  for (int hs = 0; hs < 32 / SR; ++hs) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
+        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
+      }
+    __syncthreads();
+    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
+    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
+    __syncthreads();
+  }
+  }
+}
+
+// Persistent form of gemm_pipe2_kernel: a grid of at most one wave of resident workgroups, each
+// walking a sequence of output tiles.  The DMA stream runs NST-1 K steps ahead across tile
+// boundaries, so the next tile's first stages load while the current one finishes, and the
+// epilogue (straight from registers, no barrier) drains while the next tile's MFMAs run.
+//   Tile order: the logical tiles (groups of gm m-tiles walked column by column) are split into
+//   8 contiguous chunks, one per XCD (workgroup b runs on XCD b % 8); the workgroups of an XCD
+//   take the tiles of its chunk round-robin, so the tiles in flight on one XCD are neighbours
+//   and share A rows and B columns in its L2.  Tiles whose rows are all padding are skipped.
+template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG>
+__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_persist_kernel(AS as, const bf16_t* __restrict__ Bw,
+                                                                       int32_t N, int32_t K, OM om, EpiP ep,
+                                                                       int32_t m_tiles, int32_t n_tiles,
+                                                                       int32_t pe_ld, int32_t gm) {
+  static_assert(NST >= 2 && NST <= 4, "stages");
+  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
+  constexpr int BK = TL::BK, NW = TL::NW;
+  constexpr int STG = (BM + BN) * BK;
+  constexpr int ROWS_PER_DMA = 1024 / (BK * 2);
+  constexpr int ADMA = BM / ROWS_PER_DMA / NW;
+  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
+  constexpr int P = ADMA + BDMA;
+  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
+  static_assert(P * (NST - 1) < 64, "vmcnt range");
+  constexpr int KS = BK / 16;
+  static_assert(KS % 2 == 0, "fragment buffers alternate by step parity");
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[STG];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[STG];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[NST > 2 ? STG : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t st3[NST > 3 ? STG : 8];
+  auto stage = [&](auto sc) -> bf16_t* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return st0;
+    else if constexpr (s == 1) return st1;
+    else if constexpr (s == 2) return st2;
+    else return st3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
+
+  // this workgroup's tiles: c0 + q + j * Gx for j = 0, 1, ... below c1
+  const int T = m_tiles * n_tiles;
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % 8, q = blockIdx.x / 8;
+  const int Gx = G / 8 + (xcd < G % 8 ? 1 : 0);
+  const int before = xcd * (G / 8) + min(xcd, G % 8);
+  const int c0 = (int)((int64_t)T * before / G);
+  const int c1 = (int)((int64_t)T * (before + Gx) / G);
+  const int n_my = c1 - c0 > q ? (c1 - c0 - q + Gx - 1) / Gx : 0;
+  const int gsize = gm * n_tiles;
+  auto coord = [&](int j) -> TileCoord {
+    const int t = c0 + q + j * Gx;
+    const int g = t / gsize;
+    const int first_m = g * gm;
+    const int gh = m_tiles - first_m < gm ? m_tiles - first_m : gm;
+    const int in_g = t - g * gsize;
+    return TileCoord{__builtin_amdgcn_readfirstlane(first_m + in_g % gh),
+                     __builtin_amdgcn_readfirstlane(in_g / gh)};
+  };
+  auto live = [&](int j) { return as.tile_live((int64_t)coord(j).mt * BM, BM); };
+  auto next_live = [&](int j) {
+    while (j < n_my && !live(j)) ++j;
+    return j;
+  };
+  int cj = next_live(0);  // tile being multiplied
+  if (cj >= n_my) return;
+
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
+  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
+  constexpr int CPR = BK / 8;
+  int achunk[ADMA], bchunk[BDMA], arl[ADMA], brl[BDMA];
+#pragma unroll
+  for (int j = 0; j < ADMA; ++j) {
+    arl[j] = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
+    achunk[j] = (lane % CPR) ^ swz<BK>(arl[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < BDMA; ++j) {
+    brl[j] = (wv * BDMA + j) * ROWS_PER_DMA + lane / CPR;
+    bchunk[j] = (lane % CPR) ^ swz<BK>(brl[j]);
+  }
+  // DMA side: tile dj, K step dk, and the per-lane row offsets of tile dj (all out of range once
+  // the sequence is exhausted, so the stream keeps its shape with zero-filling loads)
+  typename AS::BRow arow[ADMA];
+  uint32_t boffr[BDMA];
+  int dj = cj, dk = 0;
+  auto setup = [&](int j) {
+    const bool ok = j < n_my;
+    const TileCoord tc = ok ? coord(j) : TileCoord{m_tiles, 0};
+    const int64_t m0 = (int64_t)tc.mt * BM;
+    const int n0 = tc.nt * BN;
+#pragma unroll
+    for (int i = 0; i < ADMA; ++i) arow[i] = as.brow(m0 + arl[i]);
+#pragma unroll
+    for (int i = 0; i < BDMA; ++i) {
+      const int n = n0 + brl[i];
+      boffr[i] = (ok && n < N) ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
+    }
+  };
+  const int nk = (K + BK * NST - 1) / (BK * NST) * NST;
+  auto dma = [&](bf16_t* st) {
+#pragma unroll
+    for (int j = 0; j < ADMA; ++j) {
+      const int k = dk * BK + achunk[j] * 8;
+      const uint32_t off = as.boff(arow[j], as.kc(k));
+      bf16_t* dst = st + (wv * ADMA + j) * ROWS_PER_DMA * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < BDMA; ++j) {
+      const int k = dk * BK + bchunk[j] * 8;
+      const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
+      bf16_t* dst = st + BM * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+    if (++dk == nk) {
+      dk = 0;
+      dj = next_live(dj + 1);
+      setup(dj);
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+  auto zero = [&]() {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  };
+  zero();
+
+  const int aoff = (wm * TL::WTM + l32) * BK;
+  const int boff = BM * BK + (wn * TL::WTN + l32) * BK;
+  const int sw = swz<BK>(l32);
+  bf16x8_t fa[2][TM], fb[2][TN];
+  auto rd = [&](const bf16_t* st, int ks, int buf) {
+    const int ch = ((ks * 2 + half) ^ sw) * 8;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoff + i * 32 * BK + ch);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boff + j * 32 * BK + ch);
+  };
+  auto mm = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+  };
+  auto barrier = [&]() {
+    cbar();
+    __builtin_amdgcn_s_barrier();
+    cbar();
+  };
+
+  setup(dj);
+  dma(st0);
+  dma(st1);
+  if constexpr (NST > 2) dma(st2);
+  if constexpr (NST > 3) dma(st3);
+  wait_vm_lds0<P * (NST - 1)>();
+  barrier();
+  rd(st0, 0, 0);
+
+  int ck = 0;
+  auto step = [&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    const bf16_t* cur = stage(sc);
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      rd(cur, ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mm(ks & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm_lds0<P * (NST - 2)>();
+    barrier();
+    dma(stage(sc));
+    rd(stage(std::integral_constant<int, (s + 1) % NST>()), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mm((KS - 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  while (cj < n_my) {
+    step(std::integral_constant<int, 0>());
+    step(std::integral_constant<int, 1>());
+    if constexpr (NST > 2) step(std::integral_constant<int, 2>());
+    if constexpr (NST > 3) step(std::integral_constant<int, 3>());
+    ck += NST;  // nk is a multiple of NST: a tile ends on the last step of a group
+    if (ck == nk) {
+      const TileCoord tc = coord(cj);
+      epilogue_direct<EPI, OT, TM, TN>(acc, (int64_t)tc.mt * BM + wm * TL::WTM, tc.nt * BN + wn * TL::WTN,
+                                       N, om, ep, pe_ld, lane);
+      zero();
+      ck = 0;
+      cj = next_live(cj + 1);
+    }
+  }
+  wait_vm_lds0<0>();  // the trailing zero-filling DMAs land before the LDS is released
+}
+
 // MFMA fragments of one K-step (BK = 32: 32-row blocks 2048 bytes apart) read from LDS by one
 // (outputs are early-clobber: no output may share a register with the address inputs)
 // inline-asm block that waits for its own reads before it ends, so the compiler never sees an
@@ -795,15 +1658,9 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ring_kernel(AS as, cons
   const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv / TL::WGN, wn = wv % TL::WGN;
-  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t m_tiles = gridDim.x / n_tiles;
-  const int64_t gsize = (int64_t)gm * n_tiles;
-  const int64_t g = tile / gsize;
-  const int64_t first_m = g * gm;
-  const int64_t gh = min<int64_t>(m_tiles - first_m, gm);
-  const int64_t in_g = tile - g * gsize;
-  const int64_t mt = first_m + in_g % gh;
-  const int nt = (int)(in_g / gh);
+  const TileCoord tc = tile_coord(n_tiles, gm);
+  const int64_t mt = tc.mt;
+  const int nt = tc.nt;
   const int64_t m0 = mt * BM;
   const int n0 = nt * BN;
   if (!as.tile_live(m0, BM)) return;
@@ -985,16 +1842,23 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(AS as, const float* __res
 // ============================================================================================
 // dispatch
 // ============================================================================================
-template <typename T, class TL, class AS, class OM, int EPI, int TAG>
+// NST = 0: gemm_dtl_kernel (one tile in flight); NST >= 3: gemm_ilv_kernel with NST stages.
+template <typename T, class TL, class AS, class OM, int EPI, int TAG, int NST = 0>
 hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, const EpiP& ep,
                int64_t m_rows, int32_t pe_ld, hipStream_t s) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     const int n_tiles = (N + TL::BN - 1) / TL::BN;
     const int64_t m_tiles = (m_rows + TL::BM - 1) / TL::BM;
     if (m_tiles * n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_dtl_kernel<TL, AS, OM, EPI, bf16_t, TAG>),
-                       dim3((unsigned)(m_tiles * n_tiles)), dim3(TL::NT), 0, s, as, Bw, N, K, om, ep,
-                       n_tiles, pe_ld, AE_GEMM_GROUP_M);
+    if (m_tiles * n_tiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    if constexpr (NST == 0)
+      hipLaunchKernelGGL((gemm_dtl_kernel<TL, AS, OM, EPI, bf16_t, TAG>),
+                         dim3((unsigned)(m_tiles * n_tiles)), dim3(TL::NT), 0, s, as, Bw, N, K, om, ep,
+                         n_tiles, pe_ld, AE_GEMM_GROUP_M);
+    else
+      hipLaunchKernelGGL((gemm_ilv_kernel<TL, NST, AS, OM, EPI, bf16_t, TAG>),
+                         dim3((unsigned)(m_tiles * n_tiles)), dim3(TL::NT), 0, s, as, Bw, N, K, om, ep,
+                         n_tiles, pe_ld, AE_GEMM_GROUP_M);
   } else {
     if constexpr (EPI == EPI_SWIGLU) {
       return hipErrorInvalidValue;  // the fp32 path applies SwiGLU in a separate kernel
@@ -1009,26 +1873,39 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
   return hipGetLastError();
 }
 
-// Tile choice (measured on MI355X with the shapes of the tower, M = 6000): 256x128 tiles with
-// 8 waves (two per SIMD, BK 32) for the wide outputs (N >= 2048: FFN1, head proj2, adapter);
-// 128x128 tiles with BK 64 and two workgroups per CU for N = 1280 and N = 3840 (o-proj, FFN2,
-// conv_out, proj1, QKV), where the wider tile leaves CUs idle in the last round.
+// Tile choice (measured on MI355X with the shapes of the tower, M = 6000):
+//  - N = 1280 or 3840 (o-proj, FFN2, conv_out, proj1, QKV): 128x128 tiles, BK 64, two workgroups
+//    per CU; a wider tile leaves CUs idle in the last round.
+//  - N = 5120 (FFN1): 256x128 tiles, 8 waves (two per SIMD), BK 32.
+//  - K >= 2048 (adapter gate/up and down, head proj2): 256x256 tiles, 8 waves, BK 32, four
+//    stages with the refill DMAs spread over the MFMAs.
 using TileWide = Tile<256, 128, 4, 2, 32, 1>;
 using TileNarrow = Tile<128, 128, 2, 2, 64, 2>;
-inline bool use_wide_tile(int64_t /*M*/, int64_t N) { return N >= 2048 && N != 3840; }
+using TileLarge = Tile<256, 256, 2, 4, 32, 1>;
+enum class LinKind { Narrow, Wide, Large };
+inline LinKind lin_kind(int64_t /*M*/, int64_t N, int64_t K) {
+  if (N == 1280 || N == 3840 || N < 2048) return LinKind::Narrow;
+  if (K >= 2048) return LinKind::Large;
+  return LinKind::Wide;
+}
 
-// conv2/conv3 (N = 480 output channels)
+// conv2/conv3 (N = 480 output channels, K = 9 * 480): 256x256 tiles with four stages measured
+// fastest (the 480 channels fill two 256-wide column tiles at 94%)
 #ifndef AE_CONV_TILE
-#define AE_CONV_TILE 0
+#define AE_CONV_TILE 1
 #endif
 #if AE_CONV_TILE == 0
 using TileConv = Tile<256, 128, 4, 2, 32, 1>;
+constexpr int kConvStages = 0;
 #elif AE_CONV_TILE == 1
-using TileConv = Tile<256, 256, 2, 4, 64, 1>;
+using TileConv = Tile<256, 256, 2, 4, 32, 1>;
+constexpr int kConvStages = 4;
 #elif AE_CONV_TILE == 2
-using TileConv = Tile<128, 128, 2, 2, 64, 2>;
+using TileConv = Tile<256, 128, 4, 2, 32, 1>;
+constexpr int kConvStages = 4;
 #else
-using TileConv = Tile<256, 160, 4, 1, 64, 1>;
+using TileConv = Tile<128, 128, 2, 2, 64, 2>;
+constexpr int kConvStages = 0;
 #endif
 
 template <typename T, int TAG, int EPI>
@@ -1038,9 +1915,14 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
   EpiP ep{a.bias, a.C, a.pe, a.tok_pos};
   const T* Bw = reinterpret_cast<const T*>(a.W);
   const int pe_ld = EPI == EPI_PE ? a.N : 0;
-  if (use_wide_tile(a.M, a.N))
-    return run<T, TileWide, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
-  return run<T, TileNarrow, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+  switch (lin_kind(a.M, a.N, a.K)) {
+    case LinKind::Large:
+      return run<T, TileLarge, ALinear<T>, OLinear, EPI, TAG, 4>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+    case LinKind::Wide:
+      return run<T, TileWide, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+    default:
+      return run<T, TileNarrow, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+  }
 }
 
 }  // namespace
@@ -1089,8 +1971,10 @@ hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T*
   OConv om{g.wins, rows_per_win, Fout, C, level, Lout_max, m_rows};
   EpiP ep{bias, out, nullptr, nullptr};
   if (level == 2)
-    return run<T, TileConv, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV2>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
-  return run<T, TileConv, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV3>(as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
+    return run<T, TileConv, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV2, kConvStages>(as, wpk, C, 9 * C, om, ep,
+                                                                                     m_rows, 0, s);
+  return run<T, TileConv, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV3, kConvStages>(as, wpk, C, 9 * C, om, ep,
+                                                                                   m_rows, 0, s);
 }
 
 template hipError_t launch_linear<bf16_t>(const LinearArgs&, int, int, hipStream_t);

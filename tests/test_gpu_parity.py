@@ -65,8 +65,12 @@ def test_op_layernorm(D, dtype):
     assert np.abs(got - ref).max() <= tol * np.abs(ref).max()
 
 
+# (M, N, K): small and ragged shapes, and one of each tile path (128x128: N = 1280 / 3840 /
+# N < 2048; 256x128: N >= 2048 with K < 2048; 256x256 four-stage: N >= 2048 with K >= 2048, here
+# with K not a multiple of the 128-deep stage group and M, N not multiples of the tile)
 LINEAR_SHAPES = [(1, 64, 64), (130, 200, 72), (300, 3840, 1280), (257, 1280, 5120),
-                 (129, 1024, 4320), (64, 128, 8)]
+                 (129, 1024, 4320), (64, 128, 8), (333, 2560, 1032), (301, 2112, 2216),
+                 (77, 4096, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", LINEAR_SHAPES)
