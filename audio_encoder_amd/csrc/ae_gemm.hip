@@ -10,12 +10,13 @@
 // time).  Epilogues fuse the bias, exact GELU, the fp32 residual update, the sinusoidal
 // positions and the SwiGLU gate into the store.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950.  Workgroup tile 128x128, K step 64, four
-// waves each owning a 64x64 sub-tile (2x2 MFMA blocks, fp32 accumulators).  Global loads of
-// the next K step are issued into registers before the MFMAs of the current one and written
-// to the second LDS buffer afterwards (LDS double buffering, one barrier per K step).  LDS
-// rows are 128 bytes with the 16-byte chunk index XOR-swizzled by (row & 7), so the 32 rows a
-// wave reads for one MFMA operand hit distinct banks.
+// bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950 with fp32 accumulators.  Tiles move from global
+// memory straight into LDS with buffer_load_dwordx4 ... lds (16 bytes per lane, no VGPR
+// staging); LDS rows are XOR-swizzled so the fragment reads are free of bank conflicts; the
+// epilogue stages accumulator rows through LDS for coalesced stores.  Two kernels:
+//   gemm_dtl_kernel  one K tile in flight, all fragments of a tile read before the next DMA;
+//   gemm_ilv_kernel  NST stages in separate LDS arrays, refill DMAs spread over the MFMAs.
+// The tile shape and kernel per call are chosen in the dispatch section at the end.
 //
 // fp32 path (the fp32 tiny configuration): a 64x64 VALU tile with the same loaders and
 // epilogues.
@@ -188,42 +189,17 @@ __device__ inline void epi_store(const EpiP& ep, int64_t off, int64_t row, int c
 // ============================================================================================
 // bf16 MFMA kernel
 // ============================================================================================
-constexpr int NTHR = 256;
-
-__device__ inline uint4 ld16(const bf16_t* p) {
-  return p ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
-}
-
 // Block tile BM x BN x BK, WGM x WGN waves, each owning (BM/WGM) x (BN/WGN) as TM x TN blocks
-// of 32x32 MFMA output.  MINB workgroups are meant to share a CU (occupancy hint).  NPF register
-// sets form a ring of K tiles in flight from HBM/L2, so a tile's loads are issued NPF tiles
-// before it is written to LDS (the global load latency exceeds one tile of MFMA work).
-template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int MINB_ = 1, int NPF_ = 1>
+// of 32x32 MFMA output.  MINB workgroups are meant to share a CU (occupancy hint).
+template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int MINB_ = 1>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_, MINB = MINB_;
-  static constexpr int NPF = NPF_;  // K tiles in flight between global load and LDS store
   static constexpr int NW = WGM * WGN, NT = 64 * NW;  // waves, threads
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  static constexpr int CPR = BK / 8;                   // 16-byte chunks per tile row
-  static constexpr int RS = NT / CPR;                  // rows covered by one loader pass
-  static constexpr int AR = BM / RS, BR = BN / RS;     // chunks per thread per K step
-  static_assert(TM * 32 == WTM && TN * 32 == WTN && AR * RS == BM && BR * RS == BN, "tile");
+  static_assert(TM * 32 == WTM && TN * 32 == WTN, "tile");
   static_assert(BK == 32 || BK == 64, "BK");
 };
-using TileL = Tile<256, 256, 2, 2>;   // 4 waves, wave tile 128 x 128
-using TileL8 = Tile<256, 256, 2, 4>;  // 8 waves, wave tile 128 x 64 (two waves per SIMD)
-using TileL8b = Tile<256, 256, 4, 2>; // 8 waves, wave tile 64 x 128
-using TileM = Tile<256, 128, 2, 2>;   // 4 waves, wave tile 128 x 64
-using TileM8 = Tile<256, 128, 4, 2>;  // 8 waves, wave tile 64 x 64
-using TileMk = Tile<256, 128, 2, 2, 32, 2>;  // 4 waves, BK 32, two workgroups per CU
-using TileSk = Tile<128, 128, 2, 2, 32, 3>;  // 4 waves, BK 32, three workgroups per CU
-using TileS = Tile<128, 128, 2, 2, 64, 2>;   // 4 waves, BK 64, two workgroups per CU
-using TileSk3 = Tile<128, 128, 2, 2, 32, 3, 3>;  // + 3 tiles in flight
-using TileSk2 = Tile<128, 128, 2, 2, 32, 3, 2>;
-using TileMk3 = Tile<256, 128, 2, 2, 32, 2, 3>;
-using TileM83 = Tile<256, 128, 4, 2, 32, 1, 3>;  // 8 waves, BK 32
-using TileL83 = Tile<256, 256, 2, 4, 32, 1, 2>;  // 8 waves, BK 32, 2 in flight
 
 // Workgroups are dispatched round-robin over the 8 XCDs; remap so that consecutive logical
 // tiles (same A rows, neighbouring B columns) run on the same XCD and share its L2.
@@ -325,262 +301,9 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes)
 }
 
 // TAG only names the call site (one kernel symbol per role, so profiles separate them)
-#ifndef AE_GEMM_CPOL
-#define AE_GEMM_CPOL 0  // cache policy bits of the tile loads
-#endif
 #ifndef AE_GEMM_GROUP_M
 #define AE_GEMM_GROUP_M 8
 #endif
-#ifndef AE_GEMM_SCHED
-#define AE_GEMM_SCHED 3
-#endif
-
-// SCHED bit 0: software-pipeline the K loop across the barrier (the last K-step's MFMAs run
-// after the barrier, covering the LDS reads of the next tile's first K-step).  SCHED bit 1:
-// order each K-step as [LDS reads of the next K-step][MFMAs of this one] for the scheduler.
-template <class TL, class AS, class OM, int EPI, typename OT, int TAG, int SCHED = AE_GEMM_SCHED>
-__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_bf16_kernel(AS as, const bf16_t* __restrict__ Bw,
-                                                         int32_t N, int32_t K, OM om, EpiP ep,
-                                                         int32_t n_tiles, int32_t pe_ld, int32_t gm) {
-  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN, AR = TL::AR, BR = TL::BR;
-  constexpr int WTN = TL::WTN, BK = TL::BK, CPR = TL::CPR;
-  constexpr int SMEM = 2 * (BM + BN) * BK;  // bf16 elements: double-buffered A and B tiles
-  // epilogue staging: SR rows of each wave's tile at a time (32, or 16 when 32 do not fit)
-  constexpr int SR = (TL::NW * 32 * (WTN + 4) * 4 <= SMEM * 2) ? 32 : 16;
-  static_assert(TL::NW * SR * (WTN + 4) * 4 <= SMEM * 2, "epilogue staging must fit in the tiles");
-  __shared__ __attribute__((aligned(16))) bf16_t smem[SMEM];
-  bf16_t* const sA = smem;                 // [2][BM * BK]
-  bf16_t* const sB = smem + 2 * BM * BK;   // [2][BN * BK]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-  const int wv = tid >> 6;
-  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
-  // tile order: XCD-contiguous ranges, then groups of `gm` M-tiles swept column by column so the
-  // tiles an XCD runs at once share a few A row-panels and B column-panels in its L2
-  const TileCoord tc = tile_coord(n_tiles, gm);
-  const int64_t mt = tc.mt;
-  const int nt = tc.nt;
-  const int64_t m0 = mt * BM;
-  const int n0 = nt * BN;
-  if (!as.tile_live(m0, BM)) return;
-
-  // global -> register loader: 16-byte chunk c of rows lr + 32*i, via buffer loads whose
-  // out-of-range offsets return zero (ragged M/N tails, conv padding taps)
-  const int c = tid % CPR;
-  const int lr = tid / CPR;
-  constexpr int RS = TL::RS;
-  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
-  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
-  typename AS::BRow arow[AR];
-  uint32_t boffr[BR];
-#pragma unroll
-  for (int i = 0; i < AR; ++i) arow[i] = as.brow(m0 + lr + RS * i);
-#pragma unroll
-  for (int i = 0; i < BR; ++i) {
-    const int n = n0 + lr + RS * i;
-    boffr[i] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
-  }
-  constexpr int NSET = TL::NPF > 2 ? TL::NPF : 2;
-  u32x4_t ra[NSET][AR], rb[NSET][BR];  // register sets
-  auto gload = [&](int kt, int set) {
-    const int k = kt * BK + c * 8;
-    const auto kc = as.kc(k);
-    const bool kok = k < K;
-#pragma unroll
-    for (int i = 0; i < AR; ++i)
-      ra[set][i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, (int)as.boff(arow[i], kc), 0, AE_GEMM_CPOL);
-#pragma unroll
-    for (int i = 0; i < BR; ++i) {
-      const uint32_t off = (kok && boffr[i] != 0x80000000u) ? boffr[i] + (uint32_t)k * 2u : 0x80000000u;
-      rb[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, (int)off, 0, AE_GEMM_CPOL);
-    }
-  };
-  auto sstore = [&](int buf, int set) {
-#pragma unroll
-    for (int i = 0; i < AR; ++i) {
-      const int r = lr + RS * i;
-      *reinterpret_cast<u32x4_t*>(&sA[buf * BM * BK + r * BK + ((c ^ swz<BK>(r)) * 8)]) = ra[set][i];
-    }
-#pragma unroll
-    for (int i = 0; i < BR; ++i) {
-      const int r = lr + RS * i;
-      *reinterpret_cast<u32x4_t*>(&sB[buf * BN * BK + r * BK + ((c ^ swz<BK>(r)) * 8)]) = rb[set][i];
-    }
-  };
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  // MFMA operand rows of this lane (the swizzle key depends on row % 16 = l32 % 16 only)
-  const int arow0 = wm * TL::WTM + l32;
-  const int brow0 = wn * TL::WTN + l32;
-  const int sw = swz<BK>(l32);
-  bf16x8_t af[2][TM], bfr[2][TN];
-  auto fload = [&](int buf, int ks, int slot) {
-    const bf16_t* pa = sA + buf * BM * BK + arow0 * BK;
-    const bf16_t* pb = sB + buf * BN * BK + brow0 * BK;
-    const int ch = ((ks * 2 + half) ^ sw) * 8;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) af[slot][i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * BK + ch);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[slot][j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * BK + ch);
-  };
-
-  auto mfmas = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][i], bfr[slot][j], acc[i][j],
-                                                            0, 0, 0);
-  };
-  constexpr int KS = BK / 16;
-  const int nk = (K + BK - 1) / BK;
-  if constexpr (TL::NPF > 1) {
-    // register ring: tile t is loaded into set t % NPF right after that set's previous tile was
-    // written to LDS, i.e. NPF tiles of MFMA work before it is needed
-    constexpr int NPF = TL::NPF;
-#pragma unroll
-    for (int p = 0; p < NPF; ++p)
-      if (p < nk) gload(p, p);
-    sstore(0, 0);
-    if (NPF < nk) gload(NPF, 0);
-    __syncthreads();
-    fload(0, 0, 0);
-    auto iter = [&](int kt, auto ph) {
-      constexpr int P = decltype(ph)::value;  // kt % NPF
-      constexpr int PN = (P + 1) % NPF;       // set of tile kt + 1
-      const bool more = kt + 1 < nk;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) {
-          fload(kt & 1, ks + 1, (ks + 1) & 1);
-        } else if (more) {
-          sstore((kt + 1) & 1, PN);
-          if (kt + 1 + NPF < nk) gload(kt + 1 + NPF, PN);
-          __syncthreads();
-          fload((kt + 1) & 1, 0, 0);
-        }
-        if constexpr (SCHED & 2) {
-          __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
-        }
-        mfmas(ks & 1);
-      }
-    };
-    for (int kt = 0; kt < nk; kt += NPF) {
-      iter(kt, std::integral_constant<int, 0>());
-      if constexpr (NPF > 1) if (kt + 1 < nk) iter(kt + 1, std::integral_constant<int, 1 % NPF>());
-      if constexpr (NPF > 2) if (kt + 2 < nk) iter(kt + 2, std::integral_constant<int, 2 % NPF>());
-      if constexpr (NPF > 3) if (kt + 3 < nk) iter(kt + 3, std::integral_constant<int, 3 % NPF>());
-    }
-    __syncthreads();
-  } else if constexpr ((SCHED & 5) == 0) {
-    gload(0, 0);
-    sstore(0, 0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1, 0);
-      fload(cur, 0, 0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) fload(cur, ks + 1, (ks + 1) & 1);
-        mfmas(ks & 1);
-      }
-      if (kt + 1 < nk) sstore(cur ^ 1, 0);
-      __syncthreads();
-    }
-  } else if constexpr ((SCHED & 4) == 0) {
-    gload(0, 0);
-    sstore(0, 0);
-    __syncthreads();
-    fload(0, 0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) gload(kt + 1, 0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) {
-          fload(cur, ks + 1, (ks + 1) & 1);
-        } else if (more) {
-          sstore(cur ^ 1, 0);
-          __syncthreads();
-          fload(cur ^ 1, 0, 0);
-        }
-        if constexpr (SCHED & 2) {
-          __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // DS reads (next K-step)
-          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);  // MFMAs (this K-step)
-        }
-        mfmas(ks & 1);
-      }
-    }
-    __syncthreads();  // the epilogue reuses the tile buffers as staging
-  } else {
-    // two-deep register prefetch: tile t lives in register set t & 1 from its load (issued two
-    // tiles ahead) until its LDS store at the end of tile t - 1
-    gload(0, 0);
-    sstore(0, 0);
-    __syncthreads();
-    if (nk > 1) gload(1, 1);
-    fload(0, 0, 0);
-    auto iter = [&](int kt, auto parity) {
-      constexpr int P = decltype(parity)::value;  // kt & 1
-      const bool more = kt + 1 < nk;
-      if (kt + 2 < nk) gload(kt + 2, P);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) {
-          fload(P, ks + 1, (ks + 1) & 1);
-        } else if (more) {
-          sstore(1 - P, 1 - P);
-          __syncthreads();
-          fload(1 - P, 0, 0);
-        }
-        if constexpr (SCHED & 2) {
-          __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
-        }
-        mfmas(ks & 1);
-      }
-    };
-    for (int kt = 0; kt < nk; kt += 2) {
-      iter(kt, std::integral_constant<int, 0>());
-      if (kt + 1 < nk) iter(kt + 1, std::integral_constant<int, 1>());
-    }
-    __syncthreads();
-  }
-
-  // epilogue through LDS: each wave writes SR rows of its accumulators row-major, then reads
-  // them back four columns per lane for 16-byte (fp32) / 8-byte (bf16) stores
-  constexpr int LDW = WTN + 4;
-  float* stg = reinterpret_cast<float*>(smem) + wv * SR * LDW;
-  const int wcol = n0 + wn * TL::WTN;
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-  for (int hs = 0; hs < 32 / SR; ++hs) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
-        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
-      }
-    __syncthreads();
-    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
-    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
-    __syncthreads();
-  }
-  }
-}
 
 // Direct-to-LDS variant: the tile loads are buffer_load_dwordx4 ... lds (gfx950 LDS DMA, 16
 // bytes per lane), so tile data never passes through VGPRs.  One LDS DMA instruction fills
@@ -732,461 +455,13 @@ __device__ inline void wait_vm_lds0() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
 }
 
-// Direct-to-LDS kernel with an NST-stage ring (tile kt+NST-1 is in flight while tile kt is
-// multiplied).  Each stage is its own __shared__ array: the compiler then knows which DMA a
-// fragment read can depend on, waits for that one only, and is free to interleave the reads of
-// one K step with the MFMAs of the previous one.  Per K tile:
-//   wait until this wave's DMA of tile kt has landed and its LDS reads of the stage about to
-//   be refilled are done; barrier (all waves) -> DMA of tile kt+NST-1 into the stage read at
-//   kt-1 -> fragment reads and MFMAs of tile kt.
+// NST-stage direct-to-LDS kernel.  Each stage is its own __shared__ array, so the compiler's
+// wait-count tracking knows which DMA a fragment read depends on and never holds a read back
+// for the DMAs of other stages.  One barrier per K step, at its start: it publishes tile kt and
+// frees the stage read in step kt-1, which is then refilled with tile kt+NST-1 in KS slices,
+// one slice issued between the MFMAs of each K sub-step; fragment reads of sub-step ks+1 are
+// issued before the MFMAs of ks.  Tile kt+NST-1 thus has NST-2 full steps to land.
 template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG>
-__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_pipe_kernel(AS as, const bf16_t* __restrict__ Bw,
-                                                                    int32_t N, int32_t K, OM om, EpiP ep,
-                                                                    int32_t n_tiles, int32_t pe_ld, int32_t gm) {
-  static_assert(NST >= 2 && NST <= 4, "stages");
-  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
-  constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
-  constexpr int STG = (BM + BN) * BK;  // bf16 elements per stage: A tile, then B tile
-  constexpr int SR = (NW * 32 * (WTN + 4) * 4 <= STG * 2) ? 32
-                     : (NW * 16 * (WTN + 4) * 4 <= STG * 2) ? 16 : 8;
-  static_assert(NW * SR * (WTN + 4) * 4 <= STG * 2, "epilogue staging must fit in one stage");
-  constexpr int ROWS_PER_DMA = 1024 / (BK * 2);
-  constexpr int ADMA = BM / ROWS_PER_DMA / NW;
-  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
-  constexpr int P = ADMA + BDMA;  // DMA instructions per wave per K tile
-  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
-  static_assert(P * (NST - 2) < 64, "vmcnt range");
-  constexpr int KS = BK / 16;
-  __shared__ __attribute__((aligned(1024))) bf16_t st0[STG];
-  __shared__ __attribute__((aligned(1024))) bf16_t st1[STG];
-  __shared__ __attribute__((aligned(1024))) bf16_t st2[NST > 2 ? STG : 8];
-  __shared__ __attribute__((aligned(1024))) bf16_t st3[NST > 3 ? STG : 8];
-  auto stage = [&](auto sc) -> bf16_t* {
-    constexpr int s = decltype(sc)::value;
-    if constexpr (s == 0) return st0;
-    else if constexpr (s == 1) return st1;
-    else if constexpr (s == 2) return st2;
-    else return st3;
-  };
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
-  const TileCoord tc = tile_coord(n_tiles, gm);
-  const int64_t mt = tc.mt;
-  const int nt = tc.nt;
-  const int64_t m0 = mt * BM;
-  const int n0 = nt * BN;
-  if (!as.tile_live(m0, BM)) return;
-
-  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
-  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
-  constexpr int CPR = BK / 8;
-  typename AS::BRow arow[ADMA];
-  int achunk[ADMA];
-  uint32_t boffr[BDMA];
-  int bchunk[BDMA];
-#pragma unroll
-  for (int j = 0; j < ADMA; ++j) {
-    const int r = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
-    achunk[j] = (lane % CPR) ^ swz<BK>(r);
-    arow[j] = as.brow(m0 + r);
-  }
-#pragma unroll
-  for (int j = 0; j < BDMA; ++j) {
-    const int r = (wv * BDMA + j) * ROWS_PER_DMA + lane / CPR;
-    bchunk[j] = (lane % CPR) ^ swz<BK>(r);
-    const int n = n0 + r;
-    boffr[j] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
-  }
-  auto dma = [&](int kt, bf16_t* st) {
-#pragma unroll
-    for (int j = 0; j < ADMA; ++j) {
-      const int k = kt * BK + achunk[j] * 8;
-      const uint32_t off = as.boff(arow[j], as.kc(k));
-      bf16_t* dst = st + (wv * ADMA + j) * ROWS_PER_DMA * BK;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
-                                               (int)off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < BDMA; ++j) {
-      const int k = kt * BK + bchunk[j] * 8;
-      const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
-      bf16_t* dst = st + BM * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
-                                               (int)off, 0, 0, 0);
-    }
-  };
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  const int arow0 = wm * TL::WTM + l32;
-  const int brow0 = wn * TL::WTN + l32;
-  const int sw = swz<BK>(l32);
-  auto compute = [&](const bf16_t* st) {
-    const bf16_t* pa = st + arow0 * BK;
-    const bf16_t* pb = st + BM * BK + brow0 * BK;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch = ((ks * 2 + half) ^ sw) * 8;
-      bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * BK + ch);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * BK + ch);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  const int nk = (K + BK - 1) / BK;
-  dma(0, st0);
-  if constexpr (NST > 2) if (1 < nk) dma(1, st1);
-  if constexpr (NST > 3) if (2 < nk) dma(2, st2);
-  auto iter = [&](int kt, auto sc) {
-    constexpr int s = decltype(sc)::value;
-    const int after = min(NST - 2, nk - 1 - kt);  // tiles issued after tile kt
-    if constexpr (NST > 3) {
-      if (after >= 2) wait_vm_lds0<2 * P>();
-      else if (after == 1) wait_vm_lds0<P>();
-      else wait_vm_lds0<0>();
-    } else if constexpr (NST > 2) {
-      if (after >= 1) wait_vm_lds0<P>();
-      else wait_vm_lds0<0>();
-    } else {
-      wait_vm_lds0<0>();
-    }
-    cbar();
-    __builtin_amdgcn_s_barrier();
-    cbar();
-    if (kt + NST - 1 < nk) dma(kt + NST - 1, stage(std::integral_constant<int, (s + NST - 1) % NST>()));
-    compute(stage(std::integral_constant<int, s>()));
-  };
-  for (int kt = 0; kt < nk; kt += NST) {
-    iter(kt, std::integral_constant<int, 0>());
-    if (kt + 1 < nk) iter(kt + 1, std::integral_constant<int, 1>());
-    if constexpr (NST > 2) if (kt + 2 < nk) iter(kt + 2, std::integral_constant<int, 2>());
-    if constexpr (NST > 3) if (kt + 3 < nk) iter(kt + 3, std::integral_constant<int, 3>());
-  }
-  wait_vm_lds0<0>();
-  __syncthreads();
-
-  constexpr int LDW = WTN + 4;
-  float* stg = reinterpret_cast<float*>(st0) + wv * SR * LDW;
-  const int wcol = n0 + wn * TL::WTN;
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-  for (int hs = 0; hs < 32 / SR; ++hs) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
-        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
-      }
-    __syncthreads();
-    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
-    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
-    __syncthreads();
-  }
-  }
-}
-
-// Epilogue straight from the accumulators of a wave (no LDS staging, no barriers).  The MFMAs
-// compute the transposed product (B fragment as the first operand), so lane l of a 32x32 block
-// holds output row l % 32 and, for register group g = v / 4, the four consecutive columns
-// 8 g + 4 (l / 32) .. +3: every lane stores 4-wide runs of its own row.
-template <int EPI, typename OT, int TM, int TN, class OM>
-__device__ __attribute__((always_inline)) inline void epilogue_direct(const f32x16_t (&acc)[TM][TN], int64_t mrow0, int ncol0,
-                                       int N, const OM& om, const EpiP& ep, int pe_ld, int lane) {
-  const int l32 = lane & 31, half = lane >> 5;
-  const bool vec = (N & 3) == 0;  // 4-wide runs are aligned and never straddle the end
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t row = mrow0 + i * 32 + l32;
-    const int64_t off = om.off(row);
-    if (off < 0) continue;
-    if constexpr (EPI == EPI_SWIGLU) {
-      // gate and up columns alternate in blocks of 32 (N % 64 == 0): block pairs (j, j+1)
-#pragma unroll
-      for (int j = 0; j + 1 < TN; j += 2) {
-        if (ncol0 + j * 32 >= N) continue;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = (ncol0 + j * 32) / 2 + 8 * g + 4 * half;
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = silu(acc[i][j][4 * g + e]) * acc[i][j + 1][4 * g + e];
-          Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off + col, o[0], o[1], o[2], o[3]);
-        }
-      }
-    } else {
-      const float* perow = nullptr;
-      if constexpr (EPI == EPI_PE) perow = ep.pe + (int64_t)ep.tok_pos[row] * pe_ld;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = ncol0 + j * 32 + 8 * g + 4 * half;
-          if (col >= N) continue;
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e];
-          if (vec) {
-            if constexpr (EPI == EPI_PE) {
-              const float4 pe = *reinterpret_cast<const float4*>(perow + col);
-              o[0] += pe.x; o[1] += pe.y; o[2] += pe.z; o[3] += pe.w;
-            } else if (ep.bias) {
-              const float4 b = *reinterpret_cast<const float4*>(ep.bias + col);
-              o[0] += b.x; o[1] += b.y; o[2] += b.z; o[3] += b.w;
-            }
-            if constexpr (EPI == EPI_RESADD) {
-              float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col);
-              const float4 c = *p;
-              *p = make_float4(c.x + o[0], c.y + o[1], c.z + o[2], c.w + o[3]);
-            } else if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_PE) {
-              *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col) =
-                  make_float4(o[0], o[1], o[2], o[3]);
-            } else {
-              if constexpr (EPI == EPI_BIAS_GELU) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = gelu_erf(o[e]);
-              }
-              Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off + col, o[0], o[1], o[2], o[3]);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (col + e >= N) break;
-              if constexpr (EPI == EPI_PE) {
-                reinterpret_cast<float*>(ep.C)[off + col + e] = o[e] + perow[col + e];
-              } else {
-                epi_store<EPI, OT>(ep, off, row, col + e, o[e]);
-              }
-            }
-          }
-        }
-      }
-    }
-  }
-}
-
-template <int P, int NMAX>
-__device__ inline void wait_tiles(int n) {  // vmcnt(P * n) lgkmcnt(0), n in [0, NMAX]
-  if constexpr (NMAX >= 3) if (n >= 3) { wait_vm_lds0<3 * P>(); return; }
-  if constexpr (NMAX >= 2) if (n >= 2) { wait_vm_lds0<2 * P>(); return; }
-  if constexpr (NMAX >= 1) if (n >= 1) { wait_vm_lds0<P>(); return; }
-  wait_vm_lds0<0>();
-}
-
-// As gemm_pipe_kernel, with the MFMA fragments double-buffered in registers: the fragment
-// reads of K step ks+1 are issued before the MFMAs of step ks, and the barrier that publishes
-// tile kt+1 sits before the MFMAs of the last step of tile kt, so the matrix pipe is fed across
-// tile boundaries even with one wave per SIMD.
-//   prologue: DMA tiles 0..NST-1, wait for tile 0, barrier, read step 0.
-//   tile kt, step ks < KS-1: read step ks+1; MFMAs of step ks.
-//   tile kt, last step: wait for tile kt+1 (and for this wave's reads), barrier, DMA of tile
-//   kt+NST into the stage just drained, read step 0 of tile kt+1; MFMAs of the last step.
-template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG, bool DIRECT = true>
-__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_pipe2_kernel(AS as, const bf16_t* __restrict__ Bw,
-                                                                     int32_t N, int32_t K, OM om, EpiP ep,
-                                                                     int32_t n_tiles, int32_t pe_ld, int32_t gm) {
-  static_assert(NST >= 2 && NST <= 4, "stages");
-  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
-  constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
-  constexpr int STG = (BM + BN) * BK;
-  constexpr int SR = (NW * 32 * (WTN + 4) * 4 <= STG * 2) ? 32
-                     : (NW * 16 * (WTN + 4) * 4 <= STG * 2) ? 16 : 8;
-  static_assert(NW * SR * (WTN + 4) * 4 <= STG * 2, "epilogue staging must fit in one stage");
-  constexpr int ROWS_PER_DMA = 1024 / (BK * 2);
-  constexpr int ADMA = BM / ROWS_PER_DMA / NW;
-  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
-  constexpr int P = ADMA + BDMA;
-  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
-  static_assert(P * (NST - 1) < 64, "vmcnt range");
-  constexpr int KS = BK / 16;
-  static_assert(KS % 2 == 0, "fragment buffers alternate by step parity");
-  __shared__ __attribute__((aligned(1024))) bf16_t st0[STG];
-  __shared__ __attribute__((aligned(1024))) bf16_t st1[STG];
-  __shared__ __attribute__((aligned(1024))) bf16_t st2[NST > 2 ? STG : 8];
-  __shared__ __attribute__((aligned(1024))) bf16_t st3[NST > 3 ? STG : 8];
-  auto stage = [&](auto sc) -> bf16_t* {
-    constexpr int s = decltype(sc)::value;
-    if constexpr (s == 0) return st0;
-    else if constexpr (s == 1) return st1;
-    else if constexpr (s == 2) return st2;
-    else return st3;
-  };
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
-  const TileCoord tc = tile_coord(n_tiles, gm);
-  const int64_t m0 = (int64_t)tc.mt * BM;
-  const int n0 = tc.nt * BN;
-  if (!as.tile_live(m0, BM)) return;
-
-  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
-  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
-  constexpr int CPR = BK / 8;
-  typename AS::BRow arow[ADMA];
-  int achunk[ADMA];
-  uint32_t boffr[BDMA];
-  int bchunk[BDMA];
-#pragma unroll
-  for (int j = 0; j < ADMA; ++j) {
-    const int r = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
-    achunk[j] = (lane % CPR) ^ swz<BK>(r);
-    arow[j] = as.brow(m0 + r);
-  }
-#pragma unroll
-  for (int j = 0; j < BDMA; ++j) {
-    const int r = (wv * BDMA + j) * ROWS_PER_DMA + lane / CPR;
-    bchunk[j] = (lane % CPR) ^ swz<BK>(r);
-    const int n = n0 + r;
-    boffr[j] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
-  }
-  auto dma = [&](int kt, bf16_t* st) {
-#pragma unroll
-    for (int j = 0; j < ADMA; ++j) {
-      const int k = kt * BK + achunk[j] * 8;
-      const uint32_t off = as.boff(arow[j], as.kc(k));
-      bf16_t* dst = st + (wv * ADMA + j) * ROWS_PER_DMA * BK;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
-                                               (int)off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < BDMA; ++j) {
-      const int k = kt * BK + bchunk[j] * 8;
-      const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
-      bf16_t* dst = st + BM * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
-                                               (int)off, 0, 0, 0);
-    }
-  };
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  const int aoff = (wm * TL::WTM + l32) * BK;
-  const int boff = BM * BK + (wn * TL::WTN + l32) * BK;
-  const int sw = swz<BK>(l32);
-  bf16x8_t fa[2][TM], fb[2][TN];
-  auto rd = [&](const bf16_t* st, int ks, int buf) {
-    const int ch = ((ks * 2 + half) ^ sw) * 8;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoff + i * 32 * BK + ch);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boff + j * 32 * BK + ch);
-  };
-  auto mm = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        if constexpr (DIRECT)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
-  };
-  auto barrier = [&]() {
-    cbar();
-    __builtin_amdgcn_s_barrier();
-    cbar();
-  };
-
-  // The K loop runs over a multiple of NST tiles, and tiles past the end of K are issued like
-  // any other: every offset is out of range, so they only write zeros into stages whose
-  // products add nothing.  The loop body is then free of branches and each wave always has the
-  // same number of DMAs in flight, so every wait below is a constant (the compiler's wait-count
-  // tracking merges the states of branches conservatively and would otherwise stall MFMAs on
-  // fragment reads they do not use).
-  const int nk = (K + BK * NST - 1) / (BK * NST) * NST;
-  dma(0, st0);
-  dma(1, st1);
-  if constexpr (NST > 2) dma(2, st2);
-  if constexpr (NST > 3) dma(3, st3);
-  wait_vm_lds0<P * (NST - 1)>();
-  barrier();
-  rd(st0, 0, 0);
-
-  auto tile_step = [&](int kt, auto sc) {
-    constexpr int s = decltype(sc)::value;
-    const bf16_t* cur = stage(sc);
-#pragma unroll
-    for (int ks = 0; ks + 1 < KS; ++ks) {
-      rd(cur, ks + 1, (ks + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs they overlap
-      mm(ks & 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_vm_lds0<P * (NST - 2)>();
-    barrier();
-    dma(kt + NST, stage(sc));
-    rd(stage(std::integral_constant<int, (s + 1) % NST>()), 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mm((KS - 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  for (int kt = 0; kt < nk; kt += NST) {
-    tile_step(kt, std::integral_constant<int, 0>());
-    tile_step(kt + 1, std::integral_constant<int, 1>());
-    if constexpr (NST > 2) tile_step(kt + 2, std::integral_constant<int, 2>());
-    if constexpr (NST > 3) tile_step(kt + 3, std::integral_constant<int, 3>());
-  }
-  if constexpr (DIRECT) {
-    epilogue_direct<EPI, OT, TM, TN>(acc, m0 + wm * TL::WTM, n0 + wn * TL::WTN, N, om, ep, pe_ld, lane);
-    wait_vm_lds0<0>();  // the trailing out-of-range DMAs land before the LDS is released
-    return;
-  }
-  wait_vm_lds0<0>();
-  __syncthreads();
-
-  constexpr int LDW = WTN + 4;
-  float* stg = reinterpret_cast<float*>(st0) + wv * SR * LDW;
-  const int wcol = n0 + wn * TL::WTN;
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-  for (int hs = 0; hs < 32 / SR; ++hs) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
-        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
-      }
-    __syncthreads();
-    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
-    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
-    __syncthreads();
-  }
-  }
-}
-
-// NST-stage direct-to-LDS kernel with the refill DMAs spread over the MFMAs.  One barrier per K
-// step, at its start: it publishes tile kt and frees the stage read in step kt-1, which is then
-// refilled with tile kt+NST-1 in KS slices, one slice issued between the MFMAs of each K
-// sub-step (issuing a whole tile's DMAs at once backs up the load queue and stalls the issuing
-// waves, MFMAs included).  Fragment reads of sub-step ks+1 are issued before the MFMAs of ks.
-template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG, bool DIRECT = false>
 __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const bf16_t* __restrict__ Bw,
                                                                    int32_t N, int32_t K, OM om, EpiP ep,
                                                                    int32_t n_tiles, int32_t pe_ld, int32_t gm) {
@@ -1290,12 +565,8 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if constexpr (DIRECT)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
-      }
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
   };
   auto barrier = [&]() {
     cbar();
@@ -1303,8 +574,12 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
     cbar();
   };
 
-  // As in gemm_pipe2_kernel: a multiple of NST steps, with out-of-range tiles past the end of K
-  // (zero fill), so every wait is a constant.
+  // The K loop runs over a multiple of NST tiles, and tiles past the end of K are issued like
+  // any other: every offset is out of range, so they only write zeros into stages whose
+  // products add nothing.  The loop body is then free of branches and each wave always has the
+  // same number of DMAs in flight, so every wait is a constant (the compiler's wait-count
+  // tracking merges the states of branches conservatively and would otherwise stall MFMAs on
+  // fragment reads they do not use).
   const int nk = (K + BK * NST - 1) / (BK * NST) * NST;
   dma_part(0, st0, 0, P);
   dma_part(1, st1, 0, P);
@@ -1339,412 +614,11 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
     step(kt + 2, std::integral_constant<int, 2>());
     if constexpr (NST > 3) step(kt + 3, std::integral_constant<int, 3>());
   }
-  if constexpr (DIRECT) {
-    epilogue_direct<EPI, OT, TM, TN>(acc, m0 + wm * TL::WTM, n0 + wn * TL::WTN, N, om, ep, pe_ld, lane);
-    wait_vm_lds0<0>();  // the trailing out-of-range DMAs land before the LDS is released
-    return;
-  }
-  wait_vm_lds0<0>();
+  wait_vm_lds0<0>();  // the trailing zero-fill DMAs land before the stages are reused
   __syncthreads();
 
   constexpr int LDW = WTN + 4;
   float* stg = reinterpret_cast<float*>(st0) + wv * SR * LDW;
-  const int wcol = n0 + wn * TL::WTN;
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-  for (int hs = 0; hs < 32 / SR; ++hs) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
-        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
-      }
-    __syncthreads();
-    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
-    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
-    __syncthreads();
-  }
-  }
-}
-
-// Persistent form of gemm_pipe2_kernel: a grid of at most one wave of resident workgroups, each
-// walking a sequence of output tiles.  The DMA stream runs NST-1 K steps ahead across tile
-// boundaries, so the next tile's first stages load while the current one finishes, and the
-// epilogue (straight from registers, no barrier) drains while the next tile's MFMAs run.
-//   Tile order: the logical tiles (groups of gm m-tiles walked column by column) are split into
-//   8 contiguous chunks, one per XCD (workgroup b runs on XCD b % 8); the workgroups of an XCD
-//   take the tiles of its chunk round-robin, so the tiles in flight on one XCD are neighbours
-//   and share A rows and B columns in its L2.  Tiles whose rows are all padding are skipped.
-template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG>
-__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_persist_kernel(AS as, const bf16_t* __restrict__ Bw,
-                                                                       int32_t N, int32_t K, OM om, EpiP ep,
-                                                                       int32_t m_tiles, int32_t n_tiles,
-                                                                       int32_t pe_ld, int32_t gm) {
-  static_assert(NST >= 2 && NST <= 4, "stages");
-  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
-  constexpr int BK = TL::BK, NW = TL::NW;
-  constexpr int STG = (BM + BN) * BK;
-  constexpr int ROWS_PER_DMA = 1024 / (BK * 2);
-  constexpr int ADMA = BM / ROWS_PER_DMA / NW;
-  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
-  constexpr int P = ADMA + BDMA;
-  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
-  static_assert(P * (NST - 1) < 64, "vmcnt range");
-  constexpr int KS = BK / 16;
-  static_assert(KS % 2 == 0, "fragment buffers alternate by step parity");
-  __shared__ __attribute__((aligned(1024))) bf16_t st0[STG];
-  __shared__ __attribute__((aligned(1024))) bf16_t st1[STG];
-  __shared__ __attribute__((aligned(1024))) bf16_t st2[NST > 2 ? STG : 8];
-  __shared__ __attribute__((aligned(1024))) bf16_t st3[NST > 3 ? STG : 8];
-  auto stage = [&](auto sc) -> bf16_t* {
-    constexpr int s = decltype(sc)::value;
-    if constexpr (s == 0) return st0;
-    else if constexpr (s == 1) return st1;
-    else if constexpr (s == 2) return st2;
-    else return st3;
-  };
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
-
-  // this workgroup's tiles: c0 + q + j * Gx for j = 0, 1, ... below c1
-  const int T = m_tiles * n_tiles;
-  const int G = gridDim.x;
-  const int xcd = blockIdx.x % 8, q = blockIdx.x / 8;
-  const int Gx = G / 8 + (xcd < G % 8 ? 1 : 0);
-  const int before = xcd * (G / 8) + min(xcd, G % 8);
-  const int c0 = (int)((int64_t)T * before / G);
-  const int c1 = (int)((int64_t)T * (before + Gx) / G);
-  const int n_my = c1 - c0 > q ? (c1 - c0 - q + Gx - 1) / Gx : 0;
-  const int gsize = gm * n_tiles;
-  auto coord = [&](int j) -> TileCoord {
-    const int t = c0 + q + j * Gx;
-    const int g = t / gsize;
-    const int first_m = g * gm;
-    const int gh = m_tiles - first_m < gm ? m_tiles - first_m : gm;
-    const int in_g = t - g * gsize;
-    return TileCoord{__builtin_amdgcn_readfirstlane(first_m + in_g % gh),
-                     __builtin_amdgcn_readfirstlane(in_g / gh)};
-  };
-  auto live = [&](int j) { return as.tile_live((int64_t)coord(j).mt * BM, BM); };
-  auto next_live = [&](int j) {
-    while (j < n_my && !live(j)) ++j;
-    return j;
-  };
-  int cj = next_live(0);  // tile being multiplied
-  if (cj >= n_my) return;
-
-  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
-  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
-  constexpr int CPR = BK / 8;
-  int achunk[ADMA], bchunk[BDMA], arl[ADMA], brl[BDMA];
-#pragma unroll
-  for (int j = 0; j < ADMA; ++j) {
-    arl[j] = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
-    achunk[j] = (lane % CPR) ^ swz<BK>(arl[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < BDMA; ++j) {
-    brl[j] = (wv * BDMA + j) * ROWS_PER_DMA + lane / CPR;
-    bchunk[j] = (lane % CPR) ^ swz<BK>(brl[j]);
-  }
-  // DMA side: tile dj, K step dk, and the per-lane row offsets of tile dj (all out of range once
-  // the sequence is exhausted, so the stream keeps its shape with zero-filling loads)
-  typename AS::BRow arow[ADMA];
-  uint32_t boffr[BDMA];
-  int dj = cj, dk = 0;
-  auto setup = [&](int j) {
-    const bool ok = j < n_my;
-    const TileCoord tc = ok ? coord(j) : TileCoord{m_tiles, 0};
-    const int64_t m0 = (int64_t)tc.mt * BM;
-    const int n0 = tc.nt * BN;
-#pragma unroll
-    for (int i = 0; i < ADMA; ++i) arow[i] = as.brow(m0 + arl[i]);
-#pragma unroll
-    for (int i = 0; i < BDMA; ++i) {
-      const int n = n0 + brl[i];
-      boffr[i] = (ok && n < N) ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
-    }
-  };
-  const int nk = (K + BK * NST - 1) / (BK * NST) * NST;
-  auto dma = [&](bf16_t* st) {
-#pragma unroll
-    for (int j = 0; j < ADMA; ++j) {
-      const int k = dk * BK + achunk[j] * 8;
-      const uint32_t off = as.boff(arow[j], as.kc(k));
-      bf16_t* dst = st + (wv * ADMA + j) * ROWS_PER_DMA * BK;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
-                                               (int)off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < BDMA; ++j) {
-      const int k = dk * BK + bchunk[j] * 8;
-      const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
-      bf16_t* dst = st + BM * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
-                                               (int)off, 0, 0, 0);
-    }
-    if (++dk == nk) {
-      dk = 0;
-      dj = next_live(dj + 1);
-      setup(dj);
-    }
-  };
-
-  f32x16_t acc[TM][TN];
-  auto zero = [&]() {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  };
-  zero();
-
-  const int aoff = (wm * TL::WTM + l32) * BK;
-  const int boff = BM * BK + (wn * TL::WTN + l32) * BK;
-  const int sw = swz<BK>(l32);
-  bf16x8_t fa[2][TM], fb[2][TN];
-  auto rd = [&](const bf16_t* st, int ks, int buf) {
-    const int ch = ((ks * 2 + half) ^ sw) * 8;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoff + i * 32 * BK + ch);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boff + j * 32 * BK + ch);
-  };
-  auto mm = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-  };
-  auto barrier = [&]() {
-    cbar();
-    __builtin_amdgcn_s_barrier();
-    cbar();
-  };
-
-  setup(dj);
-  dma(st0);
-  dma(st1);
-  if constexpr (NST > 2) dma(st2);
-  if constexpr (NST > 3) dma(st3);
-  wait_vm_lds0<P * (NST - 1)>();
-  barrier();
-  rd(st0, 0, 0);
-
-  int ck = 0;
-  auto step = [&](auto sc) {
-    constexpr int s = decltype(sc)::value;
-    const bf16_t* cur = stage(sc);
-#pragma unroll
-    for (int ks = 0; ks + 1 < KS; ++ks) {
-      rd(cur, ks + 1, (ks + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mm(ks & 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_vm_lds0<P * (NST - 2)>();
-    barrier();
-    dma(stage(sc));
-    rd(stage(std::integral_constant<int, (s + 1) % NST>()), 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mm((KS - 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  while (cj < n_my) {
-    step(std::integral_constant<int, 0>());
-    step(std::integral_constant<int, 1>());
-    if constexpr (NST > 2) step(std::integral_constant<int, 2>());
-    if constexpr (NST > 3) step(std::integral_constant<int, 3>());
-    ck += NST;  // nk is a multiple of NST: a tile ends on the last step of a group
-    if (ck == nk) {
-      const TileCoord tc = coord(cj);
-      epilogue_direct<EPI, OT, TM, TN>(acc, (int64_t)tc.mt * BM + wm * TL::WTM, tc.nt * BN + wn * TL::WTN,
-                                       N, om, ep, pe_ld, lane);
-      zero();
-      ck = 0;
-      cj = next_live(cj + 1);
-    }
-  }
-  wait_vm_lds0<0>();  // the trailing zero-filling DMAs land before the LDS is released
-}
-
-// MFMA fragments of one K-step (BK = 32: 32-row blocks 2048 bytes apart) read from LDS by one
-// (outputs are early-clobber: no output may share a register with the address inputs)
-// inline-asm block that waits for its own reads before it ends, so the compiler never sees an
-// LDS read that could alias the in-flight LDS DMA of later stages (it would otherwise wait for
-// every outstanding DMA before each read).
-typedef __attribute__((address_space(3))) const void* lds_cptr;
-template <int TM, int TN> struct FragK32;
-template <> struct FragK32<2, 2> {
-  __device__ static inline void load(lds_cptr a, lds_cptr b, bf16x8_t* af, bf16x8_t* bf) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %4 offset:2048\n\t"
-        "ds_read_b128 %2, %5\n\t"
-        "ds_read_b128 %3, %5 offset:2048\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(bf[0]), "=&v"(bf[1])
-        : "v"(a), "v"(b)
-        : "memory");
-  }
-};
-template <> struct FragK32<4, 2> {
-  __device__ static inline void load(lds_cptr a, lds_cptr b, bf16x8_t* af, bf16x8_t* bf) {
-    asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %6 offset:2048\n\t"
-        "ds_read_b128 %2, %6 offset:4096\n\t"
-        "ds_read_b128 %3, %6 offset:6144\n\t"
-        "ds_read_b128 %4, %7\n\t"
-        "ds_read_b128 %5, %7 offset:2048\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bf[0]), "=&v"(bf[1])
-        : "v"(a), "v"(b)
-        : "memory");
-  }
-};
-template <> struct FragK32<2, 4> {
-  __device__ static inline void load(lds_cptr a, lds_cptr b, bf16x8_t* af, bf16x8_t* bf) {
-    asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %6 offset:2048\n\t"
-        "ds_read_b128 %2, %7\n\t"
-        "ds_read_b128 %3, %7 offset:2048\n\t"
-        "ds_read_b128 %4, %7 offset:4096\n\t"
-        "ds_read_b128 %5, %7 offset:6144\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3])
-        : "v"(a), "v"(b)
-        : "memory");
-  }
-};
-
-// Ring-pipelined direct-to-LDS GEMM (BK = 32): NST LDS stages; the DMA of tile kt + NST - 1 is
-// issued right after the barrier of tile kt, so each tile's loads have NST - 1 tiles of MFMA
-// work to land.  Every iteration issues the same number of DMA instructions (tiles past the end
-// read as zero into a stage that is never read again), so "this tile has landed" is the fixed
-// wait vmcnt <= (NST - 2) * (DMA instructions per tile).
-template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG>
-__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ring_kernel(AS as, const bf16_t* __restrict__ Bw,
-                                                                    int32_t N, int32_t K, OM om, EpiP ep,
-                                                                    int32_t n_tiles, int32_t pe_ld, int32_t gm) {
-  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
-  constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
-  static_assert(BK == 32, "ring kernel uses BK = 32");
-  constexpr int STAGE = (BM + BN) * BK;                   // bf16 elements per stage
-  constexpr int SMEM = NST * STAGE;
-  constexpr int SR = (NW * 32 * (WTN + 4) * 4 <= SMEM * 2) ? 32 : 16;
-  static_assert(NW * SR * (WTN + 4) * 4 <= SMEM * 2, "epilogue staging must fit in the tiles");
-  constexpr int ROWS_PER_DMA = 1024 / (BK * 2);           // 16 rows of 64 bytes
-  constexpr int ADMA = BM / ROWS_PER_DMA / NW;
-  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
-  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
-  constexpr int NDMA = ADMA + BDMA;
-  constexpr int VMC = (NST - 2) * NDMA;
-  static_assert(VMC < 64, "vmcnt range");
-  constexpr int WAIT_TILE = (VMC & 15) | (7 << 4) | (15 << 8) | ((VMC >> 4) << 14);
-  constexpr int KS = BK / 16;
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
-  const TileCoord tc = tile_coord(n_tiles, gm);
-  const int64_t mt = tc.mt;
-  const int nt = tc.nt;
-  const int64_t m0 = mt * BM;
-  const int n0 = nt * BN;
-  if (!as.tile_live(m0, BM)) return;
-
-  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
-  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bw, (int64_t)N * K * 2);
-  constexpr int CPR = BK / 8;
-  typename AS::BRow arow[ADMA];
-  int achunk[ADMA];
-  uint32_t boffr[BDMA];
-  int bchunk[BDMA];
-#pragma unroll
-  for (int j = 0; j < ADMA; ++j) {
-    const int r = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
-    achunk[j] = (lane % CPR) ^ swz<BK>(r);
-    arow[j] = as.brow(m0 + r);
-  }
-#pragma unroll
-  for (int j = 0; j < BDMA; ++j) {
-    const int r = (wv * BDMA + j) * ROWS_PER_DMA + lane / CPR;
-    bchunk[j] = (lane % CPR) ^ swz<BK>(r);
-    const int n = n0 + r;
-    boffr[j] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
-  }
-  auto dma = [&](int kt, int stage) {
-    bf16_t* sa = smem + stage * STAGE;
-    bf16_t* sb = sa + BM * BK;
-#pragma unroll
-    for (int j = 0; j < ADMA; ++j) {
-      const int k = kt * BK + achunk[j] * 8;
-      const uint32_t off = as.boff(arow[j], as.kc(k));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra_rsrc, (__attribute__((address_space(3))) void*)(sa + (wv * ADMA + j) * ROWS_PER_DMA * BK),
-          16, (int)off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < BDMA; ++j) {
-      const int k = kt * BK + bchunk[j] * 8;
-      const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb_rsrc, (__attribute__((address_space(3))) void*)(sb + (wv * BDMA + j) * ROWS_PER_DMA * BK),
-          16, (int)off, 0, 0, 0);
-    }
-  };
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  const int arow0 = wm * TL::WTM + l32;
-  const int brow0 = wn * TL::WTN + l32;
-  const int sw = swz<BK>(l32);
-  const int nk = (K + BK - 1) / BK;
-#pragma unroll
-  for (int t = 0; t < NST - 1; ++t) dma(t, t);
-  int stage = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    __builtin_amdgcn_s_waitcnt(WAIT_TILE);  // this wave's DMA of tile kt has landed
-    __builtin_amdgcn_s_barrier();           // all waves: tile kt in LDS, tile kt-1 consumed
-    dma(kt + NST - 1, stage == 0 ? NST - 1 : stage - 1);
-    const bf16_t* sa = smem + stage * STAGE;
-    const bf16_t* sb = sa + BM * BK;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch = ((ks * 2 + half) ^ sw) * 8;
-      bf16x8_t af[TM], bfr[TN];
-      FragK32<TM, TN>::load((lds_cptr)(sa + arow0 * BK + ch), (lds_cptr)(sb + brow0 * BK + ch), af, bfr);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    stage = stage + 1 == NST ? 0 : stage + 1;
-  }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the trailing zero-fill DMAs have landed
-  __syncthreads();
-
-  constexpr int LDW = WTN + 4;
-  float* stg = reinterpret_cast<float*>(smem) + wv * SR * LDW;
   const int wcol = n0 + wn * TL::WTN;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {

@@ -102,7 +102,7 @@ def measured_traffic(role: str, cfg_note: str = "full-size tower, 16 x 30 s clip
     return round(t["fetch_bytes"] + t["write_bytes"])
 
 
-def cpu_baseline(pcm, weights, cfg, max_windows: int = 12) -> dict:
+def cpu_baseline(pcm, weights, cfg, max_windows: int = 24) -> dict:
     """The float64 oracle on the first `max_windows` 8 s windows of the batch (clip by clip;
     about 10-30 s of CPU work), scaled to audio-seconds per second."""
     import numpy as np
