@@ -71,11 +71,14 @@ _SIGS = {
     "encoder_output_frames": [POINTER(EncoderCfg), c_int64, POINTER(c_int64)],
     "encoder_plan_windows": [POINTER(EncoderCfg), c_int64, c_int32, POINTER(c_int32), c_int32,
                              POINTER(c_int32)],
+    "encoder_plan_windows_ragged": [POINTER(EncoderCfg), POINTER(c_int64), c_int32, POINTER(c_int32),
+                                    c_int32, POINTER(c_int32)],
     "encoder_create": [POINTER(c_float), c_int64, POINTER(EncoderCfg), POINTER(c_void_p)],
     "encoder_destroy": [c_void_p],
     "encoder_memory_stats": [c_void_p, POINTER(c_int64), POINTER(c_int64)],
     "encoder_forward": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
     "encoder_forward_long": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
+    "encoder_forward_ragged": [c_void_p, c_void_p, POINTER(c_int64), c_int32, c_void_p, c_void_p],
     "encoder_log_mel": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
     "encoder_debug_stage": [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p,
                             c_int64, c_void_p],
@@ -138,6 +141,22 @@ def encoder_plan_windows(cfg: dict, n_samples: int, batch: int) -> np.ndarray:
     _check(lib().encoder_plan_windows(ctypes.byref(c), n_samples, batch,
                                       tab.ctypes.data_as(POINTER(c_int32)), nw.value,
                                       ctypes.byref(nw)))
+    return tab
+
+
+def _lengths(lengths) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(lengths, dtype=np.int64).ravel())
+
+
+def encoder_plan_windows_ragged(cfg: dict, lengths) -> np.ndarray:
+    """Window plan of a ragged call (clips of the given sample lengths, back to back)."""
+    c, nw, L = make_cfg(cfg), c_int32(), _lengths(lengths)
+    lp = L.ctypes.data_as(POINTER(c_int64))
+    _check(lib().encoder_plan_windows_ragged(ctypes.byref(c), lp, L.size, None, 0, ctypes.byref(nw)))
+    tab = np.zeros((nw.value, 7), dtype=np.int32)
+    _check(lib().encoder_plan_windows_ragged(ctypes.byref(c), lp, L.size,
+                                             tab.ctypes.data_as(POINTER(c_int32)), nw.value,
+                                             ctypes.byref(nw)))
     return tab
 
 
@@ -207,6 +226,22 @@ class Encoder:
             out = torch.empty((F, self.cfg["d_out"]), dtype=self.out_dtype, device=pcm.device)
         _check(lib().encoder_forward_long(self._h, _ptr(pcm), N, pieces_per_pass, _ptr(out),
                                           _stream()))
+        return out
+
+    def forward_ragged(self, pcm, lengths, out=None):
+        """pcm: float32 CUDA tensor of the clips back to back (sum(lengths) samples);
+        lengths: per-clip sample counts -> [sum_c F_c, d_out], clips in order."""
+        import torch
+        assert pcm.is_cuda and pcm.dtype == torch.float32 and pcm.is_contiguous()
+        L = _lengths(lengths)
+        if int(L.sum()) != pcm.numel():
+            raise ValueError(f"lengths add up to {int(L.sum())} samples, pcm has {pcm.numel()}")
+        F = sum(self.output_frames(int(n)) for n in L) if all(n > 200 for n in L) else 0
+        if out is None:
+            out = torch.empty((max(F, 1), self.cfg["d_out"]), dtype=self.out_dtype,
+                              device=pcm.device)[:F]
+        _check(lib().encoder_forward_ragged(self._h, _ptr(pcm), L.ctypes.data_as(POINTER(c_int64)),
+                                            L.size, _ptr(out), _stream()))
         return out
 
     def log_mel(self, pcm):

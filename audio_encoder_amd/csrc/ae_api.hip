@@ -90,26 +90,41 @@ static std::vector<int64_t> blob_sizes(const encoder_cfg& c) {
 // ------------------------------------------------------------------------------------------
 // window plan
 // ------------------------------------------------------------------------------------------
-static void plan_windows(const encoder_cfg& c, int64_t n_samples, int32_t batch,
+// Clips are laid out back to back: clip b's samples start at the sum of the earlier lengths,
+// its log-mel frames at the sum of the earlier frame counts, and its windows follow those of
+// clip b-1 in the token stream (so its output rows do too).
+static void clip_spans(const encoder_cfg& c, const std::vector<int64_t>& lens,
+                       std::vector<ClipSpan>& out) {
+  out.clear();
+  int64_t so = 0, fo = 0;
+  for (int64_t n : lens) {
+    out.push_back(ClipSpan{so, n, fo});
+    so += n;
+    fo += n / c.hop;
+  }
+}
+
+static void plan_windows(const encoder_cfg& c, const std::vector<int64_t>& lens,
                          std::vector<Win>& out) {
-  const int64_t T = n_samples / c.hop;
   const int64_t wf = 8 * (int64_t)c.window_tokens;
   out.clear();
-  int64_t tok = 0;
-  for (int32_t b = 0; b < batch; ++b) {
+  int64_t tok = 0, fo = 0;
+  for (size_t b = 0; b < lens.size(); ++b) {
+    const int64_t T = lens[b] / c.hop;
     for (int64_t s = 0; s < T; s += wf) {
       Win w;
-      w.clip = b;
+      w.clip = (int32_t)b;
       w.start = (int32_t)s;
       w.L0 = (int32_t)std::min<int64_t>(wf, T - s);
       w.L1 = (w.L0 + 1) / 2;
       w.L2 = (w.L1 + 1) / 2;
       w.L3 = (w.L2 + 1) / 2;
       w.tok = (int32_t)tok;
-      w.pad = 0;
+      w.mel_row = (int32_t)(fo + s);
       tok += w.L3;
       out.push_back(w);
     }
+    fo += T;
   }
 }
 
@@ -251,7 +266,7 @@ struct encoder {
   MelTables mel;
   // workspace (grown on demand)
   struct Buf { void* p = nullptr; int64_t bytes = 0; };
-  Buf mel_raw, max_key, wtab, tpos, act1, act2, tokA, resid, xn, qkv, attn, hid, hid2, z, dbg;
+  Buf mel_raw, max_key, ctab, wtab, tpos, act1, act2, tokA, resid, xn, qkv, attn, hid, hid2, z, dbg;
   int64_t ws_bytes = 0, ws_peak = 0;
   // host staging for the plan upload
   void* pinned = nullptr;
@@ -328,14 +343,21 @@ struct Tm {
     if (_err != hipSuccess) return hip_fail(_err, #call); \
   } while (0)
 
-// workspace for passes of up to mt tokens / mw windows, and a log-mel of nclip x T frames
-encoder_status size_workspace(encoder* e, int64_t nclip, int64_t T, int64_t mt, int64_t mw,
+// log-mel of n_frames frames over nclip clips
+encoder_status size_mel(encoder* e, int64_t nclip, int64_t n_frames) {
+  encoder_status st;
+  if ((st = ensure(e, e->mel_raw, std::max<int64_t>(n_frames, 1) * 128 * 4))) return st;
+  if ((st = ensure(e, e->max_key, std::max<int64_t>(nclip, 1) * 4))) return st;
+  return ensure(e, e->ctab, std::max<int64_t>(nclip, 1) * (int64_t)sizeof(ClipSpan));
+}
+
+// workspace for passes of up to mt tokens / mw windows, and the log-mel of the call
+encoder_status size_workspace(encoder* e, int64_t nclip, int64_t n_frames, int64_t mt, int64_t mw,
                               int64_t n_win_total, int64_t n_tok_total) {
   const encoder_cfg& c = e->cfg;
   const int64_t es = (int64_t)e->esz, C = c.conv_channels, W = c.window_tokens, d = c.d_model;
   encoder_status st;
-  if ((st = ensure(e, e->mel_raw, nclip * T * 128 * 4))) return st;
-  if ((st = ensure(e, e->max_key, std::max<int64_t>(nclip, 1) * 4))) return st;
+  if ((st = size_mel(e, nclip, n_frames))) return st;
   if ((st = ensure(e, e->wtab, n_win_total * (int64_t)sizeof(Win)))) return st;
   if ((st = ensure(e, e->tpos, std::max<int64_t>(n_tok_total, 1) * 4))) return st;
   if ((st = ensure(e, e->act1, mw * 4 * W * 64 * C * es))) return st;
@@ -352,9 +374,9 @@ encoder_status size_workspace(encoder* e, int64_t nclip, int64_t T, int64_t mt, 
   return ENC_OK;
 }
 
-// plan + per-pass relative token indices, uploaded once per call
-encoder_status upload_plan(encoder* e, const std::vector<Win>& wins, const std::vector<Pass>& ps,
-                           hipStream_t s) {
+// clip spans, plan and per-pass relative token indices, uploaded once per call
+encoder_status upload_plan(encoder* e, const std::vector<ClipSpan>& clips, const std::vector<Win>& wins,
+                           const std::vector<Pass>& ps, hipStream_t s) {
   std::vector<Win> rel(wins);
   int64_t ntok = 0;
   for (const Pass& p : ps) ntok += p.ntok;
@@ -365,21 +387,25 @@ encoder_status upload_plan(encoder* e, const std::vector<Win>& wins, const std::
       for (int j = 0; j < wins[i].L3; ++j) tp[wins[i].tok + j] = j;
     }
   const int64_t wb = (int64_t)rel.size() * (int64_t)sizeof(Win), tb = ntok * 4;
-  if (e->pinned_bytes < wb + tb) {
+  const int64_t cb = (int64_t)clips.size() * (int64_t)sizeof(ClipSpan);
+  if (e->pinned_bytes < cb + wb + tb) {
     if (e->pinned) {
       AE_HIP(hipEventSynchronize(e->upload_done));
       AE_HIP(hipHostFree(e->pinned));
       e->pinned = nullptr;
       e->pinned_bytes = 0;
     }
-    AE_HIP(hipHostMalloc(&e->pinned, wb + tb, hipHostMallocDefault));
-    e->pinned_bytes = wb + tb;
+    AE_HIP(hipHostMalloc(&e->pinned, cb + wb + tb, hipHostMallocDefault));
+    e->pinned_bytes = cb + wb + tb;
   }
   AE_HIP(hipEventSynchronize(e->upload_done));  // the previous upload has left the staging area
-  std::memcpy(e->pinned, rel.data(), wb);
-  std::memcpy((char*)e->pinned + wb, tp.data(), tb);
-  AE_HIP(hipMemcpyAsync(e->wtab.p, e->pinned, wb, hipMemcpyHostToDevice, s));
-  AE_HIP(hipMemcpyAsync(e->tpos.p, (char*)e->pinned + wb, tb, hipMemcpyHostToDevice, s));
+  char* hp = (char*)e->pinned;
+  if (cb) std::memcpy(hp, clips.data(), cb);
+  if (wb) std::memcpy(hp + cb, rel.data(), wb);
+  if (tb) std::memcpy(hp + cb + wb, tp.data(), tb);
+  if (cb) AE_HIP(hipMemcpyAsync(e->ctab.p, hp, cb, hipMemcpyHostToDevice, s));
+  if (wb) AE_HIP(hipMemcpyAsync(e->wtab.p, hp + cb, wb, hipMemcpyHostToDevice, s));
+  if (tb) AE_HIP(hipMemcpyAsync(e->tpos.p, hp + cb + wb, tb, hipMemcpyHostToDevice, s));
   AE_HIP(hipEventRecord(e->upload_done, s));
   return ENC_OK;
 }
@@ -400,8 +426,8 @@ enum { ST_MEL = 0, ST_CONV1, ST_CONV2, ST_CONV3, ST_EMBED, ST_LAYER, ST_HEAD, ST
 // One pass over windows [p.win0, p.win0 + p.nwin): conv stack -> ... -> adapter, writing
 // rows [p.tok0, p.tok0 + p.ntok) of `out`.  Stops after `stop` (debug) when stop >= 0.
 template <typename T>
-encoder_status run_pass(encoder* e, const Pass& p, int64_t T_frames, void* out, hipStream_t s,
-                        int stop = -1, int stop_layer = -1) {
+encoder_status run_pass(encoder* e, const Pass& p, void* out, hipStream_t s, int stop = -1,
+                        int stop_layer = -1) {
   const encoder_cfg& c = e->cfg;
   const int C = c.conv_channels, d = c.d_model, W = c.window_tokens;
   PassGeom g;
@@ -421,9 +447,8 @@ encoder_status run_pass(encoder* e, const Pass& p, int64_t T_frames, void* out, 
   T* hid = (T*)e->hid.p;
   T* z = (T*)e->z.p;
 
-  LAUNCH(ENC_K_CONV1, launch_conv1<T>(g, (const float*)e->mel_raw.p, T_frames,
-                                      (const uint32_t*)e->max_key.p, e->conv1_w, e->conv1_b, C,
-                                      act1, s));
+  LAUNCH(ENC_K_CONV1, launch_conv1<T>(g, (const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
+                                      e->conv1_w, e->conv1_b, C, act1, s));
   if (stop == ST_CONV1) return ENC_OK;
   LAUNCH(ENC_K_CONV2, launch_conv_igemm<T>(g, 2, act1, (const T*)e->conv2_w, e->conv2_b, C, act2, s));
   if (stop == ST_CONV2) return ENC_OK;
@@ -479,12 +504,31 @@ encoder_status run_pass(encoder* e, const Pass& p, int64_t T_frames, void* out, 
   return ENC_OK;
 }
 
-// log-mel of [nclip, n_samples] into mel_raw + max keys
-encoder_status run_mel(encoder* e, const float* pcm, int64_t n_samples, int32_t nclip,
-                       hipStream_t s) {
+// log-mel of the clips (spans already uploaded to ctab) into mel_raw + max keys
+encoder_status run_mel(encoder* e, const float* pcm, int32_t nclip, int64_t t_max, hipStream_t s) {
   LAUNCH(ENC_K_OTHER, launch_clear_u32((uint32_t*)e->max_key.p, nclip, s));
-  LAUNCH(ENC_K_MEL, launch_log_mel(pcm, n_samples, nclip, e->mel, (float*)e->mel_raw.p,
-                                   (uint32_t*)e->max_key.p, s));
+  LAUNCH(ENC_K_MEL, launch_log_mel(pcm, (const ClipSpan*)e->ctab.p, nclip, t_max, e->mel,
+                                   (float*)e->mel_raw.p, (uint32_t*)e->max_key.p, s));
+  return ENC_OK;
+}
+
+// clip lengths of a ragged call -> vector (validated)
+encoder_status ragged_lengths(const encoder_cfg& c, const int64_t* lengths, int32_t n_clips,
+                              std::vector<int64_t>& lens) {
+  if (!lengths) return invalid("lengths is NULL");
+  if (n_clips < 1) return invalid("n_clips must be >= 1");
+  if (n_clips > 65535) return invalid("n_clips must be <= 65535");
+  lens.assign(lengths, lengths + n_clips);
+  int64_t frames = 0, tokens = 0;
+  for (int32_t i = 0; i < n_clips; ++i) {
+    if (lens[i] <= c.n_fft / 2)
+      return invalid("clip " + std::to_string(i) + ": length must exceed n_fft/2 = 200 (reflect padding)");
+    if (lens[i] / c.hop >= (int64_t(1) << 30)) return invalid("clip " + std::to_string(i) + " too long");
+    frames += lens[i] / c.hop;
+    tokens += frames_out(c, lens[i]);
+  }
+  if (frames >= (int64_t(1) << 31) || tokens >= (int64_t(1) << 31))
+    return invalid("too many frames for one call");
   return ENC_OK;
 }
 
@@ -501,33 +545,41 @@ encoder_status check_forward_args(encoder* e, const void* pcm, int64_t n_samples
   return ENC_OK;
 }
 
-encoder_status forward_impl(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+// lens: samples of each clip of the call (packed back to back in pcm)
+encoder_status forward_impl(encoder* e, const float* pcm, const std::vector<int64_t>& lens,
                             void* out, hipStream_t s, int64_t piece_windows, int stop = -1,
                             int stop_layer = -1, float* dst = nullptr, int64_t dst_elems = 0) {
   AE_HIP(hipSetDevice(e->device));
   const encoder_cfg& c = e->cfg;
+  const int32_t batch = (int32_t)lens.size();
+  std::vector<ClipSpan> clips;
+  clip_spans(c, lens, clips);
   std::vector<Win> wins;
-  plan_windows(c, n_samples, batch, wins);
+  plan_windows(c, lens, wins);
   const int64_t mt = max_tokens(c), mw = max_windows(c);
   std::vector<Pass> ps = split_passes(wins, mt, mw, [&](int64_t i) {
     return piece_windows > 0 && i % piece_windows == 0;
   });
   if (stop >= 0 && ps.size() > 1) return invalid("debug stages need a single pass");
-  const int64_t T = n_samples / c.hop;
-  int64_t ntok = 0;
+  int64_t ntok = 0, n_frames = 0, t_max = 0;
   for (auto& p : ps) ntok += p.ntok;
-  encoder_status st = size_workspace(e, batch, T, mt, mw, (int64_t)wins.size(), ntok);
+  for (int64_t n : lens) {
+    n_frames += n / c.hop;
+    t_max = std::max<int64_t>(t_max, n / c.hop);
+  }
+  const int64_t T = t_max;  // equal to every clip's frame count on the debug paths
+  encoder_status st = size_workspace(e, batch, n_frames, mt, mw, (int64_t)wins.size(), ntok);
   if (st) return st;
-  if ((st = upload_plan(e, wins, ps, s))) return st;
-  if ((st = run_mel(e, pcm, n_samples, batch, s))) return st;
+  if ((st = upload_plan(e, clips, wins, ps, s))) return st;
+  if ((st = run_mel(e, pcm, batch, t_max, s))) return st;
   if (stop == ST_MEL) {
     LAUNCH(ENC_K_OTHER, launch_mel_normalize((const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
                                              T, batch, dst, s));
     return ENC_OK;
   }
   for (const Pass& p : ps) {
-    if (e->bf16) st = run_pass<bf16_t>(e, p, T, out, s, stop, stop_layer);
-    else st = run_pass<float>(e, p, T, out, s, stop, stop_layer);
+    if (e->bf16) st = run_pass<bf16_t>(e, p, out, s, stop, stop_layer);
+    else st = run_pass<float>(e, p, out, s, stop, stop_layer);
     if (st) return st;
   }
   if (stop >= 0) {
@@ -559,7 +611,7 @@ void free_all(encoder* e) {
   if (!e) return;
   hipSetDevice(e->device);
   hipDeviceSynchronize();
-  encoder::Buf* bufs[] = {&e->mel_raw, &e->max_key, &e->wtab, &e->tpos, &e->act1, &e->act2,
+  encoder::Buf* bufs[] = {&e->mel_raw, &e->max_key, &e->ctab, &e->wtab, &e->tpos, &e->act1, &e->act2,
                           &e->tokA, &e->resid, &e->xn, &e->qkv, &e->attn, &e->hid, &e->hid2,
                           &e->z, &e->dbg};
   for (auto* b : bufs)
@@ -611,7 +663,27 @@ encoder_status encoder_plan_windows(const encoder_cfg* cfg, int64_t n_samples, i
   if (n_samples <= cfg->n_fft / 2) return invalid("n_samples must exceed n_fft/2 = 200");
   if (max_windows > 0 && !table) return invalid("table is NULL");
   std::vector<Win> w;
-  plan_windows(*cfg, n_samples, batch, w);
+  plan_windows(*cfg, std::vector<int64_t>((size_t)batch, n_samples), w);
+  *n_windows = (int32_t)w.size();
+  for (int32_t i = 0; i < std::min<int32_t>(max_windows, (int32_t)w.size()); ++i) {
+    int32_t* r = table + 7 * (int64_t)i;
+    r[0] = w[i].clip; r[1] = w[i].start; r[2] = w[i].L0; r[3] = w[i].L1;
+    r[4] = w[i].L2; r[5] = w[i].L3; r[6] = w[i].tok;
+  }
+  return ENC_OK;
+}
+
+encoder_status encoder_plan_windows_ragged(const encoder_cfg* cfg, const int64_t* lengths,
+                                           int32_t n_clips, int32_t* table, int32_t max_windows,
+                                           int32_t* n_windows) {
+  encoder_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!n_windows) return invalid("n_windows is NULL");
+  if (max_windows > 0 && !table) return invalid("table is NULL");
+  std::vector<int64_t> lens;
+  if ((st = ragged_lengths(*cfg, lengths, n_clips, lens))) return st;
+  std::vector<Win> w;
+  plan_windows(*cfg, lens, w);
   *n_windows = (int32_t)w.size();
   for (int32_t i = 0; i < std::min<int32_t>(max_windows, (int32_t)w.size()); ++i) {
     int32_t* r = table + 7 * (int64_t)i;
@@ -834,7 +906,8 @@ encoder_status encoder_forward(encoder* e, const float* pcm, int64_t n_samples, 
                                void* out, void* stream) {
   encoder_status st = check_forward_args(e, pcm, n_samples, batch, out);
   if (st) return st;
-  return forward_impl(e, pcm, n_samples, batch, out, (hipStream_t)stream, 0);
+  return forward_impl(e, pcm, std::vector<int64_t>((size_t)batch, n_samples), out,
+                      (hipStream_t)stream, 0);
 }
 
 encoder_status encoder_forward_long(encoder* e, const float* pcm, int64_t n_samples,
@@ -846,7 +919,18 @@ encoder_status encoder_forward_long(encoder* e, const float* pcm, int64_t n_samp
   if ((int64_t)pieces_per_pass * e->cfg.piece_tokens > max_tokens(e->cfg) ||
       (int64_t)pieces_per_pass * pw > max_windows(e->cfg))
     return invalid("pieces_per_pass * piece_tokens exceeds max_tokens_per_pass");
-  return forward_impl(e, pcm, n_samples, 1, out, (hipStream_t)stream, pw * pieces_per_pass);
+  return forward_impl(e, pcm, std::vector<int64_t>(1, n_samples), out, (hipStream_t)stream,
+                      pw * pieces_per_pass);
+}
+
+encoder_status encoder_forward_ragged(encoder* e, const float* pcm, const int64_t* lengths,
+                                      int32_t n_clips, void* out, void* stream) {
+  if (!e) return invalid("encoder handle is NULL");
+  if (!pcm || !out) return invalid("pcm and output pointers must be non-NULL");
+  std::vector<int64_t> lens;
+  encoder_status st = ragged_lengths(e->cfg, lengths, n_clips, lens);
+  if (st) return st;
+  return forward_impl(e, pcm, lens, out, (hipStream_t)stream, 0);
 }
 
 encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
@@ -856,9 +940,11 @@ encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, 
   AE_HIP(hipSetDevice(e->device));
   hipStream_t s = (hipStream_t)stream;
   const int64_t T = n_samples / e->cfg.hop;
-  if ((st = ensure(e, e->mel_raw, (int64_t)batch * T * 128 * 4))) return st;
-  if ((st = ensure(e, e->max_key, (int64_t)batch * 4))) return st;
-  if ((st = run_mel(e, pcm, n_samples, batch, s))) return st;
+  if ((st = size_mel(e, batch, (int64_t)batch * T))) return st;
+  std::vector<ClipSpan> clips;
+  clip_spans(e->cfg, std::vector<int64_t>((size_t)batch, n_samples), clips);
+  if ((st = upload_plan(e, clips, {}, {}, s))) return st;
+  if ((st = run_mel(e, pcm, batch, T, s))) return st;
   LAUNCH(ENC_K_OTHER, launch_mel_normalize((const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
                                            T, batch, mel, s));
   return ENC_OK;
@@ -876,8 +962,8 @@ encoder_status encoder_debug_stage(encoder* e, const float* pcm, int64_t n_sampl
   const int64_t F = frames_out(e->cfg, n_samples) * batch;
   if (F > max_tokens(e->cfg)) return invalid("debug stages need a single pass");
   if ((st = ensure(e, e->dbg, F * e->cfg.d_out * (int64_t)e->esz))) return st;
-  return forward_impl(e, pcm, n_samples, batch, e->dbg.p, (hipStream_t)stream, 0, stage, layer,
-                      dst, dst_elems);
+  return forward_impl(e, pcm, std::vector<int64_t>((size_t)batch, n_samples), e->dbg.p,
+                      (hipStream_t)stream, 0, stage, layer, dst, dst_elems);
 }
 
 encoder_status encoder_timing_enable(encoder* e, int32_t enable) {

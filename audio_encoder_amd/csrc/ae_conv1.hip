@@ -47,7 +47,6 @@ template <> struct Pack8<float> {
 template <typename T>
 __global__ __launch_bounds__(256) void conv1_kernel(const Win* __restrict__ wins, int32_t W,
                                                     const float* __restrict__ mel,
-                                                    int64_t T_frames,
                                                     const uint32_t* __restrict__ max_key,
                                                     const float* __restrict__ wt,
                                                     const float* __restrict__ bias, int32_t C,
@@ -65,7 +64,7 @@ __global__ __launch_bounds__(256) void conv1_kernel(const Win* __restrict__ wins
   if (t1_0 >= wn.L1) return;
 
   const float lo = key_to_float_c(max_key[wn.clip]) - 8.0f;
-  const float* mrow = mel + ((int64_t)wn.clip * T_frames + wn.start) * 128;
+  const float* mrow = mel + (int64_t)wn.mel_row * 128;
   for (int i = tid; i < (2 * RT + 1) * 130; i += blockDim.x) {
     const int r = i / 130, c = i - r * 130;
     const int t = 2 * t1_0 - 1 + r, f = c - 1;
@@ -110,9 +109,8 @@ __global__ __launch_bounds__(256) void conv1_kernel(const Win* __restrict__ wins
 }  // namespace
 
 template <typename T>
-hipError_t launch_conv1(const PassGeom& g, const float* mel, int64_t T_frames,
-                        const uint32_t* max_key, const float* w, const float* b, int32_t C,
-                        T* act1, hipStream_t s) {
+hipError_t launch_conv1(const PassGeom& g, const float* mel, const uint32_t* max_key,
+                        const float* w, const float* b, int32_t C, T* act1, hipStream_t s) {
   const int CG = C / 8;
   const int FQ = std::max(1, std::min(64, 256 / CG));
   const int threads = CG * FQ;
@@ -121,13 +119,13 @@ hipError_t launch_conv1(const PassGeom& g, const float* mel, int64_t T_frames,
   const int64_t blocks = (int64_t)g.n_win * nrb;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(conv1_kernel<T>, dim3((unsigned)blocks), dim3(threads), 0, s, g.wins, g.W,
-                     mel, T_frames, max_key, w, b, C, act1);
+                     mel, max_key, w, b, C, act1);
   return hipGetLastError();
 }
 
-template hipError_t launch_conv1<bf16_t>(const PassGeom&, const float*, int64_t, const uint32_t*,
+template hipError_t launch_conv1<bf16_t>(const PassGeom&, const float*, const uint32_t*,
                                          const float*, const float*, int32_t, bf16_t*, hipStream_t);
-template hipError_t launch_conv1<float>(const PassGeom&, const float*, int64_t, const uint32_t*,
+template hipError_t launch_conv1<float>(const PassGeom&, const float*, const uint32_t*,
                                         const float*, const float*, int32_t, float*, hipStream_t);
 
 }  // namespace ae

@@ -747,18 +747,37 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
   return hipGetLastError();
 }
 
-// Tile choice (measured on MI355X with the shapes of the tower, M = 6000):
-//  - N = 1280 or 3840 (o-proj, FFN2, conv_out, proj1, QKV): 128x128 tiles, BK 64, two workgroups
-//    per CU; a wider tile leaves CUs idle in the last round.
-//  - N = 5120 (FFN1): 256x128 tiles, 8 waves (two per SIMD), BK 32.
-//  - K >= 2048 (adapter gate/up and down, head proj2): 256x256 tiles, 8 waves, BK 32, four
-//    stages with the refill DMAs spread over the MFMAs.
+// Tile choice (measured on MI355X with the shapes of the tower):
+//  - N = 1280 or 3840 (o-proj, FFN2, conv_out, proj1, QKV) and other N < 2048: 128x128 tiles,
+//    BK 64, two workgroups per CU, as long as the tiles fit in one round of two per CU (M up to
+//    ~6500 at N = 1280).  Beyond that a second, nearly empty round would cost ~30%, and the
+//    larger tiles below are faster.
+//  - N = 5120 (FFN1) and the rest with K < 2048: 256x128 tiles, 8 waves (two per SIMD), BK 32.
+//  - K >= 2048 (adapter gate/up and down, FFN2 once M is past one round): 256x256 tiles,
+//    8 waves, BK 32, four stages with the refill DMAs spread over the MFMAs.
 using TileWide = Tile<256, 128, 4, 2, 32, 1>;
 using TileNarrow = Tile<128, 128, 2, 2, 64, 2>;
 using TileLarge = Tile<256, 256, 2, 4, 32, 1>;
 enum class LinKind { Narrow, Wide, Large };
-inline LinKind lin_kind(int64_t /*M*/, int64_t N, int64_t K) {
-  if (N == 1280 || N == 3840 || N < 2048) return LinKind::Narrow;
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+inline LinKind lin_kind(int64_t M, int64_t N, int64_t K) {
+  if (N == 1280 || N == 3840 || N < 2048) {
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles <= 2 * (int64_t)cu_count()) return LinKind::Narrow;
+  }
   if (K >= 2048) return LinKind::Large;
   return LinKind::Wide;
 }

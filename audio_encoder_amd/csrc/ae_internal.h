@@ -60,11 +60,19 @@ __device__ inline float silu(float x) { return x / (1.0f + expf(-x)); }
 // window plan (one entry per attention window; all fields int32)
 // ------------------------------------------------------------------------------------------
 struct Win {
-  int32_t clip;   // clip (row of the log-mel buffer) the window belongs to
+  int32_t clip;   // clip the window belongs to (its log-mel maximum)
   int32_t start;  // first mel frame within the clip
   int32_t L0, L1, L2, L3;  // valid lengths: frames, after conv1, conv2, conv3 (= tokens)
   int32_t tok;    // first token of the window within its pass
-  int32_t pad;
+  int32_t mel_row;  // first frame of the window in the packed log-mel buffer (all clips)
+};
+
+// One clip of a call: its samples in the packed PCM buffer and its frames in the packed
+// log-mel buffer (clips of one call may differ in length).
+struct ClipSpan {
+  int64_t smp_off;    // first sample
+  int64_t n;          // samples
+  int64_t frame_off;  // first log-mel frame (row)
 };
 
 // Geometry of one pass over a group of windows.
@@ -99,18 +107,19 @@ struct MelTables {
   const float* fb_w;        // [128][16] weights
 };
 
-// raw log10 mel of [nclip, n_samples] pcm -> mel [nclip, T, 128]; per-clip max into
-// max_key[clip] (ordered-uint encoding; must be cleared by launch_clear_u32 first)
-hipError_t launch_log_mel(const float* pcm, int64_t n_samples, int32_t nclip, const MelTables& t,
-                          float* mel, uint32_t* max_key, hipStream_t s);
+// raw log10 mel of the clips in `clips` (device, nclip spans over the packed pcm) -> packed
+// mel rows [frame_off + t][128]; per-clip max into max_key[clip] (ordered-uint encoding; must
+// be cleared by launch_clear_u32 first).  t_max: frames of the longest clip.
+hipError_t launch_log_mel(const float* pcm, const ClipSpan* clips, int32_t nclip, int64_t t_max,
+                          const MelTables& t, float* mel, uint32_t* max_key, hipStream_t s);
 hipError_t launch_clear_u32(uint32_t* p, int64_t n, hipStream_t s);
 // normalised mel from raw + max keys (in place or out of place)
 hipError_t launch_mel_normalize(const float* raw, const uint32_t* max_key, int64_t T,
                                 int32_t nclip, float* out, hipStream_t s);
 
-// conv1: raw mel + max -> act1 [n_win][4W][64][C]
+// conv1: raw packed mel (window rows at Win::mel_row) + max -> act1 [n_win][4W][64][C]
 template <typename T>
-hipError_t launch_conv1(const PassGeom& g, const float* mel, int64_t T_frames, const uint32_t* max_key,
+hipError_t launch_conv1(const PassGeom& g, const float* mel, const uint32_t* max_key,
                         const float* w, const float* b, int32_t C, T* act1, hipStream_t s);
 
 // GEMM epilogue kinds

@@ -4,6 +4,9 @@
 // n_fft 400, hop 160, WhisperFeatureExtractor-compatible; "Non-obvious gotchas" item 2: the
 // trailing STFT frame is dropped so a clip of N samples has N / 160 frames).
 //
+// Clips of one call may differ in length: clip c's samples start at clips[c].smp_off of the
+// packed PCM and its frames at row clips[c].frame_off of the packed log-mel.
+//
 // One workgroup computes FB consecutive frames of one clip:
 //   1. the FB*160 + 240 samples those frames touch are read once, coalesced, into LDS
 //      (reflection at the clip edges is an index map, no padded copy in HBM);
@@ -34,8 +37,9 @@ __device__ inline uint32_t float_to_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(256) void log_mel_kernel(const float* __restrict__ pcm, int64_t N,
-                                                      int64_t T, const float* __restrict__ twid,
+__global__ __launch_bounds__(256) void log_mel_kernel(const float* __restrict__ pcm,
+                                                      const ClipSpan* __restrict__ clips,
+                                                      const float* __restrict__ twid,
                                                       const float* __restrict__ hann,
                                                       const int32_t* __restrict__ fb_start,
                                                       const int32_t* __restrict__ fb_len,
@@ -50,8 +54,11 @@ __global__ __launch_bounds__(256) void log_mel_kernel(const float* __restrict__ 
 
   const int tid = threadIdx.x;
   const int clip = blockIdx.y;
+  const ClipSpan cs = clips[clip];
+  const int64_t N = cs.n, T = N / HOP;
   const int64_t t0 = (int64_t)blockIdx.x * FB;
-  const float* x = pcm + (int64_t)clip * N;
+  if (t0 >= T) return;  // grid spans the longest clip
+  const float* x = pcm + cs.smp_off;
 
   // 1. samples [HOP*t0 - 200, HOP*t0 - 200 + NSMP) with reflection about both clip ends
   const int64_t g0 = HOP * t0 - NFFT / 2;
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(256) void log_mel_kernel(const float* __restrict__ 
     float acc = 0.0f;
     for (int j = 0; j < nt; ++j) acc = fmaf(fb_w[m * MAXTAP + j], P[f * NB + s0 + j], acc);
     const float l = log10f(fmaxf(acc, 1e-10f));
-    mel[((int64_t)clip * T + t) * NM + m] = l;
+    mel[(cs.frame_off + t) * NM + m] = l;
     lmax = fmaxf(lmax, l);
   }
   for (int o = 32; o > 0; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
@@ -171,11 +178,12 @@ __global__ void mel_normalize_kernel(const float* __restrict__ raw, const uint32
 
 }  // namespace
 
-hipError_t launch_log_mel(const float* pcm, int64_t n_samples, int32_t nclip, const MelTables& t,
-                          float* mel, uint32_t* max_key, hipStream_t s) {
-  const int64_t T = n_samples / HOP;
-  dim3 grid((unsigned)((T + FB - 1) / FB), (unsigned)nclip);
-  hipLaunchKernelGGL(log_mel_kernel, grid, dim3(256), 0, s, pcm, n_samples, T, t.twiddle, t.window,
+hipError_t launch_log_mel(const float* pcm, const ClipSpan* clips, int32_t nclip, int64_t t_max,
+                          const MelTables& t, float* mel, uint32_t* max_key, hipStream_t s) {
+  if (nclip < 1 || t_max < 1) return hipSuccess;
+  if (nclip > 65535 || (t_max + FB - 1) / FB >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((t_max + FB - 1) / FB), (unsigned)nclip);
+  hipLaunchKernelGGL(log_mel_kernel, grid, dim3(256), 0, s, pcm, clips, t.twiddle, t.window,
                      t.fb_start, t.fb_len, t.fb_w, mel, max_key);
   return hipGetLastError();
 }

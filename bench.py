@@ -29,6 +29,8 @@ WORKLOADS = {
     "c1": "1 x 30 s clip (pink noise + harmonic bursts, peak 0.5), full-size tower, bf16",
     "c3": "512 s stream as 8 x 64 s pieces in one pass, full-size tower, bf16",
     "c4": "60 min recording as 57 sequential 64 s pieces, full-size tower, bf16",
+    "ragged": "16 clips of 5-60 s (lengths seeded, mixed content, peak 0.5) in one ragged call, "
+              "full-size tower, bf16",
 }
 
 
@@ -36,11 +38,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def work_model(cfg: dict, n_samples: int, batch: int) -> dict:
+def work_model(cfg: dict, lengths: list) -> dict:
     """Algorithmic work per step for each kernel role: FLOPs (2 per MAC over valid positions and
     in-window attention only) or HBM bytes for the bandwidth-bound roles."""
     from audio_encoder_amd import binding as B
-    tab = B.encoder_plan_windows(cfg, n_samples, batch)
+    tab = B.encoder_plan_windows_ragged(cfg, lengths)
     C, d, F, O, A = (cfg[k] for k in ("conv_channels", "d_model", "d_ffn", "d_out", "d_adapter"))
     Lh = cfg["n_layers"]
     L1, L2, L3 = (tab[:, i].astype(float) for i in (3, 4, 5))
@@ -62,16 +64,29 @@ def work_model(cfg: dict, n_samples: int, batch: int) -> dict:
         "down": 2 * ntok * O * A,
     }
     flops = float(sum(w.values()))
-    T = n_samples // 160
     bytes_ = {
-        "mel": batch * (4.0 * n_samples + 512.0 * T),
+        "mel": float(sum(4.0 * n + 512.0 * (n // 160) for n in lengths)),
         "layernorm": (2 * Lh + 1) * ntok * d * (4 + es),
     }
     return {"flops": w, "total_flops": flops, "bytes": bytes_, "ntok": int(ntok)}
 
 
+RAGGED_SECONDS = (5.0, 60.0)
+
+
+def ragged_lengths(n_clips: int = 16, seed: int = 500) -> list:
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    return [int(round(16000 * rng.uniform(*RAGGED_SECONDS))) for _ in range(n_clips)]
+
+
 def make_input(workload: str):
     from audio_encoder_amd import synth as S
+    if workload == "ragged":
+        import numpy as np
+        lens = ragged_lengths()
+        pcm = np.concatenate([S.mixed_clip(501 + i, n) for i, n in enumerate(lens)])
+        return pcm, sum(lens) / 16000.0
     if workload == "c2":
         return S.mixed_batch(range(101, 117)), 480.0
     if workload == "c1":
@@ -161,15 +176,25 @@ def main():
     pcm_np, audio_s = make_input(args.workload)
     enc = B.Encoder(weights, cfg)
     pcm = torch.from_numpy(pcm_np).cuda()
-    n_samples = pcm.shape[1]
     long_mode = args.workload in ("c3", "c4")
+    ragged = args.workload == "ragged"
     ppp = 8 if args.workload == "c3" else 1
-    wm = work_model(cfg, n_samples, pcm.shape[0])
-    F = enc.output_frames(n_samples)
-    out = torch.empty((pcm.shape[0], F, cfg["d_out"]), dtype=torch.bfloat16, device="cuda")
+    if ragged:
+        lengths = ragged_lengths()
+        n_clips, n_samples = len(lengths), max(lengths)
+        out = torch.empty((sum(enc.output_frames(n) for n in lengths), cfg["d_out"]),
+                          dtype=torch.bfloat16, device="cuda")
+    else:
+        n_clips, n_samples = pcm.shape[0], pcm.shape[1]
+        lengths = [n_samples] * n_clips
+        out = torch.empty((n_clips, enc.output_frames(n_samples), cfg["d_out"]),
+                          dtype=torch.bfloat16, device="cuda")
+    wm = work_model(cfg, lengths)
 
     def step():
-        if long_mode:
+        if ragged:
+            enc.forward_ragged(pcm, lengths, out=out)
+        elif long_mode:
             enc.forward_long(pcm[0], pieces_per_pass=ppp, out=out[0])
         else:
             enc.forward(pcm, out=out)
@@ -218,7 +243,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        cpu = cpu_baseline(pcm_np, weights, cfg)
+        clips = ([pcm_np[o:o + n] for o, n in zip(np.cumsum([0] + lengths[:-1]), lengths)]
+                 if ragged else list(pcm_np))
+        cpu = cpu_baseline(clips, weights, cfg)
         log(f"oracle: {cpu['value']:.2f} audio-s/s on {cpu['cores']} cores")
 
     wbytes, ws = enc.memory_stats()
@@ -235,9 +262,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.workload], "clips": int(pcm.shape[0]),
-                   "samples_per_clip": int(n_samples), "tokens_per_step": wm["ntok"],
-                   "audio_seconds_per_step": audio_s},
+        "config": {"workload": WORKLOADS[args.workload], "clips": int(n_clips),
+                   "samples_per_clip": int(n_samples) if not ragged else lengths,
+                   "tokens_per_step": wm["ntok"], "audio_seconds_per_step": audio_s},
         "tflops": round(tflops, 2),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roof,

@@ -110,6 +110,13 @@ ENC_API encoder_status encoder_output_frames(const encoder_cfg* cfg, int64_t n_s
 ENC_API encoder_status encoder_plan_windows(const encoder_cfg* cfg, int64_t n_samples, int32_t batch,
                                     int32_t* table, int32_t max_windows, int32_t* n_windows);
 
+/* The window plan of a ragged call (see encoder_forward_ragged): the same 7 values per window,
+ * clips in order, each clip's frames counted from its own start; the token column runs over
+ * the whole call (row of the [sum F_c, d_out] output). */
+ENC_API encoder_status encoder_plan_windows_ragged(const encoder_cfg* cfg, const int64_t* lengths,
+                                           int32_t n_clips, int32_t* table, int32_t max_windows,
+                                           int32_t* n_windows);
+
 /* ---- handle lifecycle -------------------------------------------------------------------- */
 
 /* Packs the host float32 weight blob (n_floats values, order above) for the current HIP device:
@@ -140,6 +147,17 @@ ENC_API encoder_status encoder_forward(encoder* e, const float* pcm, int64_t n_s
  * summation order. */
 ENC_API encoder_status encoder_forward_long(encoder* e, const float* pcm, int64_t n_samples,
                                     int32_t pieces_per_pass, void* out, void* stream);
+
+/* Ragged batch: several clips of different lengths in one call ("SILVERTHRONE/Ossicle-4B"
+ * card: the audio-input line of the model summary, and "Many clips in one question").
+ * pcm: device float32, the clips back to back (clip c at samples [off_c, off_c + lengths[c]),
+ * off_c = sum of the earlier lengths).  lengths: host int64 [n_clips], each > n_fft/2;
+ * 1 <= n_clips <= 65535.  out: device [sum_c F_c, d_out] with F_c = encoder_output_frames of
+ * lengths[c], clips in order, bf16 for ENC_BF16 and float32 for ENC_F32.  Each clip is
+ * normalised by its own log-mel maximum and encoded window by window, so its rows equal those
+ * of encoder_forward on that clip alone.  `lengths` is read before the call returns. */
+ENC_API encoder_status encoder_forward_ragged(encoder* e, const float* pcm, const int64_t* lengths,
+                                      int32_t n_clips, void* out, void* stream);
 
 /* Normalised log-mel only: mel device float32 [batch, n_samples/160, 128]. */
 ENC_API encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,

@@ -442,6 +442,25 @@ def encode_batch(pcm: np.ndarray, Wt: dict, cfg: dict) -> np.ndarray:
     return np.stack([encode(c, Wt, cfg) for c in np.atleast_2d(pcm)])
 
 
+def encode_ragged(clips: list, Wt: dict, cfg: dict) -> np.ndarray:
+    """Several clips of different lengths in one call (card O: the audio-input line of the
+    model summary, and "Many clips in one question"): each clip is its own recording with its
+    own log-mel maximum, encoded by ``encode``; the outputs are concatenated in clip order."""
+    return np.concatenate([encode(np.asarray(c), Wt, cfg) for c in clips], axis=0)
+
+
+def ragged_window_plan(lengths: list, window_tokens: int) -> list[dict]:
+    """Window plan of a ragged call: each clip's ``window_plan`` in clip order, tagged with the
+    clip index, with the first output token counted over the whole call."""
+    out, tok0 = [], 0
+    for c, n in enumerate(lengths):
+        plan = window_plan(n_mel_frames(int(n)), window_tokens)
+        for w in plan:
+            out.append(dict(w, clip=c, tok=w["tok"] + tok0))
+        tok0 += sum(w["L3"] for w in plan)
+    return out
+
+
 def encode_long(pcm: np.ndarray, Wt: dict, cfg: dict) -> np.ndarray:
     """Long-audio mode: the log-mel of the whole recording (one maximum for all of it), cut at
     64 s piece boundaries (800 tokens = 6400 frames); each piece is encoded on its own and

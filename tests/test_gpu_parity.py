@@ -66,11 +66,14 @@ def test_op_layernorm(D, dtype):
 
 
 # (M, N, K): small and ragged shapes, and one of each tile path (128x128: N = 1280 / 3840 /
-# N < 2048; 256x128: N >= 2048 with K < 2048; 256x256 four-stage: N >= 2048 with K >= 2048, here
-# with K not a multiple of the 128-deep stage group and M, N not multiples of the tile)
+# N < 2048 while the tiles fit two per CU; 256x128: K < 2048 otherwise; 256x256 four-stage:
+# K >= 2048 otherwise, here with K not a multiple of the 128-deep stage group and M, N not
+# multiples of the tile)
 LINEAR_SHAPES = [(1, 64, 64), (130, 200, 72), (300, 3840, 1280), (257, 1280, 5120),
                  (129, 1024, 4320), (64, 128, 8), (333, 2560, 1032), (301, 2112, 2216),
-                 (77, 4096, 2048)]
+                 (77, 4096, 2048),
+                 # N = 1280 with more 128x128 tiles than two per CU: 256x128 / 256x256 paths
+                 (7000, 1280, 1024), (6600, 1280, 2056)]
 
 
 @pytest.mark.parametrize("M,N,K", LINEAR_SHAPES)
@@ -270,6 +273,50 @@ def test_tiny_long_mode_equals_whole_clip(tiny):
     assert cos >= 0.99999 and rel <= 1e-3
 
 
+def ragged_clips(seed0, lengths):
+    return [S.mixed_clip(seed0 + i, n) if n > 1000 else S.pink_plus_bursts(seed=seed0 + i, n=n)
+            for i, n in enumerate(lengths)]
+
+
+def test_tiny_ragged_matches_oracle_and_single_clips(tiny):
+    enc, Wt = tiny
+    lengths = [64000, 30001, 201, 100000, 12345]
+    clips = ragged_clips(300, lengths)
+    got = enc.forward_ragged(to_dev(np.concatenate(clips)), lengths)
+    F = [O.n_output_frames(n, 25) for n in lengths]
+    assert got.shape == (sum(F), 512)
+    # every clip's rows equal the single-clip forward exactly: a row's arithmetic does not depend
+    # on which other windows share its pass
+    o = 0
+    for x, f in zip(clips, F):
+        assert torch.equal(got[o:o + f], enc.forward(to_dev(x[None]))[0])
+        o += f
+    cos, rel = frame_metrics(got.cpu().numpy(), O.encode_ragged(clips, Wt, O.TINY))
+    assert cos >= 0.99999 and rel <= 1e-3, (cos, rel)
+
+
+def test_tiny_ragged_in_several_passes(tiny):
+    enc, _ = tiny
+    lengths = [64000, 201, 53920, 100000]
+    pcm = to_dev(np.concatenate(ragged_clips(310, lengths)))
+    one_pass = enc.forward_ragged(pcm, lengths)
+    small = B.Encoder(S.make_weights(B.TINY, seed=0), dict(B.TINY, max_tokens_per_pass=50))
+    torch.cuda.synchronize()
+    assert torch.equal(small.forward_ragged(pcm, lengths), one_pass)
+    small.close()
+
+
+def test_ragged_rejects_bad_calls(tiny):
+    enc, _ = tiny
+    pcm = to_dev(np.zeros(64000, dtype=np.float32))
+    for lengths in ([], [64000 - 200, 200], [64000, -1]):
+        with pytest.raises(B.EncoderError) as ei:
+            enc.forward_ragged(pcm[:sum(lengths)], lengths)
+        assert ei.value.status == B.ENC_E_INVALID_ARG
+    with pytest.raises(ValueError):  # lengths must cover the buffer
+        enc.forward_ragged(pcm, [32000])
+
+
 def test_tiny_deterministic(tiny):
     enc, _ = tiny
     pcm = to_dev(S.mixed_batch([1, 2], 64000))
@@ -369,6 +416,24 @@ def test_full_c3_pieces_equal_whole(full):
         res, _ = oracle_windows(x, Wt, O.FULL, [wi])
         tok, yref, _ = res[0]
         check_bf16(got[tok:tok + yref.shape[0]], yref, f"stream window {wi}")
+
+
+def test_full_ragged_equals_single_clips(full):
+    enc, Wt = full
+    lengths = [480000, 117000, 1_030_000, 201]
+    clips = ragged_clips(400, lengths)
+    got = enc.forward_ragged(to_dev(np.concatenate(clips)), lengths)
+    F = [O.n_output_frames(n, 100) for n in lengths]
+    assert got.shape == (sum(F), 2048)
+    o = 0
+    for x, f in zip(clips, F):
+        assert torch.equal(got[o:o + f], enc.forward(to_dev(x[None]))[0])
+        o += f
+    # one window of the 7.3 s clip against the oracle
+    g = got.float().cpu().numpy()
+    res, _ = oracle_windows(clips[1], Wt, O.FULL, [0])
+    tok, yref, _ = res[0]
+    check_bf16(g[F[0] + tok:F[0] + tok + yref.shape[0]], yref, "ragged clip 1 window 0")
 
 
 def test_full_c4_hour_stream(full):

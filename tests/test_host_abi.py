@@ -86,6 +86,34 @@ def test_window_plan_is_bit_exact_with_oracle(cfg, W, n, batch):
     assert np.array_equal(got, np.array(rows, dtype=np.int32).reshape(-1, 7))
 
 
+RAGGED_LENGTHS = [[480000, 64000, 1_030_000], [201, 201], [129760, 201, 53920, 8192000],
+                  [480000] * 4, [1000, 127999, 128001, 16000]]
+
+
+@pytest.mark.parametrize("cfg,W", [(B.FULL, 100), (B.TINY, 25)])
+@pytest.mark.parametrize("lengths", RAGGED_LENGTHS)
+def test_ragged_window_plan_is_bit_exact_with_oracle(cfg, W, lengths):
+    got = B.encoder_plan_windows_ragged(cfg, lengths)
+    rows = [[w["clip"], w["start"], w["L0"], w["L1"], w["L2"], w["L3"], w["tok"]]
+            for w in O.ragged_window_plan(lengths, W)]
+    assert np.array_equal(got, np.array(rows, dtype=np.int32).reshape(-1, 7))
+    # tokens of the call = the sum of the clips' output frames
+    assert got[:, 5].sum() == sum(O.n_output_frames(n, W) for n in lengths)
+
+
+def test_ragged_plan_of_equal_clips_is_the_batch_plan():
+    a = B.encoder_plan_windows_ragged(B.FULL, [480000] * 5)
+    b = B.encoder_plan_windows(B.FULL, 480000, 5)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("lengths", [[], [480000, 200], [200], [480000, -5]])
+def test_ragged_plan_rejects_bad_lengths(lengths):
+    with pytest.raises(B.EncoderError) as ei:
+        B.encoder_plan_windows_ragged(B.FULL, lengths)
+    assert ei.value.status == B.ENC_E_INVALID_ARG
+
+
 def test_plan_of_hour_stream_has_45000_tokens():
     tab = B.encoder_plan_windows(B.FULL, 57_600_000, 1)
     assert len(tab) == 450 and tab[:, 5].sum() == 45000

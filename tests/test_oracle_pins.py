@@ -492,3 +492,48 @@ def test_windows_are_independent(tiny_weights):
     md = np.concatenate([mel[:400], mel[600:]])
     yd = O.encode_mel(md, tiny_weights, O.TINY)
     np.testing.assert_allclose(yd, np.concatenate([y[:50], y[75:]]), rtol=1e-12, atol=1e-15)
+
+
+# ---- ragged multi-clip calls (card O: several clips per question) ------------------------------
+def test_ragged_plan_of_one_clip_is_the_clip_plan():
+    for n in (201, 53920, 160000):
+        got = O.ragged_window_plan([n], 25)
+        ref = O.window_plan(O.n_mel_frames(n), 25)
+        assert [dict(w, clip=0) for w in ref] == got
+
+
+def test_ragged_plan_counts_tokens_over_the_call():
+    lens = [53920, 201, 160000]
+    plan = O.ragged_window_plan(lens, 25)
+    toks = [w["tok"] for w in plan]
+    assert toks[0] == 0 and all(b > a for a, b in zip(toks, toks[1:]))
+    assert sum(w["L3"] for w in plan) == sum(O.n_output_frames(n, 25) for n in lens)
+    # the clips' windows come in clip order and restart their frame count at 0
+    assert [w["clip"] for w in plan] == sorted(w["clip"] for w in plan)
+    assert [w["start"] for w in plan if w["clip"] == 2][0] == 0
+
+
+def test_ragged_clips_are_normalised_by_their_own_maximum(tiny_weights):
+    a = S.pink_plus_bursts(seed=21, n=53920)
+    b = S.three_sines(seed=22)[:30001]
+    y1 = O.encode_ragged([a, b], tiny_weights, O.TINY)
+    y2 = O.encode_ragged([a, 8.0 * b], tiny_weights, O.TINY)
+    Fa = O.n_output_frames(a.size, 25)
+    assert y1.shape == (Fa + O.n_output_frames(b.size, 25), 512)
+    # a louder second clip leaves the first clip's rows untouched (no shared maximum) ...
+    assert np.array_equal(y1[:Fa], y2[:Fa])
+    # ... and changes its own rows (the normalisation offset moves with its maximum)
+    assert not np.allclose(y1[Fa:], y2[Fa:])
+
+
+def test_ragged_call_is_equivariant_under_clip_order(tiny_weights):
+    a = S.pink_plus_bursts(seed=23, n=40000)
+    b = S.pink_plus_bursts(seed=24, n=201)
+    c = S.three_sines(seed=25)[:21111]
+    F = [O.n_output_frames(x.size, 25) for x in (a, b, c)]
+    y = O.encode_ragged([a, b, c], tiny_weights, O.TINY)
+    yp = O.encode_ragged([c, a, b], tiny_weights, O.TINY)
+    ya, yb, yc = y[:F[0]], y[F[0]:F[0] + F[1]], y[F[0] + F[1]:]
+    assert np.array_equal(yp, np.concatenate([yc, ya, yb]))
+    # the shortest clip (201 samples: one frame) yields one output frame
+    assert F[1] == 1 and yb.shape == (1, 512)
