@@ -79,6 +79,10 @@ _SIGS = {
     "encoder_forward": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
     "encoder_forward_long": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
     "encoder_forward_ragged": [c_void_p, c_void_p, POINTER(c_int64), c_int32, c_void_p, c_void_p],
+    "encoder_forward_taps": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, POINTER(c_int32),
+                             c_int32, c_void_p, c_void_p],
+    "encoder_splice": [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_int64, c_int32, c_void_p,
+                       c_void_p],
     "encoder_log_mel": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
     "encoder_debug_stage": [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p,
                             c_int64, c_void_p],
@@ -244,6 +248,23 @@ class Encoder:
                                             L.size, _ptr(out), _stream()))
         return out
 
+    def forward_taps(self, pcm, layers, out=None):
+        """Whole-clip forward that also returns the residual stream after each layer in
+        `layers`: (out [batch, F, d_out], taps float32 [len(layers), batch*F, d_model])."""
+        import torch
+        assert pcm.is_cuda and pcm.dtype == torch.float32 and pcm.is_contiguous()
+        B_, N = pcm.shape
+        F = self.output_frames(N)
+        if out is None:
+            out = torch.empty((B_, F, self.cfg["d_out"]), dtype=self.out_dtype, device=pcm.device)
+        L = np.ascontiguousarray(np.asarray(layers, dtype=np.int32).ravel())
+        taps = torch.empty((L.size, B_ * F, self.cfg["d_model"]), dtype=torch.float32,
+                           device=pcm.device)
+        _check(lib().encoder_forward_taps(self._h, _ptr(pcm), N, B_, _ptr(out),
+                                          L.ctypes.data_as(POINTER(c_int32)), L.size, _ptr(taps),
+                                          _stream()))
+        return out, taps
+
     def log_mel(self, pcm):
         import torch
         B, N = pcm.shape
@@ -285,6 +306,18 @@ class Encoder:
 
 
 # ---- single-kernel entry points ------------------------------------------------------------------
+def splice(frames, positions, table, n_skipped=None):
+    """table[positions[i]] = frames[i] on the GPU (audio injection); positions int64 CUDA tensor.
+    Out-of-range positions are skipped and counted into n_skipped (int32 CUDA tensor [1])."""
+    import torch
+    assert frames.dtype == table.dtype and frames.shape[-1] == table.shape[-1]
+    assert positions.dtype == torch.int64 and positions.numel() == frames.shape[0]
+    _check(lib().encoder_splice(_ptr(frames), frames.shape[0], frames.shape[-1], _ptr(positions),
+                                _ptr(table), table.shape[0], _dtype_code(table.dtype),
+                                _ptr(n_skipped), _stream()))
+    return table
+
+
 def op_linear(A, W, bias, C, epi: int):
     """C = epi(A W^T) (see encoder_op_linear)."""
     M, K = A.shape

@@ -423,11 +423,20 @@ encoder_status launch_linear_t(encoder* e, int kid, const void* A, int64_t lda, 
 // stage ids of encoder_debug_stage
 enum { ST_MEL = 0, ST_CONV1, ST_CONV2, ST_CONV3, ST_EMBED, ST_LAYER, ST_HEAD, ST_OUT };
 
+// Residual-stream exports: after layer layers[t], rows [tok0, tok0 + ntok) of the pass go to
+// dst[t][tok0 ..][d_model] (float32), ntok_total rows per tap.
+struct TapReq {
+  const int32_t* layers = nullptr;
+  int32_t n = 0;
+  float* dst = nullptr;
+  int64_t ntok_total = 0;
+};
+
 // One pass over windows [p.win0, p.win0 + p.nwin): conv stack -> ... -> adapter, writing
 // rows [p.tok0, p.tok0 + p.ntok) of `out`.  Stops after `stop` (debug) when stop >= 0.
 template <typename T>
 encoder_status run_pass(encoder* e, const Pass& p, void* out, hipStream_t s, int stop = -1,
-                        int stop_layer = -1) {
+                        int stop_layer = -1, const TapReq* taps = nullptr) {
   const encoder_cfg& c = e->cfg;
   const int C = c.conv_channels, d = c.d_model, W = c.window_tokens;
   PassGeom g;
@@ -476,6 +485,11 @@ encoder_status run_pass(encoder* e, const Pass& p, void* out, hipStream_t s, int
                                  EPI_RESADD, s)))
       return st;
     if (stop == ST_LAYER && stop_layer == l) return ENC_OK;
+    if (taps)
+      for (int32_t t = 0; t < taps->n; ++t)
+        if (taps->layers[t] == l)
+          AE_HIP(hipMemcpyAsync(taps->dst + (t * taps->ntok_total + p.tok0) * d, resid,
+                                M * d * sizeof(float), hipMemcpyDeviceToDevice, s));
   }
   LAUNCH(ENC_K_LN, launch_layernorm<T>(resid, e->lnp_g, e->lnp_b, xn, M, d, c.ln_eps, s));
   if ((st = launch_linear_t<T>(e, ENC_K_PROJ1, xn, d, e->proj1_w, e->proj1_b, hid, d, M, d, d,
@@ -548,7 +562,8 @@ encoder_status check_forward_args(encoder* e, const void* pcm, int64_t n_samples
 // lens: samples of each clip of the call (packed back to back in pcm)
 encoder_status forward_impl(encoder* e, const float* pcm, const std::vector<int64_t>& lens,
                             void* out, hipStream_t s, int64_t piece_windows, int stop = -1,
-                            int stop_layer = -1, float* dst = nullptr, int64_t dst_elems = 0) {
+                            int stop_layer = -1, float* dst = nullptr, int64_t dst_elems = 0,
+                            TapReq* taps = nullptr) {
   AE_HIP(hipSetDevice(e->device));
   const encoder_cfg& c = e->cfg;
   const int32_t batch = (int32_t)lens.size();
@@ -577,9 +592,10 @@ encoder_status forward_impl(encoder* e, const float* pcm, const std::vector<int6
                                              T, batch, dst, s));
     return ENC_OK;
   }
+  if (taps) taps->ntok_total = ntok;
   for (const Pass& p : ps) {
-    if (e->bf16) st = run_pass<bf16_t>(e, p, out, s, stop, stop_layer);
-    else st = run_pass<float>(e, p, out, s, stop, stop_layer);
+    if (e->bf16) st = run_pass<bf16_t>(e, p, out, s, stop, stop_layer, taps);
+    else st = run_pass<float>(e, p, out, s, stop, stop_layer, taps);
     if (st) return st;
   }
   if (stop >= 0) {
@@ -773,7 +789,7 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
   const size_t es = e->esz;
   std::vector<uint8_t> wh((size_t)(woff * (int64_t)es));
   auto put = [&](int64_t dst_el, int64_t idx, float v) {
-    if (es == 2) reinterpret_cast<bf16_t*>(wh.data())[dst_el + idx] = f32_to_bf16(v);
+    if (es == 2) reinterpret_cast<bf16_t*>(wh.data())[dst_el + idx] = host_f32_to_bf16(v);
     else reinterpret_cast<float*>(wh.data())[dst_el + idx] = v;
   };
   auto copy_plain = [&](int64_t dst_el, const float* s, int64_t n) {
@@ -931,6 +947,43 @@ encoder_status encoder_forward_ragged(encoder* e, const float* pcm, const int64_
   encoder_status st = ragged_lengths(e->cfg, lengths, n_clips, lens);
   if (st) return st;
   return forward_impl(e, pcm, lens, out, (hipStream_t)stream, 0);
+}
+
+encoder_status encoder_forward_taps(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+                                    void* out, const int32_t* layers, int32_t n_taps, float* taps,
+                                    void* stream) {
+  encoder_status st = check_forward_args(e, pcm, n_samples, batch, out);
+  if (st) return st;
+  if (n_taps < 0) return invalid("n_taps must be >= 0");
+  if (n_taps > 0 && (!layers || !taps)) return invalid("layers and taps must be non-NULL");
+  for (int32_t t = 0; t < n_taps; ++t)
+    if (layers[t] < 0 || layers[t] >= e->cfg.n_layers)
+      return invalid("tap " + std::to_string(t) + ": layer out of range");
+  TapReq req;
+  req.layers = layers;
+  req.n = n_taps;
+  req.dst = taps;
+  return forward_impl(e, pcm, std::vector<int64_t>((size_t)batch, n_samples), out,
+                      (hipStream_t)stream, 0, -1, -1, nullptr, 0, &req);
+}
+
+encoder_status encoder_splice(const void* frames, int64_t n_frames, int32_t dim,
+                              const int64_t* positions, void* table, int64_t table_rows,
+                              int32_t dtype, int32_t* n_skipped, void* stream) {
+  if (n_frames < 0 || table_rows < 0 || dim <= 0) return invalid("bad sizes");
+  if (n_frames > 0 && (!frames || !positions || !table))
+    return invalid("frames, positions and table must be non-NULL");
+  if (dtype != ENC_BF16 && dtype != ENC_F32) return invalid("bad dtype");
+  if (dim % 8) return invalid("dim must be a multiple of 8");
+  hipError_t err;
+  if (dtype == ENC_BF16)
+    err = launch_splice<bf16_t>((const bf16_t*)frames, n_frames, dim, positions, (bf16_t*)table,
+                                table_rows, n_skipped, (hipStream_t)stream);
+  else
+    err = launch_splice<float>((const float*)frames, n_frames, dim, positions, (float*)table,
+                               table_rows, n_skipped, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "encoder_splice");
+  return ENC_OK;
 }
 
 encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,

@@ -30,7 +30,9 @@ constexpr int QMAX = 128;   // maximum window length
 constexpr int HD = 64;      // head dimension
 constexpr int VTS = QMAX + 8;  // row stride (elements) of the transposed V and of P
 
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict__ qkv, WinRef wr,
+// Four workgroups per CU (the occupancy hint caps the kernel at 128 VGPRs; LDS 33 KB each):
+// 1024 resident (window, head) pairs instead of the 768 the unconstrained allocation allows.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn_bf16_kernel(const bf16_t* __restrict__ qkv, WinRef wr,
                                                         int32_t n_heads, int32_t d,
                                                         bf16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) bf16_t Ks[QMAX * HD];   // [key][64], chunk-swizzled
@@ -131,8 +133,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
     uint32_t own0 = 0, own1 = 0, snd0 = 0, snd1 = 0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t a0 = (uint32_t)f32_to_bf16(S[kb][4 * g + 0]) | ((uint32_t)f32_to_bf16(S[kb][4 * g + 1]) << 16);
-      const uint32_t a1 = (uint32_t)f32_to_bf16(S[kb][4 * g + 2]) | ((uint32_t)f32_to_bf16(S[kb][4 * g + 3]) << 16);
+      const uint32_t a0 = pack_bf16x2(S[kb][4 * g + 0], S[kb][4 * g + 1]);
+      const uint32_t a1 = pack_bf16x2(S[kb][4 * g + 2], S[kb][4 * g + 3]);
       if (g == g_own) { own0 = a0; own1 = a1; }
       if (g == g_send) { snd0 = a0; snd1 = a1; }
     }
@@ -159,8 +161,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
       bf16_t* o = out + (int64_t)(tok0 + q) * d + h * HD + db * 32 + 4 * half;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const uint32_t lo = (uint32_t)f32_to_bf16(O[4 * g] * inv) | ((uint32_t)f32_to_bf16(O[4 * g + 1] * inv) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(O[4 * g + 2] * inv) | ((uint32_t)f32_to_bf16(O[4 * g + 3] * inv) << 16);
+        const uint32_t lo = pack_bf16x2(O[4 * g] * inv, O[4 * g + 1] * inv);
+        const uint32_t hi = pack_bf16x2(O[4 * g + 2] * inv, O[4 * g + 3] * inv);
         *reinterpret_cast<uint2*>(o + 8 * g) = make_uint2(lo, hi);
       }
     }

@@ -23,12 +23,20 @@ __host__ __device__ inline float bf16_to_f32(bf16_t h) {
   c.u = (uint32_t)h << 16;
   return c.f;
 }
-__host__ __device__ inline bf16_t f32_to_bf16(float f) {  // round to nearest even
+// Host conversion (weight packing): round to nearest even, NaN kept quiet.
+inline bf16_t host_f32_to_bf16(float f) {
   union { uint32_t u; float f; } c;
   c.f = f;
   if ((c.u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((c.u >> 16) | ((c.u & 0xffff) ? 0x40 : 0));
   c.u += 0x7fffu + ((c.u >> 16) & 1u);
   return (bf16_t)(c.u >> 16);
+}
+// Device conversion: v_cvt_pk_bf16_f32 (round to nearest even), one instruction per pair.
+__device__ inline bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> struct StoreT;
@@ -163,5 +171,11 @@ hipError_t launch_swiglu_split(const T* gu, int64_t M, int32_t N2, T* out, hipSt
 
 template <typename T>
 hipError_t launch_to_f32(const T* src, int64_t n, float* dst, hipStream_t s);
+
+// table[pos[i]] = frames[i] for i < n (rows of dim elements); positions outside [0, rows) are
+// skipped and counted into *n_skipped (device, may be null).  dim * sizeof(T) % 16 == 0.
+template <typename T>
+hipError_t launch_splice(const T* frames, int64_t n, int32_t dim, const int64_t* pos, T* table,
+                         int64_t rows, int32_t* n_skipped, hipStream_t s);
 
 }  // namespace ae

@@ -22,8 +22,8 @@ template <typename T> struct Store4;
 template <> struct Store4<bf16_t> {
   __device__ static inline void put(bf16_t* p, float a, float b, float c, float d) {
     uint2 o;
-    o.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-    o.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+    o.x = pack_bf16x2(a, b);
+    o.y = pack_bf16x2(c, d);
     *reinterpret_cast<uint2*>(p) = o;
   }
 };

@@ -159,6 +159,28 @@ ENC_API encoder_status encoder_forward_long(encoder* e, const float* pcm, int64_
 ENC_API encoder_status encoder_forward_ragged(encoder* e, const float* pcm, const int64_t* lengths,
                                       int32_t n_clips, void* out, void* stream);
 
+/* Whole-clip path that also exports the residual stream (float32, after the layer's FFN
+ * residual add) after each layer listed in `layers` (host int32 [n_taps], each in
+ * [0, n_layers), repeats allowed): taps device float32 [n_taps, batch*F, d_model], row order as
+ * `out`.  For cross-layer adapters that read intermediate encoder states ("DeepStack"-style
+ * wiring named by the MOSS-Audio recipe page and the "scragnog/MOSS-Music-8B-Instruct-GGUF"
+ * card; the pages do not say which layers are read).  `layers` is read before the call returns. */
+ENC_API encoder_status encoder_forward_taps(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+                                    void* out, const int32_t* layers, int32_t n_taps, float* taps,
+                                    void* stream);
+
+/* Audio injection ("cstr/MOSS-Transcribe-preview-2B-GGUF" card, "Architecture", row "Audio
+ * injection"): the embedding-table rows at the prompt's audio placeholder positions are
+ * replaced by the adapter frames, in order: table[positions[i]] = frames[i], i < n_frames.
+ * frames: device [n_frames, dim]; positions: device int64 [n_frames]; table: device
+ * [table_rows, dim]; one dtype for both (ENC_BF16 or ENC_F32); dim % 8 == 0.  Positions outside
+ * [0, table_rows) are skipped and counted into *n_skipped (device int32, may be NULL; the caller
+ * clears it).  Positions should be distinct: a repeated row receives one of its frames.
+ * Asynchronous on `stream`. */
+ENC_API encoder_status encoder_splice(const void* frames, int64_t n_frames, int32_t dim,
+                              const int64_t* positions, void* table, int64_t table_rows,
+                              int32_t dtype, int32_t* n_skipped, void* stream);
+
 /* Normalised log-mel only: mel device float32 [batch, n_samples/160, 128]. */
 ENC_API encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
                                float* mel, void* stream);

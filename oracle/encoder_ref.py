@@ -449,6 +449,28 @@ def encode_ragged(clips: list, Wt: dict, cfg: dict) -> np.ndarray:
     return np.concatenate([encode(np.asarray(c), Wt, cfg) for c in clips], axis=0)
 
 
+def splice(table: np.ndarray, positions, frames: np.ndarray) -> tuple[np.ndarray, int]:
+    """Audio injection (card T, "Architecture", row "Audio injection"): the embedding rows at
+    the audio placeholder positions are replaced by the adapter frames, in order.  Returns the
+    new table and the number of positions outside the table (left alone)."""
+    out = table.copy()
+    skipped = 0
+    for i, p in enumerate(positions):
+        if 0 <= p < out.shape[0]:
+            out[p] = frames[i]
+        else:
+            skipped += 1
+    return out, skipped
+
+
+def encode_taps(pcm: np.ndarray, Wt: dict, cfg: dict, layers: list) -> tuple[np.ndarray, list]:
+    """Whole-clip encoding plus the residual stream after each listed layer (the states a
+    cross-layer adapter would read; which layers is not stated on the pages)."""
+    st = {}
+    y = encode_mel(log_mel(pcm), Wt, cfg, st)
+    return y, [st[f"layer{l}"] for l in layers]
+
+
 def ragged_window_plan(lengths: list, window_tokens: int) -> list[dict]:
     """Window plan of a ragged call: each clip's ``window_plan`` in clip order, tagged with the
     clip index, with the first output token counted over the whole call."""

@@ -317,6 +317,42 @@ def test_ragged_rejects_bad_calls(tiny):
         enc.forward_ragged(pcm, [32000])
 
 
+def test_tiny_layer_taps(tiny):
+    enc, Wt = tiny
+    xs = np.stack([S.mixed_clip(320 + b, 53920) for b in range(2)])
+    pcm = to_dev(xs)
+    out, taps = enc.forward_taps(pcm, [1, 0, 1])
+    assert torch.equal(out, enc.forward(pcm))
+    # the tapped residual equals the stage-wise export of the same layer, bit for bit
+    assert torch.equal(taps[0], taps[2])
+    for t, l in ((0, 1), (1, 0)):
+        assert np.array_equal(taps[t].cpu().numpy(), enc.debug_stage(pcm, B.STAGE_LAYER, l).cpu().numpy())
+    F = O.n_output_frames(53920, 25)
+    for b in range(2):
+        _, ref = O.encode_taps(xs[b], Wt, O.TINY, [1, 0])
+        for t in range(2):
+            g = taps[t, b * F:(b + 1) * F].cpu().numpy()
+            assert np.abs(g - ref[t]).max() <= 2e-4 * np.abs(ref[t]).max()
+    with pytest.raises(B.EncoderError):
+        enc.forward_taps(pcm, [2])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_splice_is_exact(dtype):
+    rng = np.random.default_rng(6)
+    table = rng.standard_normal((300, 2048)).astype(np.float32)
+    frames = rng.standard_normal((75, 2048)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        table, frames = bf16_round(table), bf16_round(frames)
+    pos = np.concatenate([np.arange(10, 80), [299, 300, -3, 0, 1000]])
+    ref, skipped = O.splice(table, pos, frames)
+    t = to_dev(table, dtype)
+    cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.splice(to_dev(frames, dtype), torch.from_numpy(pos).to(DEV), t, cnt)
+    assert int(cnt.item()) == skipped == 3
+    assert np.array_equal(t.float().cpu().numpy(), ref)
+
+
 def test_tiny_deterministic(tiny):
     enc, _ = tiny
     pcm = to_dev(S.mixed_batch([1, 2], 64000))

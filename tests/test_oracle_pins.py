@@ -404,9 +404,10 @@ def test_attention_invariants():
 # --------------------------------------------------------------------------------------------
 # whole tower: an independent fp64 torch assembly from library ops, and the window invariants
 # --------------------------------------------------------------------------------------------
-def torch_tower(mel, Wt, cfg):
+def torch_tower(mel, Wt, cfg, taps=None):
     """The tower written with torch.nn.functional library routines (conv2d, layer_norm, SDPA
-    with a block-diagonal mask, gelu, silu) instead of the oracle's own loops and matmuls."""
+    with a block-diagonal mask, gelu, silu) instead of the oracle's own loops and matmuls.
+    `taps` (a dict) receives the residual stream after each layer."""
     T = {k: torch.from_numpy(v) for k, v in Wt.items()}
     Wn = cfg["window_tokens"]
     outs, wins, tok = [], [], 0
@@ -438,6 +439,8 @@ def torch_tower(mel, Wt, cfg):
         a = Fn.layer_norm(x, (d,), T[p + "ln2.g"], T[p + "ln2.b"], 1e-5)
         x = x + Fn.linear(Fn.gelu(Fn.linear(a, T[p + "fc1.w"], T[p + "fc1.b"])),
                           T[p + "fc2.w"], T[p + "fc2.b"])
+        if taps is not None:
+            taps[i] = x.numpy().copy()
     z = Fn.layer_norm(x, (d,), T["ln_post.g"], T["ln_post.b"], 1e-5)
     z = Fn.linear(Fn.gelu(Fn.linear(z, T["proj1.w"], T["proj1.b"])), T["proj2.w"], T["proj2.b"])
     return Fn.linear(Fn.silu(Fn.linear(z, T["gate.w"])) * Fn.linear(z, T["up.w"]),
@@ -537,3 +540,27 @@ def test_ragged_call_is_equivariant_under_clip_order(tiny_weights):
     assert np.array_equal(yp, np.concatenate([yc, ya, yb]))
     # the shortest clip (201 samples: one frame) yields one output frame
     assert F[1] == 1 and yb.shape == (1, 512)
+
+
+# ---- layer taps and audio injection -----------------------------------------------------------
+def test_layer_taps_match_torch_assembly(tiny_weights):
+    x = S.pink_plus_bursts(seed=31, n=53920)
+    y, taps = O.encode_taps(x, tiny_weights, O.TINY, [1, 0, 1])
+    ref = {}
+    yref = torch_tower(O.log_mel(x), tiny_weights, O.TINY, ref)
+    np.testing.assert_allclose(y, yref, rtol=1e-9, atol=1e-12 * np.abs(yref).max())
+    for t, l in zip(taps, [1, 0, 1]):
+        np.testing.assert_allclose(t, ref[l], rtol=1e-9, atol=1e-12 * np.abs(ref[l]).max())
+
+
+def test_splice_replaces_exactly_the_placeholder_rows():
+    rng = np.random.default_rng(5)
+    table = rng.standard_normal((50, 16))
+    frames = rng.standard_normal((6, 16))
+    pos = [3, 4, 5, 40, 77, -1]  # the last two are outside the table
+    out, skipped = O.splice(table, pos, frames)
+    assert skipped == 2
+    keep = np.setdiff1d(np.arange(50), [3, 4, 5, 40])
+    assert np.array_equal(out[keep], table[keep])
+    assert np.array_equal(out[[3, 4, 5, 40]], frames[:4])
+    assert np.array_equal(table, O.splice(table, [], frames[:0])[0])
