@@ -81,6 +81,8 @@ _SIGS = {
     "encoder_forward_ragged": [c_void_p, c_void_p, POINTER(c_int64), c_int32, c_void_p, c_void_p],
     "encoder_forward_taps": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, POINTER(c_int32),
                              c_int32, c_void_p, c_void_p],
+    "encoder_conditioned_length": [c_int64, c_int32, POINTER(c_int64)],
+    "encoder_condition_audio": [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p],
     "encoder_splice": [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_int64, c_int32, c_void_p,
                        c_void_p],
     "encoder_log_mel": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
@@ -146,6 +148,12 @@ def encoder_plan_windows(cfg: dict, n_samples: int, batch: int) -> np.ndarray:
                                       tab.ctypes.data_as(POINTER(c_int32)), nw.value,
                                       ctypes.byref(nw)))
     return tab
+
+
+def encoder_conditioned_length(n_in: int, sample_rate: int) -> int:
+    n = c_int64()
+    _check(lib().encoder_conditioned_length(n_in, sample_rate, ctypes.byref(n)))
+    return n.value
 
 
 def _lengths(lengths) -> np.ndarray:
@@ -264,6 +272,19 @@ class Encoder:
                                           L.ctypes.data_as(POINTER(c_int32)), L.size, _ptr(taps),
                                           _stream()))
         return out, taps
+
+    def condition_audio(self, pcm, sample_rate: int, out=None):
+        """pcm: float32 CUDA tensor [n] (mono) or [n, channels] (interleaved) at sample_rate ->
+        16 kHz mono float32 [n_out] (channel mean, windowed-sinc resampling)."""
+        import torch
+        assert pcm.is_cuda and pcm.dtype == torch.float32 and pcm.is_contiguous()
+        n, ch = (pcm.shape[0], 1) if pcm.dim() == 1 else (pcm.shape[0], pcm.shape[1])
+        n_out = encoder_conditioned_length(n, sample_rate)
+        if out is None:
+            out = torch.empty(n_out, dtype=torch.float32, device=pcm.device)
+        _check(lib().encoder_condition_audio(self._h, _ptr(pcm), n, ch, sample_rate, _ptr(out),
+                                             _stream()))
+        return out
 
     def log_mel(self, pcm):
         import torch

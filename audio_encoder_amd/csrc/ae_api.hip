@@ -137,6 +137,60 @@ static int64_t frames_out(const encoder_cfg& c, int64_t n_samples) {
   return f;
 }
 
+// ------------------------------------------------------------------------------------------
+// input conditioning (resampling to 16 kHz; the filter is described in ae_resample.hip)
+// ------------------------------------------------------------------------------------------
+struct ResamplePlan { int32_t L = 1, M = 1, K = 0; };
+
+static int64_t gcd64(int64_t a, int64_t b) {
+  while (b) { const int64_t t = a % b; a = b; b = t; }
+  return a;
+}
+
+// L/M = 16000/fs in lowest terms; K = taps on each side.  Returns false for rates this build
+// does not handle (more than 4096 phases, or more than 32x downsampling).
+static bool resample_plan(int32_t fs, ResamplePlan& r) {
+  if (fs <= 0) return false;
+  const int64_t g = gcd64(fs, 16000);
+  r.L = (int32_t)(16000 / g);
+  r.M = (int32_t)(fs / g);
+  if (r.L == 1 && r.M == 1) { r.K = 0; return true; }
+  if (r.L > 4096 || r.M > 32 * r.L) return false;
+  const double fc = 0.5 * 0.945 * std::min(1.0, (double)r.L / r.M);
+  const double R = 16.0 / (2.0 * fc);
+  r.K = (int32_t)std::ceil(R);
+  return true;
+}
+
+static std::vector<float> resample_taps(const ResamplePlan& r) {
+  const double fc = 0.5 * 0.945 * std::min(1.0, (double)r.L / r.M);
+  const double R = 16.0 / (2.0 * fc);
+  const double pi = 3.14159265358979323846;
+  std::vector<float> t((size_t)r.L * 2 * r.K);
+  std::vector<double> h((size_t)2 * r.K);
+  for (int32_t p = 0; p < r.L; ++p) {
+    const double frac = (double)p / r.L;
+    double sum = 0.0;
+    for (int32_t k = 0; k < 2 * r.K; ++k) {
+      const double dd = (double)(k - r.K + 1) - frac;  // input sample minus output position
+      double v = 0.0;
+      if (std::fabs(dd) <= R) {
+        const double x = 2.0 * fc * dd;
+        const double sinc = x == 0.0 ? 1.0 : std::sin(pi * x) / (pi * x);
+        v = 2.0 * fc * sinc * 0.5 * (1.0 + std::cos(pi * dd / R));
+      }
+      h[k] = v;
+      sum += v;
+    }
+    for (int32_t k = 0; k < 2 * r.K; ++k) t[(size_t)p * 2 * r.K + k] = (float)(h[k] / sum);
+  }
+  return t;
+}
+
+static int64_t conditioned_length(int64_t n_in, const ResamplePlan& r) {
+  return (n_in * r.L + r.M - 1) / r.M;
+}
+
 struct Pass { int64_t win0, nwin, tok0, ntok; };
 
 // consecutive windows grouped into passes; a pass ends where `boundary(window)` says so or
@@ -267,6 +321,8 @@ struct encoder {
   // workspace (grown on demand)
   struct Buf { void* p = nullptr; int64_t bytes = 0; };
   Buf mel_raw, max_key, ctab, wtab, tpos, act1, act2, tokA, resid, xn, qkv, attn, hid, hid2, z, dbg;
+  Buf rs_taps;            // polyphase table of the last input-conditioning rate
+  int32_t rs_rate = 0;
   int64_t ws_bytes = 0, ws_peak = 0;
   // host staging for the plan upload
   void* pinned = nullptr;
@@ -627,7 +683,7 @@ void free_all(encoder* e) {
   if (!e) return;
   hipSetDevice(e->device);
   hipDeviceSynchronize();
-  encoder::Buf* bufs[] = {&e->mel_raw, &e->max_key, &e->ctab, &e->wtab, &e->tpos, &e->act1, &e->act2,
+  encoder::Buf* bufs[] = {&e->mel_raw, &e->max_key, &e->ctab, &e->wtab, &e->tpos, &e->rs_taps, &e->act1, &e->act2,
                           &e->tokA, &e->resid, &e->xn, &e->qkv, &e->attn, &e->hid, &e->hid2,
                           &e->z, &e->dbg};
   for (auto* b : bufs)
@@ -983,6 +1039,56 @@ encoder_status encoder_splice(const void* frames, int64_t n_frames, int32_t dim,
     err = launch_splice<float>((const float*)frames, n_frames, dim, positions, (float*)table,
                                table_rows, n_skipped, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "encoder_splice");
+  return ENC_OK;
+}
+
+encoder_status encoder_conditioned_length(int64_t n_in, int32_t sample_rate, int64_t* n_out) {
+  if (!n_out) return invalid("n_out is NULL");
+  if (n_in < 1) return invalid("n_in must be >= 1");
+  ResamplePlan r;
+  if (!resample_plan(sample_rate, r)) {
+    set_error("sample rate " + std::to_string(sample_rate) + " is not supported");
+    return ENC_E_UNSUPPORTED;
+  }
+  if (n_in > (int64_t(1) << 40)) return invalid("n_in too large");
+  *n_out = conditioned_length(n_in, r);
+  return ENC_OK;
+}
+
+encoder_status encoder_condition_audio(encoder* e, const float* in, int64_t n_in, int32_t channels,
+                                       int32_t sample_rate, float* out, void* stream) {
+  if (!e) return invalid("encoder handle is NULL");
+  if (!in || !out) return invalid("in and out must be non-NULL");
+  if (n_in < 1) return invalid("n_in must be >= 1");
+  if (channels < 1 || channels > 64) return invalid("channels must be in [1, 64]");
+  if (n_in > (int64_t(1) << 40)) return invalid("n_in too large");
+  ResamplePlan r;
+  if (!resample_plan(sample_rate, r)) {
+    set_error("sample rate " + std::to_string(sample_rate) + " is not supported");
+    return ENC_E_UNSUPPORTED;
+  }
+  AE_HIP(hipSetDevice(e->device));
+  hipStream_t s = (hipStream_t)stream;
+  encoder_status st;
+  if (r.K > 0 && e->rs_rate != sample_rate) {
+    const std::vector<float> taps = resample_taps(r);
+    const int64_t tb = (int64_t)taps.size() * 4;
+    if ((st = ensure(e, e->rs_taps, tb))) return st;
+    AE_HIP(hipEventSynchronize(e->upload_done));
+    if (e->pinned_bytes < tb) {
+      if (e->pinned) AE_HIP(hipHostFree(e->pinned));
+      e->pinned = nullptr;
+      e->pinned_bytes = 0;
+      AE_HIP(hipHostMalloc(&e->pinned, tb, hipHostMallocDefault));
+      e->pinned_bytes = tb;
+    }
+    std::memcpy(e->pinned, taps.data(), tb);
+    AE_HIP(hipMemcpyAsync(e->rs_taps.p, e->pinned, tb, hipMemcpyHostToDevice, s));
+    AE_HIP(hipEventRecord(e->upload_done, s));
+    e->rs_rate = sample_rate;
+  }
+  LAUNCH(ENC_K_OTHER, launch_resample(in, n_in, channels, r.L, r.M, r.K, (const float*)e->rs_taps.p,
+                                      out, conditioned_length(n_in, r), s));
   return ENC_OK;
 }
 

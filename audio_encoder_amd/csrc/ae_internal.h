@@ -172,6 +172,11 @@ hipError_t launch_swiglu_split(const T* gu, int64_t M, int32_t N2, T* out, hipSt
 template <typename T>
 hipError_t launch_to_f32(const T* src, int64_t n, float* dst, hipStream_t s);
 
+// mono 16 kHz from interleaved [n_in][channels]: the mean of the channels, resampled with the
+// L x 2K polyphase table `taps` (L = M = 1: downmix only)
+hipError_t launch_resample(const float* in, int64_t n_in, int32_t channels, int32_t L, int32_t M,
+                           int32_t K, const float* taps, float* out, int64_t n_out, hipStream_t s);
+
 // table[pos[i]] = frames[i] for i < n (rows of dim elements); positions outside [0, rows) are
 // skipped and counted into *n_skipped (device, may be null).  dim * sizeof(T) % 16 == 0.
 template <typename T>

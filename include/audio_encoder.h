@@ -181,6 +181,23 @@ ENC_API encoder_status encoder_splice(const void* frames, int64_t n_frames, int3
                               const int64_t* positions, void* table, int64_t table_rows,
                               int32_t dtype, int32_t* n_skipped, void* stream);
 
+/* ---- input conditioning ("SILVERTHRONE/Ossicle-4B" card: mono or stereo at any rate;
+ * "cstr/MOSS-Transcribe-preview-2B-GGUF" card, "Quick Start": the tower takes 16 kHz mono) --- */
+
+/* Samples after conditioning n_in input frames at sample_rate: ceil(n_in * 16000 / rate) (n_in
+ * at 16 kHz).  ENC_E_UNSUPPORTED for rates whose ratio to 16 kHz needs more than 4096 filter
+ * phases (16000 / gcd(rate, 16000) > 4096) or more than 32x downsampling. */
+ENC_API encoder_status encoder_conditioned_length(int64_t n_in, int32_t sample_rate, int64_t* n_out);
+
+/* 16 kHz mono from interleaved float32 PCM in (device [n_in][channels], 1 <= channels <= 64):
+ * the mean of the channels, then (rates other than 16 kHz) band-limited resampling with a
+ * Hann-windowed sinc: cutoff 0.945 x the lower Nyquist, 16 zero crossings per side, each
+ * polyphase phase normalised to unit DC gain, zeros outside the signal.  out: device float32
+ * [n_out] (encoder_conditioned_length).  The pages name no filter; this one is the documented
+ * reading.  The filter table is built on the host and cached per rate in the handle. */
+ENC_API encoder_status encoder_condition_audio(encoder* e, const float* in, int64_t n_in, int32_t channels,
+                                       int32_t sample_rate, float* out, void* stream);
+
 /* Normalised log-mel only: mel device float32 [batch, n_samples/160, 128]. */
 ENC_API encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
                                float* mel, void* stream);

@@ -449,6 +449,61 @@ def encode_ragged(clips: list, Wt: dict, cfg: dict) -> np.ndarray:
     return np.concatenate([encode(np.asarray(c), Wt, cfg) for c in clips], axis=0)
 
 
+# ---- input conditioning ---------------------------------------------------------------------
+# Card O's model summary accepts mono or stereo at any sample rate; card T's "Quick Start" feeds
+# the tower 16 kHz mono.  The pages name no resampling filter.  Reading (R29): the mean of the
+# channels; 16 kHz passes through; otherwise band-limited interpolation with a Hann-windowed
+# sinc (cutoff 0.945 x the lower Nyquist, 16 zero crossings per side), each output sample's
+# weights normalised to sum to 1 over the full window (zeros outside the signal).
+RS_ROLLOFF = 0.945
+RS_ZEROS = 16
+
+
+def downmix(x: np.ndarray) -> np.ndarray:
+    """[n] or interleaved [n, channels] -> mono [n]: the mean over channels."""
+    x = np.asarray(x, dtype=np.float64)
+    return x if x.ndim == 1 else x.mean(axis=1)
+
+
+def resample_ratio(fs: int) -> tuple[int, int]:
+    """(L, M) with L / M = 16000 / fs in lowest terms."""
+    g = math.gcd(int(fs), 16000)
+    return 16000 // g, int(fs) // g
+
+
+def conditioned_length(n_in: int, fs: int) -> int:
+    L, M = resample_ratio(fs)
+    return -(-n_in * L // M)
+
+
+def resample_to_16k(x: np.ndarray, fs: int) -> np.ndarray:
+    """Mono x at fs -> 16 kHz (R29), output sample j at input position t_j = j * fs / 16000:
+    y[j] = sum_i x[i] h(i - t_j) / sum_k h(k - t_j) with the sums over the integers i, k with
+    |i - t_j| <= R (x = 0 outside [0, n)), h(u) = 2 fc sinc(2 fc u) (1 + cos(pi u / R)) / 2,
+    fc = 0.945 min(1, 16000/fs) / 2 cycles per input sample, R = 16 / (2 fc)."""
+    x = np.asarray(x, dtype=np.float64)
+    L, M = resample_ratio(fs)
+    if L == 1 and M == 1:
+        return x.copy()
+    fc = 0.5 * RS_ROLLOFF * min(1.0, L / M)
+    R = RS_ZEROS / (2.0 * fc)
+    n_out = conditioned_length(x.size, fs)
+    y = np.zeros(n_out)
+    for j in range(n_out):
+        t = j * M / L
+        i = np.arange(math.ceil(t - R), math.floor(t + R) + 1)
+        u = i - t
+        h = 2.0 * fc * np.sinc(2.0 * fc * u) * 0.5 * (1.0 + np.cos(np.pi * u / R))
+        xi = np.where((i >= 0) & (i < x.size), x[np.clip(i, 0, x.size - 1)], 0.0)
+        y[j] = (h * xi).sum() / h.sum()
+    return y
+
+
+def condition_audio(x: np.ndarray, fs: int) -> np.ndarray:
+    """Any channel count and rate -> 16 kHz mono (R29)."""
+    return resample_to_16k(downmix(x), fs)
+
+
 def splice(table: np.ndarray, positions, frames: np.ndarray) -> tuple[np.ndarray, int]:
     """Audio injection (card T, "Architecture", row "Audio injection"): the embedding rows at
     the audio placeholder positions are replaced by the adapter frames, in order.  Returns the

@@ -353,6 +353,30 @@ def test_splice_is_exact(dtype):
     assert np.array_equal(t.float().cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("fs,ch", [(8000, 1), (22050, 2), (44100, 1), (44100, 2), (48000, 2),
+                                   (96000, 1), (16000, 2), (11025, 3)])
+def test_condition_audio_matches_oracle(tiny, fs, ch):
+    enc, _ = tiny
+    rng = np.random.default_rng(fs + ch)
+    n = int(1.3 * fs) + 17
+    x = np.stack([S.pink(rng, n) * 0.3 for _ in range(ch)], axis=1).astype(np.float32)
+    if ch == 1:
+        x = x[:, 0]
+    got = enc.condition_audio(to_dev(x), fs).cpu().numpy()
+    ref = O.condition_audio(x.astype(np.float64), fs)
+    assert got.shape == ref.shape == (O.conditioned_length(n, fs),)
+    assert np.abs(got - ref).max() <= 2e-6 * np.abs(ref).max(), np.abs(got - ref).max()
+
+
+def test_conditioned_clip_encodes_like_the_16k_clip(tiny):
+    # a 16 kHz mono clip passes through conditioning unchanged, so its encoding is unchanged
+    enc, _ = tiny
+    x = to_dev(S.three_sines())
+    y = enc.condition_audio(x, 16000)
+    assert torch.equal(y, x)
+    assert torch.equal(enc.forward(y[None]), enc.forward(x[None]))
+
+
 def test_tiny_deterministic(tiny):
     enc, _ = tiny
     pcm = to_dev(S.mixed_batch([1, 2], 64000))

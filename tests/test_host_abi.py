@@ -114,6 +114,19 @@ def test_ragged_plan_rejects_bad_lengths(lengths):
     assert ei.value.status == B.ENC_E_INVALID_ARG
 
 
+@pytest.mark.parametrize("fs", [8000, 11025, 16000, 22050, 32000, 44100, 48000, 88200, 96000, 192000])
+@pytest.mark.parametrize("n", [1, 3, 44100, 1_234_567])
+def test_conditioned_length_matches_oracle(fs, n):
+    assert B.encoder_conditioned_length(n, fs) == O.conditioned_length(n, fs)
+
+
+@pytest.mark.parametrize("fs", [44101, 7, 0, -16000, 600000])
+def test_conditioning_rejects_unsupported_rates(fs):
+    with pytest.raises(B.EncoderError) as ei:
+        B.encoder_conditioned_length(1000, fs)
+    assert ei.value.status in (B.ENC_E_UNSUPPORTED, B.ENC_E_INVALID_ARG)
+
+
 def test_plan_of_hour_stream_has_45000_tokens():
     tab = B.encoder_plan_windows(B.FULL, 57_600_000, 1)
     assert len(tab) == 450 and tab[:, 5].sum() == 45000

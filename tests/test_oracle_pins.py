@@ -564,3 +564,45 @@ def test_splice_replaces_exactly_the_placeholder_rows():
     assert np.array_equal(out[keep], table[keep])
     assert np.array_equal(out[[3, 4, 5, 40]], frames[:4])
     assert np.array_equal(table, O.splice(table, [], frames[:0])[0])
+
+
+# ---- input conditioning (R29: channel mean; windowed-sinc resampling to 16 kHz) -----------------
+@pytest.mark.parametrize("fs", [8000, 22050, 44100, 48000, 96000])
+def test_resampler_passes_an_in_band_sine_at_its_exact_phase(fs):
+    # a 1 kHz sine sampled at fs must come out as the same sine sampled at 16 kHz: output sample
+    # j sits at input time j*fs/16000 (a wrong ratio, cutoff or phase fails by far more)
+    x = np.sin(2 * np.pi * 1000 * np.arange(fs) / fs)
+    y = O.resample_to_16k(x, fs)
+    assert y.size == O.conditioned_length(fs, fs) == 16000
+    ref = np.sin(2 * np.pi * 1000 * np.arange(16000) / 16000)
+    assert np.abs(y[400:-400] - ref[400:-400]).max() < 1e-4
+
+
+@pytest.mark.parametrize("fs", [22050, 44100, 48000])
+def test_resampler_rejects_content_above_8khz(fs):
+    y = O.resample_to_16k(np.sin(2 * np.pi * 10000 * np.arange(fs) / fs), fs)
+    assert np.sqrt(np.mean(y[400:-400] ** 2)) < 1e-3  # the input RMS is 0.707
+
+
+@pytest.mark.parametrize("fs", [11025, 44100, 48000])
+def test_resampler_has_unit_dc_gain(fs):
+    y = O.resample_to_16k(np.full(fs // 2, 0.7), fs)
+    assert np.abs(y[400:-400] - 0.7).max() < 1e-12
+
+
+def test_16khz_is_passed_through_and_channels_are_averaged():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((3000, 2))
+    assert np.array_equal(O.condition_audio(x[:, 0], 16000), x[:, 0])
+    assert np.array_equal(O.condition_audio(x, 16000), x.mean(axis=1))
+    # linear: the mean of the channels resampled = the mean of the resampled channels
+    a = O.condition_audio(x, 44100)
+    b = 0.5 * (O.resample_to_16k(x[:, 0], 44100) + O.resample_to_16k(x[:, 1], 44100))
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_conditioned_length():
+    assert O.conditioned_length(44100, 44100) == 16000
+    assert O.conditioned_length(44101, 44100) == 16001  # ceil
+    assert O.conditioned_length(3, 48000) == 1
+    assert O.conditioned_length(1000, 8000) == 2000
