@@ -44,13 +44,13 @@ class EncoderCfg(ctypes.Structure):
                 ("n_layers", c_int32), ("n_heads", c_int32), ("head_dim", c_int32),
                 ("d_ffn", c_int32), ("window_tokens", c_int32), ("d_out", c_int32),
                 ("d_adapter", c_int32), ("piece_tokens", c_int32), ("dtype", c_int32),
-                ("ln_eps", c_float), ("max_tokens_per_pass", c_int64)]
+                ("ln_eps", c_float), ("max_tokens_per_pass", c_int64), ("weight_bits", c_int32)]
 
 
 def make_cfg(cfg: dict) -> EncoderCfg:
     c = EncoderCfg()
     for name, _ in EncoderCfg._fields_:
-        v = cfg[name]
+        v = cfg.get(name, 16) if name == "weight_bits" else cfg[name]
         if name == "dtype":
             v = {"bf16": ENC_BF16, "f32": ENC_F32}.get(v, v)
         setattr(c, name, v)
@@ -92,6 +92,9 @@ _SIGS = {
     "encoder_timing_read": [c_void_p, POINTER(c_double), POINTER(c_int64), c_int32],
     "encoder_op_linear": [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32,
                           c_int32, c_int32, c_void_p],
+    "encoder_quantize_int4": [POINTER(c_float), c_int64, c_int64, c_void_p, c_void_p],
+    "encoder_op_linear_int4": [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
+                               c_int32, c_int32, c_void_p],
     "encoder_op_attention": [c_void_p, c_void_p, c_int32, c_int32, c_int64, c_void_p, c_int32,
                              c_void_p],
     "encoder_op_layernorm": [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_float,
@@ -337,6 +340,26 @@ def splice(frames, positions, table, n_skipped=None):
                                 _ptr(table), table.shape[0], _dtype_code(table.dtype),
                                 _ptr(n_skipped), _stream()))
     return table
+
+
+def encoder_quantize_int4(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """float32 [N, K] -> (q uint8 [N, K/2], scales uint16 bf16 bits [N, K/128])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    q = np.zeros((N, K // 2), dtype=np.uint8)
+    sc = np.zeros((N, max(K // 128, 1)), dtype=np.uint16)
+    _check(lib().encoder_quantize_int4(w.ctypes.data_as(POINTER(c_float)), N, K,
+                                       c_void_p(q.ctypes.data), c_void_p(sc.ctypes.data)))
+    return q, sc
+
+
+def op_linear_int4(A, q, scales, bias, C, epi: int):
+    """C = epi(A @ dequant(q, scales)^T + bias) on the GPU; A/C bf16 CUDA tensors, q uint8 and
+    scales int16 (bf16 bits) CUDA tensors from encoder_quantize_int4."""
+    M, K = A.shape
+    N = q.shape[0]
+    _check(lib().encoder_op_linear_int4(_ptr(A), _ptr(q), _ptr(scales), _ptr(bias), _ptr(C), M, N,
+                                        K, epi, _stream()))
 
 
 def op_linear(A, W, bias, C, epi: int):

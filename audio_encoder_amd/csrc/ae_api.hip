@@ -60,6 +60,13 @@ static encoder_status check_cfg(const encoder_cfg* c) {
   if (c->max_tokens_per_pass < 0) return invalid("max_tokens_per_pass must be >= 0");
   if (c->max_tokens_per_pass > 0 && c->max_tokens_per_pass < c->window_tokens)
     return invalid("max_tokens_per_pass must hold at least one window");
+  if (c->weight_bits != 0 && c->weight_bits != 16 && c->weight_bits != 4)
+    return invalid("weight_bits must be 16 (or 0) or 4");
+  if (c->weight_bits == 4) {
+    if (c->dtype != ENC_BF16) return invalid("int4 weights need dtype ENC_BF16");
+    if (c->d_model % 128 || c->d_ffn % 128 || c->d_out % 128 || c->d_adapter % 128)
+      return invalid("int4 weights need d_model, d_ffn, d_out and d_adapter multiples of 128");
+  }
   if (c->sample_rate != 16000) {
     set_error("only 16 kHz input is supported (no resampling)");
     return ENC_E_UNSUPPORTED;
@@ -288,6 +295,36 @@ static void parallel_for(int64_t n, F fn) {
   for (auto& x : th) x.join();
 }
 
+// ------------------------------------------------------------------------------------------
+// int4 weight-only quantisation (round to nearest, groups of 128 along K, bf16 scales)
+// ------------------------------------------------------------------------------------------
+// Row n, group g: s = bf16(max |w| / 7); q = clamp(rint(w / s), -8, 7) (0 when s == 0); the
+// weight used on the GPU is bf16(q * s).  q is packed two per byte, even k in the low nibble.
+static void quantize_int4_rows(const float* w, int64_t N, int64_t K, uint8_t* q, bf16_t* sc) {
+  const int64_t G = K / 128;
+  parallel_for(N, [&](int64_t a, int64_t b) {
+    for (int64_t n = a; n < b; ++n) {
+      const float* row = w + n * K;
+      for (int64_t g = 0; g < G; ++g) {
+        double mx = 0.0;
+        for (int j = 0; j < 128; ++j) mx = std::max(mx, std::fabs((double)row[g * 128 + j]));
+        const bf16_t sb = host_f32_to_bf16((float)(mx / 7.0));
+        sc[n * G + g] = sb;
+        const double sd = (double)bf16_to_f32(sb);
+        for (int j = 0; j < 128; j += 2) {
+          int v[2];
+          for (int e = 0; e < 2; ++e) {
+            const double x = sd > 0.0 ? std::nearbyint((double)row[g * 128 + j + e] / sd) : 0.0;
+            v[e] = (int)std::min(7.0, std::max(-8.0, x));
+          }
+          q[n * (K / 2) + (g * 128 + j) / 2] = (uint8_t)((v[0] & 0xf) | ((v[1] & 0xf) << 4));
+        }
+      }
+    }
+  });
+}
+
+
 }  // namespace ae
 
 using namespace ae;
@@ -295,8 +332,15 @@ using namespace ae;
 // ------------------------------------------------------------------------------------------
 // handle
 // ------------------------------------------------------------------------------------------
+// One linear weight [N, K] on the device: bf16/f32 (w) or int4 + bf16 scales (q, s).
+struct WMat {
+  void* w = nullptr;
+  const uint8_t* q = nullptr;
+  const bf16_t* s = nullptr;
+};
+
 struct LayerW {
-  void *wqkv, *wo, *w1, *w2;
+  WMat wqkv, wo, w1, w2;
   float *bqkv, *bo, *b1, *b2, *ln1g, *ln1b, *ln2g, *ln2b;
 };
 
@@ -309,13 +353,14 @@ struct encoder {
   size_t esz = 2;
   // packed parameters
   void* wdev = nullptr;   // dtype weights
+  uint8_t* qdev = nullptr;  // int4 weights and their scales (weight_bits = 4)
   float* fdev = nullptr;  // float32 parameters and tables
-  int64_t wbytes = 0, fbytes = 0;
+  int64_t wbytes = 0, fbytes = 0, qbytes = 0;
   float *conv1_w, *conv1_b, *conv2_b, *conv3_b;
   void *conv2_w, *conv3_w, *conv_out_w;
   std::vector<LayerW> layers;
   float *lnp_g, *lnp_b, *proj1_b, *proj2_b;
-  void *proj1_w, *proj2_w, *gateup_w, *down_w;
+  WMat proj1_w, proj2_w, gateup_w, down_w;
   float* pe;
   MelTables mel;
   // workspace (grown on demand)
@@ -467,11 +512,11 @@ encoder_status upload_plan(encoder* e, const std::vector<ClipSpan>& clips, const
 }
 
 template <typename T>
-encoder_status launch_linear_t(encoder* e, int kid, const void* A, int64_t lda, const void* Wt,
+encoder_status launch_linear_t(encoder* e, int kid, const void* A, int64_t lda, const WMat& Wt,
                                const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
                                int epi, hipStream_t s, const float* pe = nullptr,
                                const int32_t* tok_pos = nullptr) {
-  LinearArgs a{A, lda, Wt, bias, C, ldc, M, N, K, pe, tok_pos};
+  LinearArgs a{A, lda, Wt.w, bias, C, ldc, M, N, K, pe, tok_pos, Wt.q, Wt.s};
   LAUNCH(kid, launch_linear<T>(a, epi, kid, s));
   return ENC_OK;
 }
@@ -520,7 +565,7 @@ encoder_status run_pass(encoder* e, const Pass& p, void* out, hipStream_t s, int
   LAUNCH(ENC_K_CONV3, launch_conv_igemm<T>(g, 3, act2, (const T*)e->conv3_w, e->conv3_b, C, tokA, s));
   if (stop == ST_CONV3) return ENC_OK;
   encoder_status st;
-  if ((st = launch_linear_t<T>(e, ENC_K_CONV_OUT, tokA, 16 * C, e->conv_out_w, nullptr, resid, d, M,
+  if ((st = launch_linear_t<T>(e, ENC_K_CONV_OUT, tokA, 16 * C, WMat{e->conv_out_w}, nullptr, resid, d, M,
                                d, 16 * C, EPI_PE, s, e->pe, g.tok_pos)))
     return st;
   if (stop == ST_EMBED) return ENC_OK;
@@ -689,6 +734,7 @@ void free_all(encoder* e) {
   for (auto* b : bufs)
     if (b->p) hipFree(b->p);
   if (e->wdev) hipFree(e->wdev);
+  if (e->qdev) hipFree(e->qdev);
   if (e->fdev) hipFree(e->fdev);
   if (e->pinned) hipHostFree(e->pinned);
   if (e->upload_done) hipEventDestroy(e->upload_done);
@@ -809,15 +855,38 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
     woff += (n + 127) & ~int64_t(127);
     return o;
   };
+  // with int4 weights the linear layers, head and adapter live in the int4 buffer instead
+  const bool q4 = c.weight_bits == 4;
+  auto lslot = [&](int64_t n) { return wslot(q4 ? 0 : n); };
   const int64_t o_conv2 = wslot(C * 9 * C), o_conv3 = wslot(C * 9 * C), o_co = wslot(d * 16 * C);
   std::vector<int64_t> o_qkv, o_o, o_1, o_2;
   for (int l = 0; l < c.n_layers; ++l) {
-    o_qkv.push_back(wslot(3 * d * d));
-    o_o.push_back(wslot(d * d));
-    o_1.push_back(wslot(F * d));
-    o_2.push_back(wslot(d * F));
+    o_qkv.push_back(lslot(3 * d * d));
+    o_o.push_back(lslot(d * d));
+    o_1.push_back(lslot(F * d));
+    o_2.push_back(lslot(d * F));
   }
-  const int64_t o_p1 = wslot(d * d), o_p2 = wslot(O * d), o_gu = wslot(2 * A * O), o_dn = wslot(O * A);
+  const int64_t o_p1 = lslot(d * d), o_p2 = lslot(O * d), o_gu = lslot(2 * A * O), o_dn = lslot(O * A);
+  // ---- int4 buffer: per matrix [N][K/2] bytes then [N][K/128] bf16 scales (256-byte aligned)
+  int64_t qoff = 0;
+  struct QSlot { int64_t q = 0, s = 0; };
+  auto qslot = [&](int64_t N_, int64_t K_) {
+    QSlot r;
+    if (!q4) return r;
+    r.q = qoff;
+    qoff += ((N_ * K_ / 2) + 255) & ~int64_t(255);
+    r.s = qoff;
+    qoff += ((N_ * K_ / 128 * 2) + 255) & ~int64_t(255);
+    return r;
+  };
+  std::vector<QSlot> q_qkv, q_o, q_1, q_2;
+  for (int l = 0; l < c.n_layers; ++l) {
+    q_qkv.push_back(qslot(3 * d, d));
+    q_o.push_back(qslot(d, d));
+    q_1.push_back(qslot(F, d));
+    q_2.push_back(qslot(d, F));
+  }
+  const QSlot q_p1 = qslot(d, d), q_p2 = qslot(O, d), q_gu = qslot(2 * A, O), q_dn = qslot(O, A);
   // ---- float32 parameter buffer
   int64_t foff = 0;
   auto fslot = [&](int64_t n) {
@@ -849,9 +918,16 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
     else reinterpret_cast<float*>(wh.data())[dst_el + idx] = v;
   };
   auto copy_plain = [&](int64_t dst_el, const float* s, int64_t n) {
+    if (q4) return;  // quantised below instead
     parallel_for(n, [&](int64_t a, int64_t b) {
       for (int64_t i = a; i < b; ++i) put(dst_el, i, s[i]);
     });
+  };
+  std::vector<uint8_t> qh((size_t)qoff);
+  // rows [row0, row0 + N_) of the int4 matrix at slot qs (K_ columns), from float32 rows src
+  auto quant = [&](const QSlot& qs, int64_t row0, const float* src_rows, int64_t N_, int64_t K_) {
+    quantize_int4_rows(src_rows, N_, K_, qh.data() + qs.q + row0 * K_ / 2,
+                       reinterpret_cast<bf16_t*>(qh.data() + qs.s) + row0 * (K_ / 128));
   };
   auto fcopy = [&](int64_t dst_el, const float* s, int64_t n) {
     std::memcpy(fh.data() + dst_el, s, n * sizeof(float));
@@ -884,6 +960,14 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
     copy_plain(o_qkv[l], s[2], d * d);
     copy_plain(o_qkv[l] + d * d, s[4], d * d);
     copy_plain(o_qkv[l] + 2 * d * d, s[6], d * d);
+    if (q4) {
+      quant(q_qkv[l], 0, s[2], d, d);
+      quant(q_qkv[l], d, s[4], d, d);
+      quant(q_qkv[l], 2 * d, s[6], d, d);
+      quant(q_o[l], 0, s[8], d, d);
+      quant(q_1[l], 0, s[12], F, d);
+      quant(q_2[l], 0, s[14], d, F);
+    }
     fcopy(f_bqkv[l], s[3], d);
     fcopy(f_bqkv[l] + d, s[5], d);
     fcopy(f_bqkv[l] + 2 * d, s[7], d);
@@ -905,16 +989,31 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
   copy_plain(o_p2, h[4], O * d);
   fcopy(f_p2b, h[5], O);
   // gate/up interleaved in groups of 32 rows: [gate 32 | up 32] per 64 rows
-  parallel_for(A, [&](int64_t a0, int64_t a1) {
-    for (int64_t j = a0; j < a1; ++j) {
-      const int64_t rg = 64 * (j / 32) + (j % 32);
-      for (int64_t k = 0; k < O; ++k) {
-        put(o_gu, rg * O + k, h[6][j * O + k]);
-        put(o_gu, (rg + 32) * O + k, h[7][j * O + k]);
+  if (!q4) {
+    parallel_for(A, [&](int64_t a0, int64_t a1) {
+      for (int64_t j = a0; j < a1; ++j) {
+        const int64_t rg = 64 * (j / 32) + (j % 32);
+        for (int64_t k = 0; k < O; ++k) {
+          put(o_gu, rg * O + k, h[6][j * O + k]);
+          put(o_gu, (rg + 32) * O + k, h[7][j * O + k]);
+        }
       }
-    }
-  });
+    });
+  } else {
+    quant(q_p1, 0, h[2], d, d);
+    quant(q_p2, 0, h[4], O, d);
+    std::vector<float> gu((size_t)(2 * A * O));  // the interleaved row order, then quantised
+    parallel_for(A, [&](int64_t a0, int64_t a1) {
+      for (int64_t j = a0; j < a1; ++j) {
+        const int64_t rg = 64 * (j / 32) + (j % 32);
+        std::memcpy(gu.data() + rg * O, h[6] + j * O, O * sizeof(float));
+        std::memcpy(gu.data() + (rg + 32) * O, h[7] + j * O, O * sizeof(float));
+      }
+    });
+    quant(q_gu, 0, gu.data(), 2 * A, O);
+  }
   copy_plain(o_dn, h[8], O * A);
+  if (q4) quant(q_dn, 0, h[8], O, A);
   // tables
   {
     std::vector<float> pe = pe_table(W, (int)d);
@@ -931,6 +1030,8 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
 
   hipError_t err = hipMalloc(&e->wdev, woff * (int64_t)es);
   if (err == hipSuccess) err = hipMalloc((void**)&e->fdev, foff * 4);
+  if (err == hipSuccess && q4) err = hipMalloc((void**)&e->qdev, qoff);
+  if (err == hipSuccess && q4) err = hipMemcpy(e->qdev, qh.data(), qoff, hipMemcpyHostToDevice);
   if (err == hipSuccess) err = hipMemcpy(e->wdev, wh.data(), woff * (int64_t)es, hipMemcpyHostToDevice);
   if (err == hipSuccess) err = hipMemcpy(e->fdev, fh.data(), foff * 4, hipMemcpyHostToDevice);
   if (err == hipSuccess) err = hipEventCreateWithFlags(&e->upload_done, hipEventDisableTiming);
@@ -942,19 +1043,32 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
   }
   e->wbytes = woff * (int64_t)es;
   e->fbytes = foff * 4;
+  e->qbytes = qoff;
   auto W_ = [&](int64_t o) { return (void*)((uint8_t*)e->wdev + o * (int64_t)es); };
+  auto M_ = [&](int64_t o, const QSlot& qs) {
+    WMat m;
+    if (q4) {
+      m.q = e->qdev + qs.q;
+      m.s = reinterpret_cast<const bf16_t*>(e->qdev + qs.s);
+    } else {
+      m.w = W_(o);
+    }
+    return m;
+  };
   auto F_ = [&](int64_t o) { return e->fdev + o; };
   e->conv1_w = F_(f_c1w); e->conv1_b = F_(f_c1b); e->conv2_b = F_(f_c2b); e->conv3_b = F_(f_c3b);
   e->conv2_w = W_(o_conv2); e->conv3_w = W_(o_conv3); e->conv_out_w = W_(o_co);
   for (int l = 0; l < c.n_layers; ++l) {
     LayerW L;
-    L.wqkv = W_(o_qkv[l]); L.wo = W_(o_o[l]); L.w1 = W_(o_1[l]); L.w2 = W_(o_2[l]);
+    L.wqkv = M_(o_qkv[l], q_qkv[l]); L.wo = M_(o_o[l], q_o[l]);
+    L.w1 = M_(o_1[l], q_1[l]); L.w2 = M_(o_2[l], q_2[l]);
     L.bqkv = F_(f_bqkv[l]); L.bo = F_(f_bo[l]); L.b1 = F_(f_b1[l]); L.b2 = F_(f_b2[l]);
     L.ln1g = F_(f_l1g[l]); L.ln1b = F_(f_l1b[l]); L.ln2g = F_(f_l2g[l]); L.ln2b = F_(f_l2b[l]);
     e->layers.push_back(L);
   }
   e->lnp_g = F_(f_lpg); e->lnp_b = F_(f_lpb); e->proj1_b = F_(f_p1b); e->proj2_b = F_(f_p2b);
-  e->proj1_w = W_(o_p1); e->proj2_w = W_(o_p2); e->gateup_w = W_(o_gu); e->down_w = W_(o_dn);
+  e->proj1_w = M_(o_p1, q_p1); e->proj2_w = M_(o_p2, q_p2);
+  e->gateup_w = M_(o_gu, q_gu); e->down_w = M_(o_dn, q_dn);
   e->pe = F_(f_pe);
   e->mel.twiddle = F_(f_tw);
   e->mel.window = F_(f_win);
@@ -969,7 +1083,7 @@ void encoder_destroy(encoder* e) { free_all(e); }
 
 encoder_status encoder_memory_stats(const encoder* e, int64_t* weight_bytes, int64_t* workspace_bytes) {
   if (!e) return invalid("encoder handle is NULL");
-  if (weight_bytes) *weight_bytes = e->wbytes + e->fbytes;
+  if (weight_bytes) *weight_bytes = e->wbytes + e->fbytes + e->qbytes;
   if (workspace_bytes) *workspace_bytes = e->ws_peak;
   return ENC_OK;
 }
@@ -1178,6 +1292,29 @@ encoder_status encoder_op_linear(const void* A, const void* W, const float* bias
     err = launch_linear<float>(a, map[epi], ENC_K_OTHER, s);
   }
   if (err != hipSuccess) return hip_fail(err, "encoder_op_linear");
+  return ENC_OK;
+}
+
+encoder_status encoder_quantize_int4(const float* w, int64_t N, int64_t K, uint8_t* q,
+                                     uint16_t* scales) {
+  if (!w || !q || !scales) return invalid("w, q and scales must be non-NULL");
+  if (N < 1 || K < 128 || K % 128) return invalid("need N >= 1 and K a positive multiple of 128");
+  quantize_int4_rows(w, N, K, q, scales);
+  return ENC_OK;
+}
+
+encoder_status encoder_op_linear_int4(const void* A, const uint8_t* q, const uint16_t* scales,
+                                      const float* bias, void* C, int64_t M, int32_t N, int32_t K,
+                                      int32_t epi, void* stream) {
+  if (!A || !q || !scales || !C) return invalid("A, q, scales and C must be non-NULL");
+  if (M < 0 || N <= 0 || K < 128 || K % 128) return invalid("need M >= 0, N > 0, K % 128 == 0");
+  if (epi < 0 || epi > 3) return invalid("epi must be 0..3");
+  if (epi == 3 && N % 64) return invalid("SwiGLU needs N % 64 == 0");
+  static const int map[4] = {EPI_BIAS, EPI_BIAS_GELU, EPI_RESADD, EPI_SWIGLU};
+  const int64_t ldc = epi == 3 ? N / 2 : N;
+  LinearArgs a{A, K, nullptr, bias, C, ldc, M, N, K, nullptr, nullptr, q, (const bf16_t*)scales};
+  const hipError_t err = launch_linear<bf16_t>(a, map[epi], ENC_K_OTHER, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "encoder_op_linear_int4");
   return ENC_OK;
 }
 

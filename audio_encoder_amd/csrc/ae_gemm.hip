@@ -305,6 +305,14 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes)
 #define AE_GEMM_GROUP_M 8
 #endif
 
+// int4 weight-only B operand: q [N][K/2] bytes (two's complement nibbles, element k in byte
+// k/2, even k in the low nibble) and one bf16 scale per row per group of 128 k, s [N][K/128].
+// The kernel multiplies each weight by its scale in fp32 (exact) and rounds the product to bf16.
+struct BQuant {
+  const uint8_t* q;
+  const bf16_t* s;
+};
+
 // Direct-to-LDS variant: the tile loads are buffer_load_dwordx4 ... lds (gfx950 LDS DMA, 16
 // bytes per lane), so tile data never passes through VGPRs.  One LDS DMA instruction fills
 // 1 KB of LDS at (wave-uniform base + 16 * lane); each lane therefore fetches the global chunk
@@ -313,10 +321,14 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes)
 //   issue the DMA of the next tile into the other buffer -> MFMAs.
 // The DMA of tile kt+1 thus overlaps the MFMAs of tile kt, and the compiler's conservative
 // wait before LDS reads never falls between a DMA and the fragment reads it could delay.
-template <class TL, class AS, class OM, int EPI, typename OT, int TAG>
+// BQ: B is int4 (BQuant): each thread loads 16-byte chunks of 32 weights into registers with the
+// next tile's A DMA, and at the top of the next iteration dequantises them into the B tile (same
+// swizzled bf16 layout as the DMA path) before the barrier.
+template <class TL, class AS, class OM, int EPI, typename OT, int TAG, bool BQ = false>
 __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const bf16_t* __restrict__ Bw,
                                                                    int32_t N, int32_t K, OM om, EpiP ep,
-                                                                   int32_t n_tiles, int32_t pe_ld, int32_t gm) {
+                                                                   int32_t n_tiles, int32_t pe_ld, int32_t gm,
+                                                                   BQuant bq) {
   constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
   constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
   constexpr int SMEM = 2 * (BM + BN) * BK;
@@ -324,8 +336,11 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
   static_assert(NW * SR * (WTN + 4) * 4 <= SMEM * 2, "epilogue staging must fit in the tiles");
   constexpr int ROWS_PER_DMA = 1024 / (BK * 2);           // tile rows filled by one instruction
   constexpr int ADMA = BM / ROWS_PER_DMA / NW;            // DMA instructions per wave per tile
-  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
-  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
+  constexpr int BDMA = BQ ? 0 : BN / ROWS_PER_DMA / NW;
+  static_assert(ADMA * ROWS_PER_DMA * NW == BM && (BQ || BDMA * ROWS_PER_DMA * NW == BN), "dma split");
+  constexpr int QSEG = BK / 32;                 // 32-weight int4 chunks per tile row
+  constexpr int QCH = BN * QSEG;                // chunks per tile
+  static_assert(!BQ || QCH <= TL::NT, "one int4 chunk per thread at most");
   constexpr int KS = BK / 16;
   __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM];
   bf16_t* const sA = smem;
@@ -348,8 +363,8 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
   constexpr int CPR = BK / 8;
   typename AS::BRow arow[ADMA];
   int achunk[ADMA];
-  uint32_t boffr[BDMA];
-  int bchunk[BDMA];
+  uint32_t boffr[BDMA > 0 ? BDMA : 1];
+  int bchunk[BDMA > 0 ? BDMA : 1];
 #pragma unroll
   for (int j = 0; j < ADMA; ++j) {
     const int r = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
@@ -382,6 +397,47 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
     }
   };
 
+  // int4 B: thread tid < QCH owns tile row qr, 32-weight segment qs
+  const int qr = tid / QSEG, qs = tid % QSEG;
+  const bool qact = BQ && tid < QCH;
+  const bool qrow_ok = qact && n0 + qr < N;
+  const uint8_t* qrow = BQ ? bq.q + (int64_t)(n0 + qr) * (K / 2) : nullptr;
+  const bf16_t* srow = BQ ? bq.s + (int64_t)(n0 + qr) * (K / 128) : nullptr;
+  uint4 qv = make_uint4(0u, 0u, 0u, 0u);
+  bf16_t sv = 0;
+  auto qload = [&](int kt) {
+    if constexpr (BQ) {
+      qv = make_uint4(0u, 0u, 0u, 0u);
+      sv = 0;
+      const int k = kt * BK + qs * 32;
+      if (qrow_ok && k < K) {
+        qv = *reinterpret_cast<const uint4*>(qrow + k / 2);
+        sv = srow[k / 128];
+      }
+    }
+  };
+  auto qstore = [&](int buf) {
+    if constexpr (BQ) {
+      if (qact) {
+        const float sf = bf16_to_f32(sv);
+        const uint32_t w4[4] = {qv.x, qv.y, qv.z, qv.w};
+        bf16_t* row = sB + buf * BN * BK + qr * BK;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {  // 8 weights per word: nibble j holds weight 8c + j
+          uint32_t o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int q0 = (int)(w4[c] << (28 - 8 * i)) >> 28;
+            const int q1 = (int)(w4[c] << (24 - 8 * i)) >> 28;
+            o[i] = pack_bf16x2((float)q0 * sf, (float)q1 * sf);
+          }
+          const int lc = qs * 4 + c;
+          *reinterpret_cast<uint4*>(row + ((lc ^ swz<BK>(qr)) * 8)) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      }
+    }
+  };
+
   f32x16_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -396,9 +452,11 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
   bf16x8_t af[KS][TM], bfr[KS][TN];
   const int nk = (K + BK - 1) / BK;
   dma(0, 0);
+  qload(0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA of tile kt has landed
+    qstore(cur);                         // int4 B: dequantise tile kt into buffer cur
     __syncthreads();                     // every wave's DMA landed; buffer cur^1 is free
     const bf16_t* pa = sA + cur * BM * BK + arow0 * BK;
     const bf16_t* pb = sB + cur * BN * BK + brow0 * BK;
@@ -410,7 +468,10 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[ks][j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * BK + ch);
     }
-    if (kt + 1 < nk) dma(kt + 1, cur ^ 1);
+    if (kt + 1 < nk) {
+      dma(kt + 1, cur ^ 1);
+      qload(kt + 1);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -717,18 +778,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(AS as, const float* __res
 // dispatch
 // ============================================================================================
 // NST = 0: gemm_dtl_kernel (one tile in flight); NST >= 3: gemm_ilv_kernel with NST stages.
-template <typename T, class TL, class AS, class OM, int EPI, int TAG, int NST = 0>
+template <typename T, class TL, class AS, class OM, int EPI, int TAG, int NST = 0, bool BQ = false>
 hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, const EpiP& ep,
-               int64_t m_rows, int32_t pe_ld, hipStream_t s) {
+               int64_t m_rows, int32_t pe_ld, hipStream_t s, BQuant bq = BQuant{nullptr, nullptr}) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     const int n_tiles = (N + TL::BN - 1) / TL::BN;
     const int64_t m_tiles = (m_rows + TL::BM - 1) / TL::BM;
     if (m_tiles * n_tiles == 0) return hipSuccess;
     if (m_tiles * n_tiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    static_assert(!BQ || NST == 0, "int4 weights run in the one-stage kernel");
     if constexpr (NST == 0)
-      hipLaunchKernelGGL((gemm_dtl_kernel<TL, AS, OM, EPI, bf16_t, TAG>),
+      hipLaunchKernelGGL((gemm_dtl_kernel<TL, AS, OM, EPI, bf16_t, TAG, BQ>),
                          dim3((unsigned)(m_tiles * n_tiles)), dim3(TL::NT), 0, s, as, Bw, N, K, om, ep,
-                         n_tiles, pe_ld, AE_GEMM_GROUP_M);
+                         n_tiles, pe_ld, AE_GEMM_GROUP_M, bq);
     else
       hipLaunchKernelGGL((gemm_ilv_kernel<TL, NST, AS, OM, EPI, bf16_t, TAG>),
                          dim3((unsigned)(m_tiles * n_tiles)), dim3(TL::NT), 0, s, as, Bw, N, K, om, ep,
@@ -808,6 +870,19 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
   EpiP ep{a.bias, a.C, a.pe, a.tok_pos};
   const T* Bw = reinterpret_cast<const T*>(a.W);
   const int pe_ld = EPI == EPI_PE ? a.N : 0;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (a.Wq) {
+      if (a.K % 128 != 0 || !a.Ws) return hipErrorInvalidValue;
+      const BQuant bq{a.Wq, a.Ws};
+      if (lin_kind(a.M, a.N, a.K) == LinKind::Narrow)
+        return run<T, TileNarrow, ALinear<T>, OLinear, EPI, TAG, 0, true>(as, Bw, a.N, a.K, om, ep, a.M,
+                                                                         pe_ld, s, bq);
+      return run<T, TileWide, ALinear<T>, OLinear, EPI, TAG, 0, true>(as, Bw, a.N, a.K, om, ep, a.M,
+                                                                     pe_ld, s, bq);
+    }
+  } else {
+    if (a.Wq) return hipErrorInvalidValue;
+  }
   switch (lin_kind(a.M, a.N, a.K)) {
     case LinKind::Large:
       return run<T, TileLarge, ALinear<T>, OLinear, EPI, TAG, 4>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);

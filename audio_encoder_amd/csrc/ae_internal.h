@@ -148,6 +148,8 @@ struct LinearArgs {
   int64_t M; int32_t N; int32_t K;
   // EPI_PE: pe table [window tokens][N] and each row's position within its window
   const float* pe; const int32_t* tok_pos;
+  // int4 weight-only B (bf16 path, K % 128 == 0): W is then unused; q [N][K/2], s [N][K/128]
+  const uint8_t* Wq = nullptr; const bf16_t* Ws = nullptr;
 };
 template <typename T>
 hipError_t launch_linear(const LinearArgs& a, int epi, int tag, hipStream_t s);

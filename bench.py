@@ -117,13 +117,15 @@ def measured_traffic(role: str, cfg_note: str = "full-size tower, 16 x 30 s clip
     return round(t["fetch_bytes"] + t["write_bytes"])
 
 
-def cpu_baseline(pcm, weights, cfg, max_windows: int = 24) -> dict:
+def cpu_baseline(pcm, weights, cfg, max_windows: int = 24, int4: bool = False) -> dict:
     """The float64 oracle on the first `max_windows` 8 s windows of the batch (clip by clip;
     about 10-30 s of CPU work), scaled to audio-seconds per second."""
     import numpy as np
 
     import oracle as O
     Wt = O.unpack_weights(weights, O.FULL)
+    if int4:
+        Wt = O.int4_weights(Wt, O.FULL)
     W = cfg["window_tokens"]
     t0 = time.perf_counter()
     frames = nwin = clips = 0
@@ -153,6 +155,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weight-bits", type=int, default=16, choices=(16, 4),
+                    help="4: int4 weight-only linear layers, head and adapter (dequantised in the "
+                         "GEMM loader); the CPU baseline then runs on the dequantised weights")
     ap.add_argument("--roofline-steps", type=int, default=3)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the run, launch one plain device copy of this many MiB (a "
@@ -170,7 +175,7 @@ def main():
     from audio_encoder_amd import binding as B
     from audio_encoder_amd import synth as S
 
-    cfg = dict(B.FULL)
+    cfg = dict(B.FULL, weight_bits=args.weight_bits)
     log("generating weights and input")
     weights = S.make_weights(cfg, seed=0)
     pcm_np, audio_s = make_input(args.workload)
@@ -245,7 +250,7 @@ def main():
         log("timing the CPU oracle")
         clips = ([pcm_np[o:o + n] for o, n in zip(np.cumsum([0] + lengths[:-1]), lengths)]
                  if ragged else list(pcm_np))
-        cpu = cpu_baseline(clips, weights, cfg)
+        cpu = cpu_baseline(clips, weights, cfg, int4=args.weight_bits == 4)
         log(f"oracle: {cpu['value']:.2f} audio-s/s on {cpu['cores']} cores")
 
     wbytes, ws = enc.memory_stats()
@@ -260,7 +265,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if args.weight_bits == 16 else "bf16 (int4 weights)",
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload], "clips": int(n_clips),
                    "samples_per_clip": int(n_samples) if not ragged else lengths,

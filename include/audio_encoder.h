@@ -81,6 +81,11 @@ typedef struct {
   float ln_eps;
   int64_t max_tokens_per_pass; /* bounds the activation workspace; larger inputs run in several
                                   window-aligned passes.  0 selects 8192.                    */
+  int32_t weight_bits;    /* 16 (or 0): weights in dtype.  4: int4 weight-only for the layer
+                             linears, head and adapter (encoder_quantize_int4 at create; "to_4bit"
+                             of the "SILVERTHRONE/Ossicle-4B" card), dequantised to bf16 in the
+                             GEMM loader; needs ENC_BF16 and d_model, d_ffn, d_out, d_adapter
+                             multiples of 128.  Convs and conv_out stay in dtype.           */
 } encoder_cfg;
 
 typedef struct encoder encoder; /* opaque handle */
@@ -243,6 +248,21 @@ ENC_API encoder_status encoder_op_linear(const void* A, const void* W, const flo
 /* Windowed attention.  qkv device [ntok, 3*n_heads*64] (q | k | v, head h = columns 64h..64h+63
  * of each part), windows device int32 [n_windows, 2] = {first token, length <= 128}.  out device
  * [ntok, n_heads*64].  Softmax in float32. */
+/* int4 weight-only quantisation of a float32 [N, K] weight (host; K % 128 == 0): per row and
+ * group of 128 inputs, scale s = bf16(max |w| / 7) and q = clamp(rint(w / s), -8, 7) (0 for an
+ * all-zero group); q packed two per byte [N, K/2] (even k in the low nibble, two's complement),
+ * scales bf16 bit patterns [N, K/128].  The GPU multiplies q by s in fp32 (exact) and rounds the
+ * weight to bf16.  Storage for the "to_4bit" option of the "SILVERTHRONE/Ossicle-4B" card
+ * (round-to-nearest, groups of 128). */
+ENC_API encoder_status encoder_quantize_int4(const float* w, int64_t N, int64_t K, uint8_t* q,
+                                     uint16_t* scales);
+
+/* encoder_op_linear with int4 weights (q, scales from encoder_quantize_int4, on the device) and
+ * bf16 A / C; K % 128 == 0. */
+ENC_API encoder_status encoder_op_linear_int4(const void* A, const uint8_t* q, const uint16_t* scales,
+                                      const float* bias, void* C, int64_t M, int32_t N, int32_t K,
+                                      int32_t epi, void* stream);
+
 ENC_API encoder_status encoder_op_attention(const void* qkv, const int32_t* windows, int32_t n_windows,
                                     int32_t n_heads, int64_t ntok, void* out, int32_t dtype,
                                     void* stream);

@@ -504,6 +504,55 @@ def condition_audio(x: np.ndarray, fs: int) -> np.ndarray:
     return resample_to_16k(downmix(x), fs)
 
 
+# ---- int4 weight-only (card O: to_4bit, round to nearest; groups of 128; R32) -----------------
+def bf16(x) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def quantize_int4(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """[N, K] (K a multiple of 128) -> (q int8 [N, K] in [-8, 7], s float32 [N, K/128]).
+    Per row and group of 128 inputs: s = bf16(float32(max |w| / 7)), q = clip(rint(w / s), -8, 7)
+    (q = 0 where s = 0)."""
+    w = np.asarray(w, dtype=np.float64)
+    N, K = w.shape
+    g = w.reshape(N, K // 128, 128)
+    s = bf16((np.abs(g).max(axis=2) / 7.0).astype(np.float32))
+    sd = s.astype(np.float64)[:, :, None]
+    q = np.where(sd > 0, np.clip(np.rint(g / np.where(sd > 0, sd, 1.0)), -8, 7), 0.0)
+    return q.reshape(N, K).astype(np.int8), s
+
+
+def dequant_int4(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """The weight the GPU multiplies with: bf16(q * s) (the product is exact in float32)."""
+    N, K = q.shape
+    prod = (q.reshape(N, K // 128, 128).astype(np.float32) * s[:, :, None]).reshape(N, K)
+    return bf16(prod).astype(np.float64)
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """Two weights per byte, even k in the low nibble (two's complement)."""
+    u = (q.astype(np.int16) & 0xF).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+INT4_MATRICES = ("q.w", "k.w", "v.w", "o.w", "fc1.w", "fc2.w")
+INT4_HEAD = ("proj1.w", "proj2.w", "gate.w", "up.w", "down.w")
+
+
+def int4_weights(Wt: dict, cfg: dict) -> dict:
+    """The weights of an int4 configuration: every layer linear, the head projections and the
+    adapter replaced by their dequantised int4 versions; convs, conv_out, biases and norms as
+    they are."""
+    out = dict(Wt)
+    names = [f"layers.{i}.{m}" for i in range(cfg["n_layers"]) for m in INT4_MATRICES]
+    for name in names + list(INT4_HEAD):
+        out[name] = dequant_int4(*quantize_int4(Wt[name]))
+    return out
+
+
 def splice(table: np.ndarray, positions, frames: np.ndarray) -> tuple[np.ndarray, int]:
     """Audio injection (card T, "Architecture", row "Audio injection"): the embedding rows at
     the audio placeholder positions are replaced by the adapter frames, in order.  Returns the

@@ -117,6 +117,49 @@ def test_op_linear(M, N, K, epi, dtype):
         assert np.all(err <= 2 ** -8 * np.abs(ref) + 1e-4 * scale), err.max()
 
 
+INT4_SHAPES = [(130, 256, 128), (300, 1280, 1280), (333, 2560, 1024), (77, 4096, 2048),
+               (7000, 1280, 1280), (65, 1024, 5120)]
+
+
+@pytest.mark.parametrize("M,N,K", INT4_SHAPES)
+@pytest.mark.parametrize("epi", [0, 1, 2, 3])
+def test_op_linear_int4(M, N, K, epi):
+    if epi == 3 and N % 64:
+        pytest.skip("SwiGLU needs N % 64 == 0")
+    rng = np.random.default_rng(M + N + K + epi)
+    A = bf16_round(rng.standard_normal((M, K)).astype(np.float32))
+    W = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    q, sc = B.encoder_quantize_int4(W)
+    Wd = O.dequant_int4(*O.quantize_int4(W))
+    acc = A.astype(np.float64) @ Wd.T
+    qd = torch.from_numpy(q).to(DEV)
+    sd = torch.from_numpy(sc.view(np.int16)).to(DEV)
+    if epi == 3:
+        cols = np.arange(N // 2)
+        ref = O.silu(acc[:, 64 * (cols // 32) + cols % 32]) * acc[:, 64 * (cols // 32) + 32 + cols % 32]
+        C = torch.zeros((M, N // 2), dtype=torch.bfloat16, device=DEV)
+        B.op_linear_int4(to_dev(A, torch.bfloat16), qd, sd, None, C, 3)
+    elif epi == 2:
+        C0 = rng.standard_normal((M, N)).astype(np.float32)
+        ref = C0 + acc + bias
+        C = to_dev(C0)
+        B.op_linear_int4(to_dev(A, torch.bfloat16), qd, sd, to_dev(bias), C, 2)
+    else:
+        ref = acc + bias
+        if epi == 1:
+            ref = O.gelu(ref)
+        C = torch.zeros((M, N), dtype=torch.bfloat16, device=DEV)
+        B.op_linear_int4(to_dev(A, torch.bfloat16), qd, sd, to_dev(bias), C, epi)
+    got = C.float().cpu().numpy()
+    scale = np.sqrt(np.mean(ref ** 2)) + 1e-30
+    err = np.abs(got - ref)
+    if epi == 2:
+        assert err.max() <= 2e-5 * scale * max(1.0, np.sqrt(K / 64)), err.max()
+    else:
+        assert np.all(err <= 2 ** -8 * np.abs(ref) + 1e-4 * scale), err.max()
+
+
 def attention_case(lengths, d, rng):
     ntok = int(sum(lengths))
     qkv = rng.standard_normal((ntok, 3 * d)).astype(np.float32)
@@ -377,6 +420,23 @@ def test_conditioned_clip_encodes_like_the_16k_clip(tiny):
     assert torch.equal(enc.forward(y[None]), enc.forward(x[None]))
 
 
+def test_tiny_int4_tower_matches_oracle_on_dequantised_weights():
+    cfg = dict(B.TINY, dtype="bf16", weight_bits=4)
+    w = S.make_weights(cfg, seed=0)
+    enc = B.Encoder(w, cfg)
+    Wt4 = O.int4_weights(O.unpack_weights(w, O.TINY), O.TINY)
+    for n in (64000, 53920):
+        x = S.mixed_clip(330, n)
+        got = enc.forward(to_dev(x[None])).float().cpu().numpy()[0]
+        ref = O.encode(x, Wt4, O.TINY)
+        check_bf16(got, ref, f"tiny int4 {n}")
+    wbytes, _ = enc.memory_stats()
+    enc16 = B.Encoder(w, dict(B.TINY, dtype="bf16"))
+    assert wbytes < enc16.memory_stats()[0]
+    enc.close()
+    enc16.close()
+
+
 def test_tiny_deterministic(tiny):
     enc, _ = tiny
     pcm = to_dev(S.mixed_batch([1, 2], 64000))
@@ -494,6 +554,24 @@ def test_full_ragged_equals_single_clips(full):
     res, _ = oracle_windows(clips[1], Wt, O.FULL, [0])
     tok, yref, _ = res[0]
     check_bf16(g[F[0] + tok:F[0] + tok + yref.shape[0]], yref, "ragged clip 1 window 0")
+
+
+def test_full_int4_window_matches_oracle(full):
+    _, Wt = full
+    cfg = dict(B.FULL, weight_bits=4)
+    log("int4: creating encoder")
+    enc = B.Encoder(S.make_weights(cfg, seed=0), cfg)
+    wbytes, _ = enc.memory_stats()
+    log(f"int4 weights: {wbytes / 1e9:.3f} GB")
+    assert wbytes < 0.45e9
+    x = S.pink_plus_bursts(seed=1)
+    got = enc.forward(to_dev(x[None])).float().cpu().numpy()[0]
+    enc.close()
+    log("int4: quantising the oracle's weights")
+    Wt4 = O.int4_weights(Wt, O.FULL)
+    res, _ = oracle_windows(x, Wt4, O.FULL, [1])
+    tok, yref, _ = res[0]
+    check_bf16(got[tok:tok + yref.shape[0]], yref, "int4 C1 window 1")
 
 
 def test_full_c4_hour_stream(full):

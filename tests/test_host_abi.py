@@ -127,6 +127,25 @@ def test_conditioning_rejects_unsupported_rates(fs):
     assert ei.value.status in (B.ENC_E_UNSUPPORTED, B.ENC_E_INVALID_ARG)
 
 
+@pytest.mark.parametrize("N,K", [(3, 128), (37, 1280), (64, 2048)])
+def test_library_int4_quantiser_is_bit_exact_with_oracle(N, K):
+    rng = np.random.default_rng(N + K)
+    w = (rng.standard_normal((N, K)) * rng.uniform(0.001, 0.1, size=(N, 1))).astype(np.float32)
+    w[0, :128] = 0.0
+    w[-1, -128:] *= 1e4
+    q, sc = B.encoder_quantize_int4(w)
+    q0, s0 = O.quantize_int4(w)
+    assert np.array_equal(q, O.pack_int4(q0))
+    assert np.array_equal(sc, s0.view(np.uint32) >> 16)
+
+
+def test_int4_config_checks():
+    assert B.encoder_validate_cfg(dict(B.FULL, weight_bits=4)) == B.ENC_OK
+    assert B.encoder_validate_cfg(dict(B.TINY, weight_bits=4)) == B.ENC_E_INVALID_ARG  # fp32
+    assert B.encoder_validate_cfg(dict(B.TINY, dtype="bf16", weight_bits=4)) == B.ENC_OK
+    assert B.encoder_validate_cfg(dict(B.FULL, weight_bits=8)) == B.ENC_E_INVALID_ARG
+
+
 def test_plan_of_hour_stream_has_45000_tokens():
     tab = B.encoder_plan_windows(B.FULL, 57_600_000, 1)
     assert len(tab) == 450 and tab[:, 5].sum() == 45000

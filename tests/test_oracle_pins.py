@@ -606,3 +606,40 @@ def test_conditioned_length():
     assert O.conditioned_length(44101, 44100) == 16001  # ceil
     assert O.conditioned_length(3, 48000) == 1
     assert O.conditioned_length(1000, 8000) == 2000
+
+
+# ---- int4 weight-only (R32) ---------------------------------------------------------------------
+def test_int4_quantiser_recovers_representable_weights():
+    rng = np.random.default_rng(12)
+    N, K = 6, 512
+    s0 = O.bf16(rng.uniform(0.001, 0.05, size=(N, K // 128)).astype(np.float32))
+    q0 = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    q0.reshape(N, K // 128, 128)[:, :, 5] = 7  # every group reaches |q| = 7
+    w = (q0.reshape(N, K // 128, 128) * s0[:, :, None].astype(np.float64)).reshape(N, K)
+    q, s = O.quantize_int4(w)
+    assert np.array_equal(q, q0) and np.array_equal(s, s0)
+    np.testing.assert_array_equal(O.dequant_int4(q, s), O.bf16(w.astype(np.float32)))
+
+
+def test_int4_error_is_half_a_step_plus_bf16_rounding():
+    rng = np.random.default_rng(13)
+    w = rng.standard_normal((16, 1024)) * 0.02
+    w[3, 128:256] = 0.0  # an all-zero group: scale 0, weights 0
+    q, s = O.quantize_int4(w)
+    assert q.min() >= -8 and q.max() <= 7
+    assert s[3, 1] == 0 and not q[3, 128:256].any()
+    err = np.abs(O.dequant_int4(q, s) - w)
+    step = np.repeat(s.astype(np.float64), 128, axis=1)
+    assert np.all(err <= 0.5 * step * (1 + 2 ** -7) + np.abs(w) * 2 ** -8 + 1e-30)
+
+
+def test_int4_packing_order():
+    q = np.array([[1, -2, 7, -8, 0, -1, 3, 4]], dtype=np.int8)
+    assert list(O.pack_int4(q)[0]) == [0xE1, 0x87, 0xF0, 0x43]
+
+
+def test_int4_weights_touch_only_the_linear_matrices(tiny_weights):
+    W4 = O.int4_weights(tiny_weights, O.TINY)
+    for k, v in tiny_weights.items():
+        quantised = k.endswith(O.INT4_MATRICES) or k in O.INT4_HEAD
+        assert np.array_equal(W4[k], v) != quantised or not v.any(), k
