@@ -228,62 +228,113 @@ __device__ inline TileCoord tile_coord(int n_tiles, int gm) {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// Epilogue of SR staged accumulator rows (row-major, stride LDW floats) of one wave: rows
-// rbase.., columns wcol..wcol+WTN-1.  Each lane handles 4 consecutive columns per step.
-template <int EPI, typename OT, int WTN, int SR, class OM>
-__device__ inline void epilogue_rows(const float* stg, int LDW, int64_t rbase, int wcol, int N,
-                                     const OM& om, const EpiP& ep, int pe_ld, int lane) {
-    if constexpr (EPI == EPI_SWIGLU) {
-    constexpr int Q = WTN / 8;  // 4-wide outputs per row
-    for (int idx = lane; idx < SR * Q; idx += 64) {
-      const int r = idx / Q, q4 = idx - (idx / Q) * Q;
-      const int p = (4 * q4) / 32, jj = (4 * q4) % 32;
-      if (wcol + 64 * p >= N) continue;
-      const int64_t off = om.off(rbase + r);
-      if (off < 0) continue;
-      const float4 g = *reinterpret_cast<const float4*>(stg + r * LDW + 64 * p + jj);
-      const float4 u = *reinterpret_cast<const float4*>(stg + r * LDW + 64 * p + 32 + jj);
-      const int col = (wcol + 64 * p) / 2 + jj;
-      OT* dst = reinterpret_cast<OT*>(ep.C) + off + col;
-      Store4x<OT>::put(dst, silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w);
+// Compiler-only barrier: no LDS access moves across it, and unlike __syncthreads() it adds
+// no release fence (which would wait for every LDS DMA in flight, deeper stages included).
+__device__ inline void cbar() { asm volatile("" ::: "memory"); }
+
+// Epilogue of one wave.  Its TM x TN accumulator blocks (32x32 each; tile rows rbase0..,
+// columns wcol..wcol+WTN-1) pass through the wave's own SR staging rows in LDS (stride WTN + 4
+// floats), SR rows per round, and leave as 16-byte (fp32) or 8-byte (bf16) row pieces: each lane
+// owns 4 consecutive columns of every (64 / (WTN / 4))-th staged row.
+//
+// Ordering.  The staging rows belong to this wave alone and a wave's LDS accesses execute in
+// order, so compiler fences are all the ordering the staging needs (a workgroup barrier would
+// also wait for the wave's outstanding stores).  Global stores and loads share one in-order
+// completion counter here, so a load issued after a store cannot be waited for without waiting
+// for the store: the bias is loaded once up front, and everything a round reads from global
+// memory (its output row offsets, which may read the window table, and the residual of the
+// fp32 update) is loaded one round ahead, before the stores of the current round.
+template <int EPI, typename OT, int TM, int TN, int WTN, int SR, class OM>
+__device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16_t (&acc)[TM][TN], float* stg,
+                                                                   int64_t rbase0, int wcol, int N, const OM& om,
+                                                                   const EpiP& ep, int pe_ld, int lane) {
+  constexpr int LDW = WTN + 4;
+  constexpr int HS = 32 / SR;       // rounds per 32-row block
+  constexpr int ROUNDS = TM * HS;
+  constexpr bool GATE = EPI == EPI_SWIGLU;
+  constexpr int Q = GATE ? WTN / 8 : WTN / 4;  // lanes per staged row
+  constexpr int RPI = 64 / Q;                   // staged rows per 64 lanes
+  constexpr int T = SR / RPI;                   // rows per lane per round
+  static_assert(RPI * Q == 64 && T * RPI == SR, "epilogue lane map");
+  const int l32 = lane & 31, half = lane >> 5;
+  const int q4 = lane % Q, rs = lane / Q;
+  // gate: (gate, up) pairs of 32 columns interleaved in 64-column groups; the output column is
+  // half the group's start plus the position within the pair
+  const int gp = GATE ? (4 * q4) / 32 : 0, gj = GATE ? (4 * q4) % 32 : 0;
+  const int scol = GATE ? 64 * gp + gj : 4 * q4;          // staged column
+  const int col = GATE ? (wcol + 64 * gp) / 2 + gj : wcol + 4 * q4;  // output column
+  const bool colok = GATE ? wcol + 64 * gp < N : col < N;
+  float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (EPI != EPI_PE && !GATE)
+    if (ep.bias && colok) bv = *reinterpret_cast<const float4*>(ep.bias + col);
+
+  auto row_of = [&](int rd, int t) -> int64_t { return rbase0 + (rd / HS) * 32 + (rd % HS) * SR + rs + RPI * t; };
+  int64_t offn[T];
+  float4 resn[T];
+  auto prefetch = [&](int rd) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      offn[t] = colok ? om.off(row_of(rd, t)) : -1;
+      if constexpr (EPI == EPI_RESADD)
+        resn[t] = offn[t] >= 0 ? *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(ep.C) + offn[t] + col)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-  } else {
-    constexpr int Q = WTN / 4;
-    for (int idx = lane; idx < SR * Q; idx += 64) {
-      const int r = idx / Q, q4 = idx - (idx / Q) * Q;
-      const int col = wcol + 4 * q4;
-      if (col >= N) continue;
-      const int64_t row = rbase + r;
-      const int64_t off = om.off(row);
-      if (off < 0) continue;
-      float4 a = *reinterpret_cast<const float4*>(stg + r * LDW + 4 * q4);
-      if constexpr (EPI == EPI_PE) {
-        const float4 pe = *reinterpret_cast<const float4*>(ep.pe + (int64_t)ep.tok_pos[row] * pe_ld + col);
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col) =
-            make_float4(a.x + pe.x, a.y + pe.y, a.z + pe.z, a.w + pe.w);
+  };
+  prefetch(0);
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    const int i = rd / HS, hs = rd % HS;
+    cbar();  // the previous round's staging reads are issued before these writes
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
+        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
+      }
+    cbar();
+    float4 a[T], g2[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      a[t] = *reinterpret_cast<const float4*>(stg + (rs + RPI * t) * LDW + scol);
+      if constexpr (GATE) g2[t] = *reinterpret_cast<const float4*>(stg + (rs + RPI * t) * LDW + scol + 32);
+    }
+    int64_t off[T];
+    float4 res[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      off[t] = offn[t];
+      res[t] = resn[t];
+    }
+    if (rd + 1 < ROUNDS) prefetch(rd + 1);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (off[t] < 0) continue;
+      float4 x = a[t];
+      if constexpr (GATE) {
+        Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off[t] + col, silu(x.x) * g2[t].x, silu(x.y) * g2[t].y,
+                         silu(x.z) * g2[t].z, silu(x.w) * g2[t].w);
+      } else if constexpr (EPI == EPI_PE) {
+        const float4 pe = *reinterpret_cast<const float4*>(ep.pe + (int64_t)ep.tok_pos[row_of(rd, t)] * pe_ld + col);
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off[t] + col) =
+            make_float4(x.x + pe.x, x.y + pe.y, x.z + pe.z, x.w + pe.w);
       } else {
-        if (ep.bias) {
-          const float4 b = *reinterpret_cast<const float4*>(ep.bias + col);
-          a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-        }
+        x.x += bv.x; x.y += bv.y; x.z += bv.z; x.w += bv.w;
         if constexpr (EPI == EPI_RESADD) {
-          float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col);
-          const float4 o = *p;
-          *p = make_float4(o.x + a.x, o.y + a.y, o.z + a.z, o.w + a.w);
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off[t] + col) =
+              make_float4(res[t].x + x.x, res[t].y + x.y, res[t].z + x.z, res[t].w + x.w);
         } else if constexpr (EPI == EPI_STORE_F32) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off + col) = a;
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off[t] + col) = x;
         } else {
           if constexpr (EPI == EPI_BIAS_GELU) {
-            a.x = gelu_erf(a.x); a.y = gelu_erf(a.y); a.z = gelu_erf(a.z); a.w = gelu_erf(a.w);
+            x.x = gelu_erf(x.x); x.y = gelu_erf(x.y); x.z = gelu_erf(x.z); x.w = gelu_erf(x.w);
           }
-          Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off + col, a.x, a.y, a.z, a.w);
+          Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off[t] + col, x.x, x.y, x.z, x.w);
         }
       }
     }
   }
 }
-
-
 
 // LDS tile rows are BK*2 bytes.  The 16-byte chunk index is XORed with a row hash so that 16
 // consecutive rows at one logical chunk cover all 64 banks: for 128-byte rows (BK 64) the row
@@ -480,33 +531,12 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
   }
-  __syncthreads();
+  __syncthreads();  // every wave is done with the tiles; the LDS is reused for staging
 
-  constexpr int LDW = WTN + 4;
-  float* stg = reinterpret_cast<float*>(smem) + wv * SR * LDW;
-  const int wcol = n0 + wn * TL::WTN;
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-  for (int hs = 0; hs < 32 / SR; ++hs) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
-        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
-      }
-    __syncthreads();
-    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
-    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
-    __syncthreads();
-  }
-  }
+  wave_epilogue<EPI, OT, TM, TN, WTN, SR>(acc, reinterpret_cast<float*>(smem) + wv * SR * (WTN + 4),
+                                          m0 + wm * TL::WTM, n0 + wn * TL::WTN, N, om, ep, pe_ld, lane);
 }
 
-// Compiler-only barrier: no LDS access moves across it, and unlike __syncthreads() it adds
-// no release fence (which would wait for every LDS DMA in flight, deeper stages included).
-__device__ inline void cbar() { asm volatile("" ::: "memory"); }
 
 // s_waitcnt vmcnt(VM) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
 // vmcnt[5:4] in bits 15:14)
@@ -678,26 +708,8 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
   wait_vm_lds0<0>();  // the trailing zero-fill DMAs land before the stages are reused
   __syncthreads();
 
-  constexpr int LDW = WTN + 4;
-  float* stg = reinterpret_cast<float*>(st0) + wv * SR * LDW;
-  const int wcol = n0 + wn * TL::WTN;
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-  for (int hs = 0; hs < 32 / SR; ++hs) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * half + (v & 3) - hs * SR;
-        if (r >= 0 && r < SR) stg[r * LDW + 32 * j + l32] = acc[i][j][v];
-      }
-    __syncthreads();
-    const int64_t rbase = m0 + wm * TL::WTM + i * 32 + hs * SR;
-    epilogue_rows<EPI, OT, WTN, SR>(stg, LDW, rbase, wcol, N, om, ep, pe_ld, lane);
-    __syncthreads();
-  }
-  }
+  wave_epilogue<EPI, OT, TM, TN, WTN, SR>(acc, reinterpret_cast<float*>(st0) + wv * SR * (WTN + 4),
+                                          m0 + wm * TL::WTM, n0 + wn * TL::WTN, N, om, ep, pe_ld, lane);
 }
 
 // ============================================================================================

@@ -50,8 +50,9 @@ template <> struct StoreT<bf16_t> {
 // Exact-form GELU x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)).  erfc(z) for z >= 0 is evaluated
 // with Abramowitz & Stegun's formula 7.1.28, erfc(z) ~ (1 + a1 z + ... + a6 z^6)^-16
 // (|error in erf| <= 3e-7; <= 2e-6 when evaluated in fp32): six FMAs, four squarings and one
-// reciprocal, no exponential.  The negative branch uses erfc directly, so the left tail does
-// not cancel 1 + erf; |GELU error| <= 1e-6 everywhere.
+// hardware reciprocal (v_rcp_f32, 1 ulp; a correctly rounded division would cost ten
+// instructions and buy nothing at this error), no exponential.  The negative branch uses erfc
+// directly, so the left tail does not cancel 1 + erf; |GELU error| <= 1e-6 everywhere.
 __device__ inline float gelu_erf(float x) {
   const float z = fabsf(x) * 0.70710678118654752f;
   float p = fmaf(z, 0.0000430638f, 0.0002765672f);
@@ -64,7 +65,7 @@ __device__ inline float gelu_erf(float x) {
   p *= p;
   p *= p;
   p *= p;
-  const float erfc_z = __frcp_rn(p);
+  const float erfc_z = __builtin_amdgcn_rcpf(p);
   const float hx = 0.5f * x;
   return x >= 0.0f ? fmaf(-hx, erfc_z, x) : hx * erfc_z;
 }
