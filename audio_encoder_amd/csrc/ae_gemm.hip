@@ -53,7 +53,7 @@ struct ALinear {
   __device__ uint32_t boff(const BRow& x, const KC& c) const {
     return c.ok ? x.off + (uint32_t)(c.k * (int)sizeof(T)) : 0x80000000u;
   }
-  __device__ int64_t bytes() const { return M * lda * (int64_t)sizeof(T); }
+  __host__ __device__ int64_t bytes() const { return M * lda * (int64_t)sizeof(T); }
   __device__ const void* base() const { return A; }
 };
 
@@ -120,7 +120,7 @@ struct AConv {
   __device__ uint32_t boff(const BRow& x, const KC& c) const {
     return (c.ok && (x.mask & c.bit)) ? (uint32_t)((x.off + c.toff) * (int)sizeof(T)) : 0x80000000u;
   }
-  __device__ int64_t bytes() const { return (int64_t)wins_bytes; }
+  __host__ __device__ int64_t bytes() const { return (int64_t)wins_bytes; }
   __device__ const void* base() const { return in; }
   int64_t wins_bytes;  // bytes of the input activation
 };
@@ -130,22 +130,62 @@ struct AConv {
 // ============================================================================================
 struct OLinear {
   int64_t M, ldc;
-  __device__ int64_t off(int64_t r) const { return r < M ? r * ldc : -1; }
+  struct Ctx {};
+  __device__ Ctx ctx(int64_t) const { return Ctx{}; }
+  __device__ int64_t off(const Ctx&, int64_t r) const { return r < M ? r * ldc : -1; }
+  __device__ int64_t off_row(int64_t r) const { return r < M ? r * ldc : -1; }
 };
 
+template <int LEVEL, bool SPAN2>
 struct OConv {
   const Win* wins;
-  int32_t rows_per_win, Fout, C, level, Lout_max;
-  int64_t m_rows;
-  __device__ int64_t off(int64_t r) const {
-    if (r >= m_rows) return -1;
-    const int w = (int)(r / rows_per_win);
-    const int loc = (int)(r - (int64_t)w * rows_per_win);
+  int32_t rows_per_win, Fout, C, Lout_max;
+  int64_t m_rows;  // < 2^31
+  // SPAN2: a window has at least as many rows as one wave's share of a tile, so the rows of a
+  // wave lie in two windows at most; their two table entries are read once per wave with
+  // scalar loads (which do not wait behind the wave's stores).  Otherwise each row reads its
+  // own entry.  Straight-line code either way (rows outside the output are rejected by the
+  // final select), so that the epilogue's loads and stores are not split by branches.
+  struct Ctx { int w0; Win a, b; };
+  __device__ Ctx ctx(int64_t r0) const {
+    Ctx c{};
+    if constexpr (SPAN2) {
+      const int n_win = (int)(m_rows / rows_per_win);
+      const int w0 = __builtin_amdgcn_readfirstlane((int)((r0 < m_rows ? r0 : m_rows - 1) / rows_per_win));
+      c.w0 = w0;
+      c.a = wins[w0];
+      c.b = wins[w0 + 1 < n_win ? w0 + 1 : w0];
+    }
+    return c;
+  }
+  __device__ int64_t off(const Ctx& c, int64_t r) const {
+    const bool inr = r < m_rows;
+    int w, loc;
+    Win wn;
+    if constexpr (SPAN2) {
+      const int d = inr ? (int)(r - (int64_t)c.w0 * rows_per_win) : 0;
+      const bool second = d >= rows_per_win;
+      w = c.w0 + (second ? 1 : 0);
+      loc = second ? d - rows_per_win : d;
+      wn.L2 = second ? c.b.L2 : c.a.L2;
+      wn.L3 = second ? c.b.L3 : c.a.L3;
+      wn.tok = second ? c.b.tok : c.a.tok;
+    } else {
+      const int rr = inr ? (int)r : 0;
+      w = rr / rows_per_win;
+      loc = rr - w * rows_per_win;
+      wn = wins[w];
+    }
     const int t = loc / Fout, f = loc - (loc / Fout) * Fout;
-    const Win wn = wins[w];
-    if (t >= (level == 2 ? wn.L2 : wn.L3)) return -1;
-    if (level == 2) return (((int64_t)w * Lout_max + t) * Fout + f) * C;
-    return ((int64_t)(wn.tok + t) * Fout + f) * C;  // token rows [tok][16][C]
+    int64_t o;
+    if constexpr (LEVEL == 2) o = (((int64_t)w * Lout_max + t) * Fout + f) * C;
+    else o = ((int64_t)(wn.tok + t) * Fout + f) * C;  // token rows [tok][16][C]
+    return (inr && t < (LEVEL == 2 ? wn.L2 : wn.L3)) ? o : -1;
+  }
+  // any row, its own table entry (fp32 path)
+  __device__ int64_t off_row(int64_t r) const {
+    const OConv<LEVEL, false> o{wins, rows_per_win, Fout, C, Lout_max, m_rows};
+    return o.off(typename OConv<LEVEL, false>::Ctx{}, r);
   }
 };
 
@@ -154,21 +194,7 @@ struct EpiP {
   void* C;
   const float* pe;
   const int32_t* tok_pos;
-};
-
-template <typename T> struct Store4x;
-template <> struct Store4x<bf16_t> {
-  __device__ static inline void put(bf16_t* p, float a, float b, float c, float d) {
-    uint2 o;
-    o.x = pack_bf16x2(a, b);
-    o.y = pack_bf16x2(c, d);
-    *reinterpret_cast<uint2*>(p) = o;
-  }
-};
-template <> struct Store4x<float> {
-  __device__ static inline void put(float* p, float a, float b, float c, float d) {
-    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-  }
+  int64_t c_bytes;  // extent of C in bytes (buffer-store range; < 2^31)
 };
 
 template <int EPI, typename OT>
@@ -228,6 +254,14 @@ __device__ inline TileCoord tile_coord(int n_tiles, int gm) {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  // raw buffer: stride 0, range check against `bytes`; dword3 0x00020000 (32-bit data format)
+  // integer clamp (a 64-bit min lowers to a vector f64 op here, which would drag the whole
+  // descriptor into vector registers and wrap every buffer load in a waterfall loop)
+  const int n = __builtin_amdgcn_readfirstlane(bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+
 // Compiler-only barrier: no LDS access moves across it, and unlike __syncthreads() it adds
 // no release fence (which would wait for every LDS DMA in flight, deeper stages included).
 __device__ inline void cbar() { asm volatile("" ::: "memory"); }
@@ -248,14 +282,19 @@ template <int EPI, typename OT, int TM, int TN, int WTN, int SR, class OM>
 __device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16_t (&acc)[TM][TN], float* stg,
                                                                    int64_t rbase0, int wcol, int N, const OM& om,
                                                                    const EpiP& ep, int pe_ld, int lane) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   constexpr int LDW = WTN + 4;
   constexpr int HS = 32 / SR;       // rounds per 32-row block
   constexpr int ROUNDS = TM * HS;
   constexpr bool GATE = EPI == EPI_SWIGLU;
+  constexpr bool F32OUT = EPI == EPI_RESADD || EPI == EPI_PE || EPI == EPI_STORE_F32;
+  constexpr int ES = F32OUT ? 4 : (int)sizeof(OT);
   constexpr int Q = GATE ? WTN / 8 : WTN / 4;  // lanes per staged row
   constexpr int RPI = 64 / Q;                   // staged rows per 64 lanes
   constexpr int T = SR / RPI;                   // rows per lane per round
   static_assert(RPI * Q == 64 && T * RPI == SR, "epilogue lane map");
+  constexpr uint32_t NOWHERE = 0x80000000u;     // out of range: loads read 0, stores are dropped
   const int l32 = lane & 31, half = lane >> 5;
   const int q4 = lane % Q, rs = lane / Q;
   // gate: (gate, up) pairs of 32 columns interleaved in 64-column groups; the output column is
@@ -264,20 +303,26 @@ __device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16
   const int scol = GATE ? 64 * gp + gj : 4 * q4;          // staged column
   const int col = GATE ? (wcol + 64 * gp) / 2 + gj : wcol + 4 * q4;  // output column
   const bool colok = GATE ? wcol + 64 * gp < N : col < N;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(ep.C, ep.c_bytes);
   float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (EPI != EPI_PE && !GATE)
     if (ep.bias && colok) bv = *reinterpret_cast<const float4*>(ep.bias + col);
 
+  const typename OM::Ctx octx = om.ctx(rbase0);
   auto row_of = [&](int rd, int t) -> int64_t { return rbase0 + (rd / HS) * 32 + (rd % HS) * SR + rs + RPI * t; };
-  int64_t offn[T];
+  // byte offset of this lane's 4 outputs in row (rd, t), or NOWHERE
+  uint32_t offn[T];
   float4 resn[T];
   auto prefetch = [&](int rd) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      offn[t] = colok ? om.off(row_of(rd, t)) : -1;
+      // computed for every lane and selected, so that no branch splits the loads and stores
+      // (the wait-count pass would then wait for all of them where the branches merge)
+      const int64_t off = om.off(octx, row_of(rd, t));
+      const uint32_t o = (uint32_t)((off + col) * ES);
+      offn[t] = (colok & (off >= 0)) ? o : NOWHERE;
       if constexpr (EPI == EPI_RESADD)
-        resn[t] = offn[t] >= 0 ? *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(ep.C) + offn[t] + col)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        resn[t] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(crs, (int)offn[t], 0, 0));
     }
   };
   prefetch(0);
@@ -299,7 +344,7 @@ __device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16
       a[t] = *reinterpret_cast<const float4*>(stg + (rs + RPI * t) * LDW + scol);
       if constexpr (GATE) g2[t] = *reinterpret_cast<const float4*>(stg + (rs + RPI * t) * LDW + scol + 32);
     }
-    int64_t off[T];
+    uint32_t off[T];
     float4 res[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -309,28 +354,28 @@ __device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16
     if (rd + 1 < ROUNDS) prefetch(rd + 1);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      if (off[t] < 0) continue;
       float4 x = a[t];
       if constexpr (GATE) {
-        Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off[t] + col, silu(x.x) * g2[t].x, silu(x.y) * g2[t].y,
-                         silu(x.z) * g2[t].z, silu(x.w) * g2[t].w);
+        x = make_float4(silu(x.x) * g2[t].x, silu(x.y) * g2[t].y, silu(x.z) * g2[t].z, silu(x.w) * g2[t].w);
       } else if constexpr (EPI == EPI_PE) {
-        const float4 pe = *reinterpret_cast<const float4*>(ep.pe + (int64_t)ep.tok_pos[row_of(rd, t)] * pe_ld + col);
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off[t] + col) =
-            make_float4(x.x + pe.x, x.y + pe.y, x.z + pe.z, x.w + pe.w);
+        // rows outside the output read position 0 (their stores are dropped)
+        const int64_t row = row_of(rd, t);
+        const int pos = off[t] != NOWHERE ? ep.tok_pos[row] : 0;
+        const float4 pe = *reinterpret_cast<const float4*>(ep.pe + (int64_t)pos * pe_ld + (colok ? col : 0));
+        x = make_float4(x.x + pe.x, x.y + pe.y, x.z + pe.z, x.w + pe.w);
       } else {
         x.x += bv.x; x.y += bv.y; x.z += bv.z; x.w += bv.w;
-        if constexpr (EPI == EPI_RESADD) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off[t] + col) =
-              make_float4(res[t].x + x.x, res[t].y + x.y, res[t].z + x.z, res[t].w + x.w);
-        } else if constexpr (EPI == EPI_STORE_F32) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.C) + off[t] + col) = x;
-        } else {
-          if constexpr (EPI == EPI_BIAS_GELU) {
-            x.x = gelu_erf(x.x); x.y = gelu_erf(x.y); x.z = gelu_erf(x.z); x.w = gelu_erf(x.w);
-          }
-          Store4x<OT>::put(reinterpret_cast<OT*>(ep.C) + off[t] + col, x.x, x.y, x.z, x.w);
+        if constexpr (EPI == EPI_RESADD)
+          x = make_float4(res[t].x + x.x, res[t].y + x.y, res[t].z + x.z, res[t].w + x.w);
+        if constexpr (EPI == EPI_BIAS_GELU) {
+          x.x = gelu_erf(x.x); x.y = gelu_erf(x.y); x.z = gelu_erf(x.z); x.w = gelu_erf(x.w);
         }
+      }
+      if constexpr (ES == 4) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), crs, (int)off[t], 0, 0);
+      } else {
+        const u32x2 o = {pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w)};
+        __builtin_amdgcn_raw_buffer_store_b64(o, crs, (int)off[t], 0, 0);
       }
     }
   }
@@ -343,13 +388,6 @@ __device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16
 template <int BK>
 __device__ __host__ constexpr int swz(int r) { return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3; }
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
-  // raw buffer: stride 0, range check against `bytes`; dword3 0x00020000 (32-bit data format)
-  // integer clamp (a 64-bit min lowers to a vector f64 op here, which would drag the whole
-  // descriptor into vector registers and wrap every buffer load in a waterfall loop)
-  const int n = __builtin_amdgcn_readfirstlane(bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
-}
 
 // TAG only names the call site (one kernel symbol per role, so profiles separate them)
 #ifndef AE_GEMM_GROUP_M
@@ -546,17 +584,22 @@ __device__ inline void wait_vm_lds0() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
 }
 
-// NST-stage direct-to-LDS kernel.  Each stage is its own __shared__ array, so the compiler's
-// wait-count tracking knows which DMA a fragment read depends on and never holds a read back
-// for the DMAs of other stages.  One barrier per K step, at its start: it publishes tile kt and
-// frees the stage read in step kt-1, which is then refilled with tile kt+NST-1 in KS slices,
-// one slice issued between the MFMAs of each K sub-step; fragment reads of sub-step ks+1 are
-// issued before the MFMAs of ks.  Tile kt+NST-1 thus has NST-2 full steps to land.
+// NST-stage direct-to-LDS kernel (NST = 2..4).  Each stage is its own __shared__ array, so the
+// compiler's wait-count tracking knows which DMA a fragment read depends on and never holds a
+// read back for the DMAs of other stages.
+//
+// Schedule of K step kt (tile kt in stage kt % NST; its first MFMA fragments already in
+// registers): the fragment reads of sub-step ks+1 are issued before the MFMAs of ks, so LDS
+// latency hides behind MFMAs.  Before the MFMAs of the last sub-step, one barrier publishes tile
+// kt+1 and retires every wave's reads of tile kt; the first fragments of tile kt+1 are then
+// read, and the freed stage is refilled with tile kt+NST, its DMAs interleaved with those last
+// MFMAs.  A tile's DMAs therefore have NST-1 steps to land, and no wave ever waits on LDS
+// reads issued after a barrier.
 template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG>
 __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const bf16_t* __restrict__ Bw,
                                                                    int32_t N, int32_t K, OM om, EpiP ep,
                                                                    int32_t n_tiles, int32_t pe_ld, int32_t gm) {
-  static_assert(NST >= 3 && NST <= 4, "stages: the last refill slice needs a step of slack");
+  static_assert(NST >= 2 && NST <= 4, "stages");
   constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
   constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
   constexpr int STG = (BM + BN) * BK;
@@ -570,9 +613,10 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
   static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
   static_assert(P * (NST - 1) < 64, "vmcnt range");
   constexpr int KS = BK / 16;
+  static_assert(KS % 2 == 0, "the fragment double buffer alternates within a tile");
   __shared__ __attribute__((aligned(1024))) bf16_t st0[STG];
   __shared__ __attribute__((aligned(1024))) bf16_t st1[STG];
-  __shared__ __attribute__((aligned(1024))) bf16_t st2[STG];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[NST > 2 ? STG : 8];
   __shared__ __attribute__((aligned(1024))) bf16_t st3[NST > 3 ? STG : 8];
   auto stage = [&](auto sc) -> bf16_t* {
     constexpr int s = decltype(sc)::value;
@@ -611,11 +655,10 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
     const int n = n0 + r;
     boffr[j] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
   }
-  // DMA instructions [lo, hi) of tile kt (A rows first, then B rows)
-  auto dma_part = [&](int kt, bf16_t* st, int lo, int hi) {
+  // all DMA instructions of tile kt into stage st (A rows first, then B rows)
+  auto dma = [&](int kt, bf16_t* st) {
 #pragma unroll
     for (int j = 0; j < ADMA; ++j) {
-      if (j < lo || j >= hi) continue;
       const int k = kt * BK + achunk[j] * 8;
       const uint32_t off = as.boff(arow[j], as.kc(k));
       bf16_t* dst = st + (wv * ADMA + j) * ROWS_PER_DMA * BK;
@@ -624,7 +667,6 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
     }
 #pragma unroll
     for (int j = 0; j < BDMA; ++j) {
-      if (ADMA + j < lo || ADMA + j >= hi) continue;
       const int k = kt * BK + bchunk[j] * 8;
       const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
       bf16_t* dst = st + BM * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
@@ -672,37 +714,43 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
   // tracking merges the states of branches conservatively and would otherwise stall MFMAs on
   // fragment reads they do not use).
   const int nk = (K + BK * NST - 1) / (BK * NST) * NST;
-  dma_part(0, st0, 0, P);
-  dma_part(1, st1, 0, P);
-  if constexpr (NST > 3) dma_part(2, st2, 0, P);
+  dma(0, st0);
+  dma(1, st1);
+  if constexpr (NST > 2) dma(2, st2);
+  if constexpr (NST > 3) dma(3, st3);
+  wait_vm_lds0<P * (NST - 1)>();  // tile 0 landed
+  barrier();
+  rd(st0, 0, 0);
 
   auto step = [&](int kt, auto sc) {
     constexpr int s = decltype(sc)::value;
-    constexpr int sf = (s + NST - 1) % NST;  // stage freed by this step's barrier
-    wait_vm_lds0<P * (NST - 2)>();           // tile kt landed; tiles kt+1 .. kt+NST-2 in flight
-    barrier();
-    const bf16_t* cur = stage(sc);
-    bf16_t* nxt = stage(std::integral_constant<int, sf>());
-    rd(cur, 0, 0);
+    bf16_t* cur = stage(sc);
+    const bf16_t* nxt = stage(std::integral_constant<int, (s + 1) % NST>());
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) rd(cur, ks + 1, (ks + 1) & 1);
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      rd(cur, ks + 1, (ks + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
-      dma_part(kt + NST - 1, nxt, ks * P / KS, (ks + 1) * P / KS);
       mm(ks & 1);
-      // alternate refill DMAs and MFMAs
-#pragma unroll
-      for (int d = ks * P / KS; d < (ks + 1) * P / KS; ++d) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
+    wait_vm_lds0<P * (NST - 2)>();  // tile kt+1 landed; this wave's reads of tile kt retired
+    barrier();
+    rd(nxt, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    dma(kt + NST, cur);
+    mm((KS - 1) & 1);
+    // alternate the refill DMAs with the last MFMAs
+#pragma unroll
+    for (int d = 0; d < P; ++d) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
   for (int kt = 0; kt < nk; kt += NST) {
     step(kt, std::integral_constant<int, 0>());
     step(kt + 1, std::integral_constant<int, 1>());
-    step(kt + 2, std::integral_constant<int, 2>());
+    if constexpr (NST > 2) step(kt + 2, std::integral_constant<int, 2>());
     if constexpr (NST > 3) step(kt + 3, std::integral_constant<int, 3>());
   }
   wait_vm_lds0<0>();  // the trailing zero-fill DMAs land before the stages are reused
@@ -770,7 +818,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(AS as, const float* __res
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t row = m0 + ty * 4 + i;
-    const int64_t off = om.off(row);
+    const int64_t off = om.off_row(row);
     if (off < 0) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -789,7 +837,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(AS as, const float* __res
 // ============================================================================================
 // dispatch
 // ============================================================================================
-// NST = 0: gemm_dtl_kernel (one tile in flight); NST >= 3: gemm_ilv_kernel with NST stages.
+// NST = 0: gemm_dtl_kernel (one tile in flight); NST >= 2: gemm_ilv_kernel with NST stages.
 template <typename T, class TL, class AS, class OM, int EPI, int TAG, int NST = 0, bool BQ = false>
 hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, const EpiP& ep,
                int64_t m_rows, int32_t pe_ld, hipStream_t s, BQuant bq = BQuant{nullptr, nullptr}) {
@@ -798,6 +846,10 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
     const int64_t m_tiles = (m_rows + TL::BM - 1) / TL::BM;
     if (m_tiles * n_tiles == 0) return hipSuccess;
     if (m_tiles * n_tiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    // every operand is addressed through 32-bit buffer offsets
+    constexpr int64_t kMaxBytes = 0x7fffffff;
+    if (as.bytes() > kMaxBytes || (int64_t)N * K * 2 > kMaxBytes || ep.c_bytes > kMaxBytes)
+      return hipErrorInvalidValue;
     static_assert(!BQ || NST == 0, "int4 weights run in the one-stage kernel");
     if constexpr (NST == 0)
       hipLaunchKernelGGL((gemm_dtl_kernel<TL, AS, OM, EPI, bf16_t, TAG, BQ>),
@@ -821,18 +873,21 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
   return hipGetLastError();
 }
 
-// Tile choice (measured on MI355X with the shapes of the tower):
-//  - N = 1280 or 3840 (o-proj, FFN2, conv_out, proj1, QKV) and other N < 2048: 128x128 tiles,
-//    BK 64, two workgroups per CU, as long as the tiles fit in one round of two per CU (M up to
-//    ~6500 at N = 1280).  Beyond that a second, nearly empty round would cost ~30%, and the
-//    larger tiles below are faster.
-//  - N = 5120 (FFN1) and the rest with K < 2048: 256x128 tiles, 8 waves (two per SIMD), BK 32.
-//  - K >= 2048 (adapter gate/up and down, FFN2 once M is past one round): 256x256 tiles,
-//    8 waves, BK 32, four stages with the refill DMAs spread over the MFMAs.
+// Tile choice (measured on MI355X with the shapes of the tower, M = 6000 and 7281):
+//  - K >= 2048 (FFN2, conv_out, the adapter): staged kernel with BK 64, whose 128-byte row
+//    pieces make full use of each L2 request (64-byte pieces reach about two thirds of the
+//    rate).  128x256 tiles with three stages when they fit in one round on the CUs (FFN2 at
+//    M = 6000), else 256x256 with two stages.
+//  - N = 3840 (QKV), and N = 1280 or other N < 2048 while the tiles fit in one round of two per
+//    CU: 128x128 tiles, BK 64, two workgroups per CU.  Beyond that a second, nearly empty round
+//    would cost ~30%, and the larger tiles below are faster.
+//  - The rest with K < 2048 (FFN1, proj2): 256x128 tiles, 8 waves (two per SIMD), BK 32.
 using TileWide = Tile<256, 128, 4, 2, 32, 1>;
 using TileNarrow = Tile<128, 128, 2, 2, 64, 2>;
-using TileLarge = Tile<256, 256, 2, 4, 32, 1>;
-enum class LinKind { Narrow, Wide, Large };
+using TileLarge = Tile<256, 256, 2, 4, 64, 1>;
+using TileTall = Tile<128, 256, 2, 4, 64, 1>;
+constexpr int kLargeStages = 2, kTallStages = 3;
+enum class LinKind { Narrow, Wide, Large, Tall };
 
 int cu_count() {
   static int cached[64] = {0};
@@ -847,17 +902,25 @@ int cu_count() {
   return cached[dev];
 }
 
+inline int64_t tile_count(int64_t M, int64_t N, int64_t bm, int64_t bn) {
+  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+}
+
 inline LinKind lin_kind(int64_t M, int64_t N, int64_t K) {
-  if (N == 1280 || N == 3840 || N < 2048) {
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    if (tiles <= 2 * (int64_t)cu_count()) return LinKind::Narrow;
-  }
-  if (K >= 2048) return LinKind::Large;
+  const int64_t cus = cu_count();
+  if (K >= 2048) return tile_count(M, N, 128, 256) <= cus ? LinKind::Tall : LinKind::Large;
+  if (N == 3840) return LinKind::Narrow;
+  if ((N == 1280 || N < 2048) && tile_count(M, N, 128, 128) <= 2 * cus) return LinKind::Narrow;
   return LinKind::Wide;
 }
 
-// conv2/conv3 (N = 480 output channels, K = 9 * 480): 256x256 tiles with four stages measured
-// fastest (the 480 channels fill two 256-wide column tiles at 94%)
+// int4 weights run in the one-stage kernel, which dequantises B on its way into LDS
+inline bool int4_narrow(int64_t M, int64_t N) {
+  return (N == 1280 || N == 3840 || N < 2048) && tile_count(M, N, 128, 128) <= 2 * (int64_t)cu_count();
+}
+
+// conv2/conv3 (N = 480 output channels, K = 9 * 480): 256x256 tiles, the 480 channels filling
+// two 256-wide column tiles at 94%
 #ifndef AE_CONV_TILE
 #define AE_CONV_TILE 1
 #endif
@@ -868,25 +931,26 @@ constexpr int kConvStages = 0;
 using TileConv = Tile<256, 256, 2, 4, 32, 1>;
 constexpr int kConvStages = 4;
 #elif AE_CONV_TILE == 2
-using TileConv = Tile<256, 128, 4, 2, 32, 1>;
-constexpr int kConvStages = 4;
+using TileConv = Tile<256, 256, 2, 4, 64, 1>;
+constexpr int kConvStages = 2;
 #else
-using TileConv = Tile<128, 128, 2, 2, 64, 2>;
-constexpr int kConvStages = 0;
+using TileConv = Tile<128, 256, 2, 4, 64, 1>;
+constexpr int kConvStages = 3;
 #endif
 
 template <typename T, int TAG, int EPI>
 hipError_t lin(const LinearArgs& a, hipStream_t s) {
   ALinear<T> as{reinterpret_cast<const T*>(a.A), a.lda, a.M, a.K};
   OLinear om{a.M, a.ldc};
-  EpiP ep{a.bias, a.C, a.pe, a.tok_pos};
+  constexpr bool f32out = EPI == EPI_RESADD || EPI == EPI_PE || EPI == EPI_STORE_F32;
+  EpiP ep{a.bias, a.C, a.pe, a.tok_pos, a.M * a.ldc * (int64_t)(f32out ? 4 : sizeof(T))};
   const T* Bw = reinterpret_cast<const T*>(a.W);
   const int pe_ld = EPI == EPI_PE ? a.N : 0;
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (a.Wq) {
       if (a.K % 128 != 0 || !a.Ws) return hipErrorInvalidValue;
       const BQuant bq{a.Wq, a.Ws};
-      if (lin_kind(a.M, a.N, a.K) == LinKind::Narrow)
+      if (int4_narrow(a.M, a.N))
         return run<T, TileNarrow, ALinear<T>, OLinear, EPI, TAG, 0, true>(as, Bw, a.N, a.K, om, ep, a.M,
                                                                          pe_ld, s, bq);
       return run<T, TileWide, ALinear<T>, OLinear, EPI, TAG, 0, true>(as, Bw, a.N, a.K, om, ep, a.M,
@@ -897,7 +961,9 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
   }
   switch (lin_kind(a.M, a.N, a.K)) {
     case LinKind::Large:
-      return run<T, TileLarge, ALinear<T>, OLinear, EPI, TAG, 4>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+      return run<T, TileLarge, ALinear<T>, OLinear, EPI, TAG, kLargeStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+    case LinKind::Tall:
+      return run<T, TileTall, ALinear<T>, OLinear, EPI, TAG, kTallStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
     case LinKind::Wide:
       return run<T, TileWide, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
     default:
@@ -945,16 +1011,30 @@ hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T*
   const int Lout_max = Lin_max / 2;
   const int rows_per_win = Lout_max * Fout;
   const int64_t m_rows = (int64_t)g.n_win * rows_per_win;
-  if ((int64_t)g.n_win * Lin_max * Fin * C >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   AConv<T> as{in, g.wins, C, Fin, Fout, Lin_max, level, rows_per_win, 9 * C, m_rows,
               (int64_t)g.n_win * Lin_max * Fin * C * (int64_t)sizeof(T)};
-  OConv om{g.wins, rows_per_win, Fout, C, level, Lout_max, m_rows};
-  EpiP ep{bias, out, nullptr, nullptr};
-  if (level == 2)
-    return run<T, TileConv, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV2, kConvStages>(as, wpk, C, 9 * C, om, ep,
-                                                                                     m_rows, 0, s);
-  return run<T, TileConv, AConv<T>, OConv, EPI_BIAS_GELU, ENC_K_CONV3, kConvStages>(as, wpk, C, 9 * C, om, ep,
-                                                                                   m_rows, 0, s);
+  if (m_rows >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const int64_t out_rows = level == 2 ? (int64_t)g.n_win * Lout_max * Fout : g.n_tok * Fout;
+  EpiP ep{bias, out, nullptr, nullptr, out_rows * C * (int64_t)sizeof(T)};
+  // a wave covers TileConv::WTM rows of the tile
+  if (rows_per_win >= TileConv::WTM) {
+    if (level == 2) {
+      OConv<2, true> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
+      return run<T, TileConv, AConv<T>, OConv<2, true>, EPI_BIAS_GELU, ENC_K_CONV2, kConvStages>(
+          as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
+    }
+    OConv<3, true> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
+    return run<T, TileConv, AConv<T>, OConv<3, true>, EPI_BIAS_GELU, ENC_K_CONV3, kConvStages>(
+        as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
+  }
+  if (level == 2) {
+    OConv<2, false> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
+    return run<T, TileConv, AConv<T>, OConv<2, false>, EPI_BIAS_GELU, ENC_K_CONV2, kConvStages>(
+        as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
+  }
+  OConv<3, false> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
+  return run<T, TileConv, AConv<T>, OConv<3, false>, EPI_BIAS_GELU, ENC_K_CONV3, kConvStages>(
+      as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
 }
 
 template hipError_t launch_linear<bf16_t>(const LinearArgs&, int, int, hipStream_t);
