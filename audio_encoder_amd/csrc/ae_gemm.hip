@@ -873,20 +873,24 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
   return hipGetLastError();
 }
 
-// Tile choice (measured on MI355X with the shapes of the tower, M = 6000 and 7281):
-//  - K >= 2048 (FFN2, conv_out, the adapter): staged kernel with BK 64, whose 128-byte row
-//    pieces make full use of each L2 request (64-byte pieces reach about two thirds of the
-//    rate).  128x256 tiles with three stages when they fit in one round on the CUs (FFN2 at
-//    M = 6000), else 256x256 with two stages.
-//  - N = 3840 (QKV), and N = 1280 or other N < 2048 while the tiles fit in one round of two per
-//    CU: 128x128 tiles, BK 64, two workgroups per CU.  Beyond that a second, nearly empty round
-//    would cost ~30%, and the larger tiles below are faster.
-//  - The rest with K < 2048 (FFN1, proj2): 256x128 tiles, 8 waves (two per SIMD), BK 32.
+// Tile choice.  Candidates (the staged kernel unless noted):
+//   Large  256x256, BK 64, 2 stages, one workgroup per CU
+//   Tall   128x256, BK 64, 3 stages, one workgroup per CU
+//   Narrow 128x128, BK 64, 2 stages, two workgroups per CU
+//   Wide   256x128, BK 32, one-stage kernel, one workgroup per CU
+// BK 64 moves 128-byte row pieces, a whole L2 request each (64-byte pieces reach about two
+// thirds of the rate).  The GELU epilogue is VALU-heavy and runs after the K loop; with two
+// workgroups per CU one's epilogue overlaps the other's MFMAs, so it takes Narrow.  Otherwise
+// the kernel is chosen by its predicted time: rounds of tiles over the CUs times a per-tile
+// cost proportional to the tile's area.  The constants (microseconds per 10^6 x tile area x K)
+// are least-squares fits to measurements on MI355X over the tower's shapes at M = 6000 and
+// 7281 (QKV, o-proj, FFN2, proj1/2, adapter); the rule picks the fastest kernel, or one within
+// 2% of it, in every measured case.
 using TileWide = Tile<256, 128, 4, 2, 32, 1>;
 using TileNarrow = Tile<128, 128, 2, 2, 64, 2>;
 using TileLarge = Tile<256, 256, 2, 4, 64, 1>;
 using TileTall = Tile<128, 256, 2, 4, 64, 1>;
-constexpr int kLargeStages = 2, kTallStages = 3;
+constexpr int kLargeStages = 2, kTallStages = 3, kNarrowStages = 2;
 enum class LinKind { Narrow, Wide, Large, Tall };
 
 int cu_count() {
@@ -906,12 +910,22 @@ inline int64_t tile_count(int64_t M, int64_t N, int64_t bm, int64_t bn) {
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
-inline LinKind lin_kind(int64_t M, int64_t N, int64_t K) {
+inline LinKind lin_kind(int64_t M, int64_t N, bool gelu_epilogue) {
+  if (gelu_epilogue) return LinKind::Narrow;
   const int64_t cus = cu_count();
-  if (K >= 2048) return tile_count(M, N, 128, 256) <= cus ? LinKind::Tall : LinKind::Large;
-  if (N == 3840) return LinKind::Narrow;
-  if ((N == 1280 || N < 2048) && tile_count(M, N, 128, 128) <= 2 * cus) return LinKind::Narrow;
-  return LinKind::Wide;
+  auto cost = [&](int64_t bm, int64_t bn, int64_t per_cu, double us_per_mel) {
+    const int64_t slots = per_cu * cus;
+    const int64_t rounds = (tile_count(M, N, bm, bn) + slots - 1) / slots;
+    return (double)rounds * us_per_mel * (double)(bm * bn);
+  };
+  const double large = cost(256, 256, 1, 0.393), tall = cost(128, 256, 1, 0.448);
+  const double narrow = cost(128, 128, 2, 0.912), wide = cost(256, 128, 1, 0.502);
+  LinKind k = LinKind::Large;
+  double best = large;
+  if (tall < best) { best = tall; k = LinKind::Tall; }
+  if (narrow < best) { best = narrow; k = LinKind::Narrow; }
+  if (wide < best) k = LinKind::Wide;
+  return k;
 }
 
 // int4 weights run in the one-stage kernel, which dequantises B on its way into LDS
@@ -959,7 +973,7 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
   } else {
     if (a.Wq) return hipErrorInvalidValue;
   }
-  switch (lin_kind(a.M, a.N, a.K)) {
+  switch (lin_kind(a.M, a.N, EPI == EPI_BIAS_GELU)) {
     case LinKind::Large:
       return run<T, TileLarge, ALinear<T>, OLinear, EPI, TAG, kLargeStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
     case LinKind::Tall:
@@ -967,7 +981,7 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
     case LinKind::Wide:
       return run<T, TileWide, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
     default:
-      return run<T, TileNarrow, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+      return run<T, TileNarrow, ALinear<T>, OLinear, EPI, TAG, kNarrowStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
   }
 }
 
