@@ -933,24 +933,12 @@ inline bool int4_narrow(int64_t M, int64_t N) {
   return (N == 1280 || N == 3840 || N < 2048) && tile_count(M, N, 128, 128) <= 2 * (int64_t)cu_count();
 }
 
-// conv2/conv3 (N = 480 output channels, K = 9 * 480): 256x256 tiles, the 480 channels filling
-// two 256-wide column tiles at 94%
-#ifndef AE_CONV_TILE
-#define AE_CONV_TILE 1
-#endif
-#if AE_CONV_TILE == 0
-using TileConv = Tile<256, 128, 4, 2, 32, 1>;
-constexpr int kConvStages = 0;
-#elif AE_CONV_TILE == 1
+// conv2/conv3 (N = 480 output channels, K = 9 * 480): 256x256 tiles, BK 32, four stages (the
+// 480 channels fill two 256-wide column tiles at 94%).  Measured on MI355X against 256x256/BK 64
+// with two stages, 128x256/BK 64 with three, and 128x128 with two workgroups per CU (BK 64 and
+// BK 32): 13-35% slower for conv2.
 using TileConv = Tile<256, 256, 2, 4, 32, 1>;
 constexpr int kConvStages = 4;
-#elif AE_CONV_TILE == 2
-using TileConv = Tile<256, 256, 2, 4, 64, 1>;
-constexpr int kConvStages = 2;
-#else
-using TileConv = Tile<128, 256, 2, 4, 64, 1>;
-constexpr int kConvStages = 3;
-#endif
 
 template <typename T, int TAG, int EPI>
 hipError_t lin(const LinearArgs& a, hipStream_t s) {
