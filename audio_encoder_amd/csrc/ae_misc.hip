@@ -44,13 +44,19 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
   const float4* xr = reinterpret_cast<const float4*>(x + row * D);
-  float4 v[NJ];
-  float s = 0.0f;
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+  // gain and bias are loaded with the row, so their latency is not paid after the reductions
+  float4 v[NJ], gg[NJ], bb[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     v[j] = xr[lane + 64 * j];
-    s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+    gg[j] = g4[lane + 64 * j];
+    bb[j] = b4[lane + 64 * j];
   }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
   const float mean = wave_sum(s) * (1.0f / D);
   float q = 0.0f;
 #pragma unroll
@@ -59,15 +65,12 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
     q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
   }
   const float rstd = rsqrtf(wave_sum(q) * (1.0f / D) + eps);
-  const float4* g4 = reinterpret_cast<const float4*>(g);
-  const float4* b4 = reinterpret_cast<const float4*>(b);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int c4 = lane + 64 * j;
-    const float4 gg = g4[c4], bb = b4[c4];
-    Store4<T>::put(y + row * D + 4 * c4, (v[j].x - mean) * rstd * gg.x + bb.x,
-                   (v[j].y - mean) * rstd * gg.y + bb.y, (v[j].z - mean) * rstd * gg.z + bb.z,
-                   (v[j].w - mean) * rstd * gg.w + bb.w);
+    Store4<T>::put(y + row * D + 4 * c4, (v[j].x - mean) * rstd * gg[j].x + bb[j].x,
+                   (v[j].y - mean) * rstd * gg[j].y + bb[j].y, (v[j].z - mean) * rstd * gg[j].z + bb[j].z,
+                   (v[j].w - mean) * rstd * gg[j].w + bb[j].w);
   }
 }
 
