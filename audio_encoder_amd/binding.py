@@ -44,13 +44,19 @@ class EncoderCfg(ctypes.Structure):
                 ("n_layers", c_int32), ("n_heads", c_int32), ("head_dim", c_int32),
                 ("d_ffn", c_int32), ("window_tokens", c_int32), ("d_out", c_int32),
                 ("d_adapter", c_int32), ("piece_tokens", c_int32), ("dtype", c_int32),
-                ("ln_eps", c_float), ("max_tokens_per_pass", c_int64), ("weight_bits", c_int32)]
+                ("ln_eps", c_float), ("max_tokens_per_pass", c_int64), ("weight_bits", c_int32),
+                ("split_small_gemms", c_int32)]
 
 
 def make_cfg(cfg: dict) -> EncoderCfg:
     c = EncoderCfg()
     for name, _ in EncoderCfg._fields_:
-        v = cfg.get(name, 16) if name == "weight_bits" else cfg[name]
+        if name == "weight_bits":
+            v = cfg.get(name, 16)
+        elif name == "split_small_gemms":
+            v = cfg.get(name, 0)
+        else:
+            v = cfg[name]
         if name == "dtype":
             v = {"bf16": ENC_BF16, "f32": ENC_F32}.get(v, v)
         setattr(c, name, v)

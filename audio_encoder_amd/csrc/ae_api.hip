@@ -62,6 +62,8 @@ static encoder_status check_cfg(const encoder_cfg* c) {
     return invalid("max_tokens_per_pass must hold at least one window");
   if (c->weight_bits != 0 && c->weight_bits != 16 && c->weight_bits != 4)
     return invalid("weight_bits must be 16 (or 0) or 4");
+  if (c->split_small_gemms != 0 && c->split_small_gemms != 1)
+    return invalid("split_small_gemms must be 0 or 1");
   if (c->weight_bits == 4) {
     if (c->dtype != ENC_BF16) return invalid("int4 weights need dtype ENC_BF16");
     if (c->d_model % 128 || c->d_ffn % 128 || c->d_out % 128 || c->d_adapter % 128)
@@ -366,6 +368,7 @@ struct encoder {
   // workspace (grown on demand)
   struct Buf { void* p = nullptr; int64_t bytes = 0; };
   Buf mel_raw, max_key, ctab, wtab, tpos, act1, act2, tokA, resid, xn, qkv, attn, hid, hid2, z, dbg;
+  Buf splitk;             // fp32 partial products of split-K GEMMs (bf16 path)
   Buf rs_taps;            // polyphase table of the last input-conditioning rate
   int32_t rs_rate = 0;
   int64_t ws_bytes = 0, ws_peak = 0;
@@ -472,6 +475,7 @@ encoder_status size_workspace(encoder* e, int64_t nclip, int64_t n_frames, int64
   if ((st = ensure(e, e->hid, mt * hidw * es))) return st;
   if (!e->bf16 && (st = ensure(e, e->hid2, mt * 2 * c.d_adapter * es))) return st;
   if ((st = ensure(e, e->z, mt * c.d_out * es))) return st;
+  if (e->bf16 && c.split_small_gemms && (st = ensure(e, e->splitk, kSplitKScratchBytes))) return st;
   return ENC_OK;
 }
 
@@ -516,7 +520,8 @@ encoder_status launch_linear_t(encoder* e, int kid, const void* A, int64_t lda, 
                                const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
                                int epi, hipStream_t s, const float* pe = nullptr,
                                const int32_t* tok_pos = nullptr) {
-  LinearArgs a{A, lda, Wt.w, bias, C, ldc, M, N, K, pe, tok_pos, Wt.q, Wt.s};
+  LinearArgs a{A, lda, Wt.w, bias, C, ldc, M, N, K, pe, tok_pos, Wt.q, Wt.s,
+               (float*)e->splitk.p, e->splitk.bytes};
   LAUNCH(kid, launch_linear<T>(a, epi, kid, s));
   return ENC_OK;
 }
@@ -730,7 +735,7 @@ void free_all(encoder* e) {
   hipDeviceSynchronize();
   encoder::Buf* bufs[] = {&e->mel_raw, &e->max_key, &e->ctab, &e->wtab, &e->tpos, &e->rs_taps, &e->act1, &e->act2,
                           &e->tokA, &e->resid, &e->xn, &e->qkv, &e->attn, &e->hid, &e->hid2,
-                          &e->z, &e->dbg};
+                          &e->z, &e->dbg, &e->splitk};
   for (auto* b : bufs)
     if (b->p) hipFree(b->p);
   if (e->wdev) hipFree(e->wdev);

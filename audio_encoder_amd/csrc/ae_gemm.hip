@@ -195,6 +195,7 @@ struct EpiP {
   const float* pe;
   const int32_t* tok_pos;
   int64_t c_bytes;  // extent of C in bytes (buffer-store range; < 2^31)
+  int64_t c_slice;  // split-K: elements between the partial products of consecutive K ranges
 };
 
 template <int EPI, typename OT>
@@ -304,6 +305,7 @@ __device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16
   const int col = GATE ? (wcol + 64 * gp) / 2 + gj : wcol + 4 * q4;  // output column
   const bool colok = GATE ? wcol + 64 * gp < N : col < N;
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(ep.C, ep.c_bytes);
+  const int64_t slice = (int64_t)blockIdx.y * ep.c_slice;  // split-K partial of this K range
   float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (EPI != EPI_PE && !GATE)
     if (ep.bias && colok) bv = *reinterpret_cast<const float4*>(ep.bias + col);
@@ -319,7 +321,7 @@ __device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16
       // computed for every lane and selected, so that no branch splits the loads and stores
       // (the wait-count pass would then wait for all of them where the branches merge)
       const int64_t off = om.off(octx, row_of(rd, t));
-      const uint32_t o = (uint32_t)((off + col) * ES);
+      const uint32_t o = (uint32_t)((off + col + slice) * ES);
       offn[t] = (colok & (off >= 0)) ? o : NOWHERE;
       if constexpr (EPI == EPI_RESADD)
         resn[t] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(crs, (int)offn[t], 0, 0));
@@ -595,10 +597,13 @@ __device__ inline void wait_vm_lds0() {
 // read, and the freed stage is refilled with tile kt+NST, its DMAs interleaved with those last
 // MFMAs.  A tile's DMAs therefore have NST-1 steps to land, and no wave ever waits on LDS
 // reads issued after a barrier.
+// Split K: workgroup row blockIdx.y covers K range [blockIdx.y * k_span, + k_span) (k_span a
+// multiple of BK * NST); a single range covers all of K.
 template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG>
 __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const bf16_t* __restrict__ Bw,
                                                                    int32_t N, int32_t K, OM om, EpiP ep,
-                                                                   int32_t n_tiles, int32_t pe_ld, int32_t gm) {
+                                                                   int32_t n_tiles, int32_t pe_ld, int32_t gm,
+                                                                   int32_t k_span) {
   static_assert(NST >= 2 && NST <= 4, "stages");
   constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
   constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
@@ -656,19 +661,23 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
     boffr[j] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
   }
   // all DMA instructions of tile kt into stage st (A rows first, then B rows)
+  const int k0 = __builtin_amdgcn_readfirstlane((int)blockIdx.y * k_span);
+  const int kend = K < k0 + k_span ? K : k0 + k_span;
   auto dma = [&](int kt, bf16_t* st) {
 #pragma unroll
     for (int j = 0; j < ADMA; ++j) {
-      const int k = kt * BK + achunk[j] * 8;
-      const uint32_t off = as.boff(arow[j], as.kc(k));
+      const int k = k0 + kt * BK + achunk[j] * 8;
+      auto kc = as.kc(k);
+      kc.ok = kc.ok && k < kend;
+      const uint32_t off = as.boff(arow[j], kc);
       bf16_t* dst = st + (wv * ADMA + j) * ROWS_PER_DMA * BK;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
                                                (int)off, 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < BDMA; ++j) {
-      const int k = kt * BK + bchunk[j] * 8;
-      const uint32_t off = (k < K && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
+      const int k = k0 + kt * BK + bchunk[j] * 8;
+      const uint32_t off = (k < kend && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
       bf16_t* dst = st + BM * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
                                                (int)off, 0, 0, 0);
@@ -713,7 +722,7 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
   // same number of DMAs in flight, so every wait is a constant (the compiler's wait-count
   // tracking merges the states of branches conservatively and would otherwise stall MFMAs on
   // fragment reads they do not use).
-  const int nk = (K + BK * NST - 1) / (BK * NST) * NST;
+  const int nk = (kend - k0 + BK * NST - 1) / (BK * NST) * NST;
   dma(0, st0);
   dma(1, st1);
   if constexpr (NST > 2) dma(2, st2);
@@ -840,7 +849,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(AS as, const float* __res
 // NST = 0: gemm_dtl_kernel (one tile in flight); NST >= 2: gemm_ilv_kernel with NST stages.
 template <typename T, class TL, class AS, class OM, int EPI, int TAG, int NST = 0, bool BQ = false>
 hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, const EpiP& ep,
-               int64_t m_rows, int32_t pe_ld, hipStream_t s, BQuant bq = BQuant{nullptr, nullptr}) {
+               int64_t m_rows, int32_t pe_ld, hipStream_t s, BQuant bq = BQuant{nullptr, nullptr},
+               int32_t splits = 1, int32_t k_span = 0) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     const int n_tiles = (N + TL::BN - 1) / TL::BN;
     const int64_t m_tiles = (m_rows + TL::BM - 1) / TL::BM;
@@ -851,14 +861,16 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
     if (as.bytes() > kMaxBytes || (int64_t)N * K * 2 > kMaxBytes || ep.c_bytes > kMaxBytes)
       return hipErrorInvalidValue;
     static_assert(!BQ || NST == 0, "int4 weights run in the one-stage kernel");
+    if (splits < 1 || (splits > 1 && (NST == 0 || k_span <= 0 || (int64_t)(splits - 1) * k_span >= K)))
+      return hipErrorInvalidValue;
     if constexpr (NST == 0)
       hipLaunchKernelGGL((gemm_dtl_kernel<TL, AS, OM, EPI, bf16_t, TAG, BQ>),
                          dim3((unsigned)(m_tiles * n_tiles)), dim3(TL::NT), 0, s, as, Bw, N, K, om, ep,
                          n_tiles, pe_ld, AE_GEMM_GROUP_M, bq);
     else
       hipLaunchKernelGGL((gemm_ilv_kernel<TL, NST, AS, OM, EPI, bf16_t, TAG>),
-                         dim3((unsigned)(m_tiles * n_tiles)), dim3(TL::NT), 0, s, as, Bw, N, K, om, ep,
-                         n_tiles, pe_ld, AE_GEMM_GROUP_M);
+                         dim3((unsigned)(m_tiles * n_tiles), (unsigned)splits), dim3(TL::NT), 0, s, as, Bw, N,
+                         K, om, ep, n_tiles, pe_ld, AE_GEMM_GROUP_M, splits > 1 ? k_span : K);
   } else {
     if constexpr (EPI == EPI_SWIGLU) {
       return hipErrorInvalidValue;  // the fp32 path applies SwiGLU in a separate kernel
@@ -871,6 +883,63 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
     }
   }
   return hipGetLastError();
+}
+
+// Split-K finish: out = epilogue(sum over the S partial products + bias), the partials summed
+// in K-range order (so the result does not depend on scheduling).  ws holds S slices of
+// [M][N] fp32; each thread produces 4 consecutive output columns.
+template <int EPI, typename OT>
+__global__ __launch_bounds__(256) void splitk_finish_kernel(const float* __restrict__ ws, int32_t S, int64_t M,
+                                                            int32_t N, const float* __restrict__ bias, void* C,
+                                                            int64_t ldc, const float* __restrict__ pe,
+                                                            const int32_t* __restrict__ tok_pos, int32_t pe_ld) {
+  constexpr bool GATE = EPI == EPI_SWIGLU;
+  const int32_t q4 = (GATE ? N / 2 : N) / 4;  // 4-column groups per output row
+  const int64_t slice = M * N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < M * q4; i += (int64_t)gridDim.x * 256) {
+    const int64_t m = i / q4;
+    const int o = (int)(i - m * q4) * 4;  // output column
+    auto sum4 = [&](int col) {
+      const float* p = ws + m * N + col;
+      float4 a = *reinterpret_cast<const float4*>(p);
+      for (int sp = 1; sp < S; ++sp) {
+        const float4 b = *reinterpret_cast<const float4*>(p + sp * slice);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+      return a;
+    };
+    if constexpr (GATE) {
+      // gate and up columns interleave in groups of 32 within each 64-column group
+      const int gcol = (o / 32) * 64 + o % 32;
+      const float4 g = sum4(gcol), u = sum4(gcol + 32);
+      const uint2 v = make_uint2(pack_bf16x2(silu(g.x) * u.x, silu(g.y) * u.y), pack_bf16x2(silu(g.z) * u.z, silu(g.w) * u.w));
+      *reinterpret_cast<uint2*>(reinterpret_cast<OT*>(C) + m * ldc + o) = v;
+    } else {
+      float4 x = sum4(o);
+      float* cf = reinterpret_cast<float*>(C) + m * ldc + o;
+      if constexpr (EPI == EPI_PE) {
+        const float4 p = *reinterpret_cast<const float4*>(pe + (int64_t)tok_pos[m] * pe_ld + o);
+        *reinterpret_cast<float4*>(cf) = make_float4(x.x + p.x, x.y + p.y, x.z + p.z, x.w + p.w);
+      } else {
+        if (bias) {
+          const float4 b = *reinterpret_cast<const float4*>(bias + o);
+          x.x += b.x; x.y += b.y; x.z += b.z; x.w += b.w;
+        }
+        if constexpr (EPI == EPI_RESADD) {
+          const float4 r = *reinterpret_cast<const float4*>(cf);
+          *reinterpret_cast<float4*>(cf) = make_float4(r.x + x.x, r.y + x.y, r.z + x.z, r.w + x.w);
+        } else if constexpr (EPI == EPI_STORE_F32) {
+          *reinterpret_cast<float4*>(cf) = x;
+        } else {
+          if constexpr (EPI == EPI_BIAS_GELU) {
+            x.x = gelu_erf(x.x); x.y = gelu_erf(x.y); x.z = gelu_erf(x.z); x.w = gelu_erf(x.w);
+          }
+          *reinterpret_cast<uint2*>(reinterpret_cast<OT*>(C) + m * ldc + o) =
+              make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+        }
+      }
+    }
+  }
 }
 
 // Tile choice.  Candidates (the staged kernel unless noted):
@@ -957,6 +1026,31 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
                                                                          pe_ld, s, bq);
       return run<T, TileWide, ALinear<T>, OLinear, EPI, TAG, 0, true>(as, Bw, a.N, a.K, om, ep, a.M,
                                                                      pe_ld, s, bq);
+    }
+    // Split K when even the 128x128 tiles (two per CU) would leave more than half the CUs idle
+    // (a single clip: M = 375).  Each K range writes an fp32 partial product into the scratch,
+    // and splitk_finish_kernel sums them in order and applies the epilogue.
+    if (a.ws && a.M > 0) {
+      const int64_t cus = cu_count();
+      const int64_t tiles = tile_count(a.M, a.N, 128, 128);
+      const int64_t step = TileNarrow::BK * kNarrowStages;
+      int64_t S = std::min<int64_t>({(2 * cus) / tiles, a.K / (2 * step), 16,
+                                     a.ws_bytes / (a.M * a.N * 4)});
+      if (2 * tiles <= cus && S >= 2 && a.N % (EPI == EPI_SWIGLU ? 64 : 4) == 0) {
+        const int64_t k_span = ((a.K + S - 1) / S + step - 1) / step * step;
+        S = (a.K + k_span - 1) / k_span;
+        ALinear<T> as_p{reinterpret_cast<const T*>(a.A), a.lda, a.M, a.K};
+        OLinear om_p{a.M, a.N};
+        EpiP ep_p{nullptr, a.ws, nullptr, nullptr, S * a.M * a.N * 4, a.M * a.N};
+        hipError_t err = run<T, TileNarrow, ALinear<T>, OLinear, EPI_STORE_F32, TAG, kNarrowStages>(
+            as_p, Bw, a.N, a.K, om_p, ep_p, a.M, 0, s, BQuant{nullptr, nullptr}, (int32_t)S, (int32_t)k_span);
+        if (err != hipSuccess) return err;
+        const int64_t groups = a.M * ((EPI == EPI_SWIGLU ? a.N / 2 : a.N) / 4);
+        const int64_t blocks = std::min<int64_t>((groups + 255) / 256, 16 * cus);
+        hipLaunchKernelGGL((splitk_finish_kernel<EPI, bf16_t>), dim3((unsigned)blocks), dim3(256), 0, s, a.ws,
+                           (int32_t)S, a.M, a.N, a.bias, a.C, a.ldc, a.pe, a.tok_pos, pe_ld);
+        return hipGetLastError();
+      }
     }
   } else {
     if (a.Wq) return hipErrorInvalidValue;

@@ -157,7 +157,11 @@ struct LinearArgs {
   const float* pe; const int32_t* tok_pos;
   // int4 weight-only B (bf16 path, K % 128 == 0): W is then unused; q [N][K/2], s [N][K/128]
   const uint8_t* Wq = nullptr; const bf16_t* Ws = nullptr;
+  // split-K scratch for GEMMs too small to fill the GPU (bf16 path; null: never split)
+  float* ws = nullptr; int64_t ws_bytes = 0;
 };
+// split-K scratch each encoder keeps (fp32 partial products of the small-M GEMMs)
+constexpr int64_t kSplitKScratchBytes = int64_t(64) << 20;
 template <typename T>
 hipError_t launch_linear(const LinearArgs& a, int epi, int tag, hipStream_t s);
 

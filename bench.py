@@ -158,6 +158,9 @@ def main():
     ap.add_argument("--weight-bits", type=int, default=16, choices=(16, 4),
                     help="4: int4 weight-only linear layers, head and adapter (dequantised in the "
                          "GEMM loader); the CPU baseline then runs on the dequantised weights")
+    ap.add_argument("--split-small-gemms", action="store_true",
+                    help="split K of GEMMs too small to fill the GPU (single clips); their rows then "
+                         "round differently from the same rows in a large call")
     ap.add_argument("--roofline-steps", type=int, default=3)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the run, launch one plain device copy of this many MiB (a "
@@ -175,7 +178,7 @@ def main():
     from audio_encoder_amd import binding as B
     from audio_encoder_amd import synth as S
 
-    cfg = dict(B.FULL, weight_bits=args.weight_bits)
+    cfg = dict(B.FULL, weight_bits=args.weight_bits, split_small_gemms=int(args.split_small_gemms))
     log("generating weights and input")
     weights = S.make_weights(cfg, seed=0)
     pcm_np, audio_s = make_input(args.workload)

@@ -574,6 +574,31 @@ def test_full_int4_window_matches_oracle(full):
     check_bf16(got[tok:tok + yref.shape[0]], yref, "int4 C1 window 1")
 
 
+def test_full_split_small_gemms(full):
+    """split_small_gemms = 1: a single clip's GEMMs split K (fp32 partial products summed in
+    K-range order); a 16-clip call does not split and stays bit-identical to the default."""
+    enc, Wt = full
+    cfg = dict(B.FULL, split_small_gemms=1)
+    log("split: creating encoder")
+    enc_s = B.Encoder(S.make_weights(cfg, seed=0), cfg)
+    x = S.pink_plus_bursts(seed=1)
+    pcm = to_dev(x[None])
+    a = enc.forward(pcm)
+    b = enc_s.forward(pcm)
+    torch.cuda.synchronize()
+    assert torch.equal(b, enc_s.forward(pcm))  # deterministic
+    cos, rel = frame_metrics(b.float().cpu().numpy()[0], a.float().cpu().numpy()[0])
+    log(f"split vs unsplit: min cos {cos:.7f}  max rel-L2 {rel:.3e}")
+    assert cos >= 0.9999 and rel <= 1e-2
+    got = b.float().cpu().numpy()[0]
+    res, _ = oracle_windows(x, Wt, O.FULL, [2])
+    tok, yref, _ = res[0]
+    check_bf16(got[tok:tok + yref.shape[0]], yref, "split C1 window 2")
+    xs = to_dev(S.mixed_batch(range(101, 117)))
+    assert torch.equal(enc.forward(xs), enc_s.forward(xs))
+    enc_s.close()
+
+
 def test_full_c4_hour_stream(full):
     enc, Wt = full
     x = S.hour_stream()
