@@ -145,7 +145,29 @@ def cpu_baseline(pcm, weights, cfg, max_windows: int = 24, int4: bool = False) -
     cores = len(os.sched_getaffinity(0))
     return {"value": audio_s / dt, "unit": "audio-s/s", "cores": cores, "kind": "oracle",
             "sample": f"first {nwin} windows of the batch ({clips} clips, {audio_s:.0f} s of "
-                      f"audio), float64 NumPy, {dt:.1f} s wall"}
+                      f"audio), float64 NumPy, {dt:.1f} s wall",
+            "cpu": host_cpu_model(), "blas": blas_vendor()}
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_vendor() -> str:
+    import numpy as np
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:
+        return "unknown"
 
 
 def main():
