@@ -80,6 +80,8 @@ static int64_t max_tokens(const encoder_cfg& c) {
   return c.max_tokens_per_pass > 0 ? c.max_tokens_per_pass : 8192;
 }
 static int64_t max_windows(const encoder_cfg& c) { return max_tokens(c) / c.window_tokens + 32; }
+// passes of one call that run at once (each lane holds one pass's activations)
+constexpr int kLanes = 4;
 
 struct TensorSpec { const char* name; int64_t n; };
 
@@ -367,8 +369,17 @@ struct encoder {
   MelTables mel;
   // workspace (grown on demand)
   struct Buf { void* p = nullptr; int64_t bytes = 0; };
-  Buf mel_raw, max_key, ctab, wtab, tpos, act1, act2, tokA, resid, xn, qkv, attn, hid, hid2, z, dbg;
-  Buf splitk;             // fp32 partial products of split-K GEMMs (bf16 path)
+  Buf mel_raw, max_key, ctab, wtab, tpos, dbg;
+  // Activation workspace of one pass.  The passes of a call are independent (windows are), so
+  // they run round-robin on up to kLanes lanes at once, each with its own stream and buffers.
+  struct Lane {
+    Buf act1, act2, tokA, resid, xn, qkv, attn, hid, hid2, z;
+    Buf splitk;                    // fp32 partial products of split-K GEMMs (bf16 path)
+    hipStream_t stream = nullptr;  // created on first concurrent use
+    hipEvent_t done = nullptr;
+  };
+  std::vector<Lane> lanes;
+  hipEvent_t passes_ready = nullptr;
   Buf rs_taps;            // polyphase table of the last input-conditioning rate
   int32_t rs_rate = 0;
   int64_t ws_bytes = 0, ws_peak = 0;
@@ -455,27 +466,32 @@ encoder_status size_mel(encoder* e, int64_t nclip, int64_t n_frames) {
   return ensure(e, e->ctab, std::max<int64_t>(nclip, 1) * (int64_t)sizeof(ClipSpan));
 }
 
-// workspace for passes of up to mt tokens / mw windows, and the log-mel of the call
-encoder_status size_workspace(encoder* e, int64_t nclip, int64_t n_frames, int64_t mt, int64_t mw,
-                              int64_t n_win_total, int64_t n_tok_total) {
-  const encoder_cfg& c = e->cfg;
-  const int64_t es = (int64_t)e->esz, C = c.conv_channels, W = c.window_tokens, d = c.d_model;
+// the log-mel, window table and token positions of a call
+encoder_status size_call(encoder* e, int64_t nclip, int64_t n_frames, int64_t n_win_total,
+                         int64_t n_tok_total) {
   encoder_status st;
   if ((st = size_mel(e, nclip, n_frames))) return st;
   if ((st = ensure(e, e->wtab, n_win_total * (int64_t)sizeof(Win)))) return st;
-  if ((st = ensure(e, e->tpos, std::max<int64_t>(n_tok_total, 1) * 4))) return st;
-  if ((st = ensure(e, e->act1, mw * 4 * W * 64 * C * es))) return st;
-  if ((st = ensure(e, e->act2, mw * 2 * W * 32 * C * es))) return st;
-  if ((st = ensure(e, e->tokA, mt * 16 * C * es))) return st;
-  if ((st = ensure(e, e->resid, mt * d * 4))) return st;
-  if ((st = ensure(e, e->xn, mt * d * es))) return st;
-  if ((st = ensure(e, e->qkv, mt * 3 * d * es))) return st;
-  if ((st = ensure(e, e->attn, mt * d * es))) return st;
+  return ensure(e, e->tpos, std::max<int64_t>(n_tok_total, 1) * 4);
+}
+
+// activation workspace of one lane for passes of up to mt tokens / mw windows
+encoder_status size_lane(encoder* e, encoder::Lane& ln, int64_t mt, int64_t mw) {
+  const encoder_cfg& c = e->cfg;
+  const int64_t es = (int64_t)e->esz, C = c.conv_channels, W = c.window_tokens, d = c.d_model;
+  encoder_status st;
+  if ((st = ensure(e, ln.act1, mw * 4 * W * 64 * C * es))) return st;
+  if ((st = ensure(e, ln.act2, mw * 2 * W * 32 * C * es))) return st;
+  if ((st = ensure(e, ln.tokA, mt * 16 * C * es))) return st;
+  if ((st = ensure(e, ln.resid, mt * d * 4))) return st;
+  if ((st = ensure(e, ln.xn, mt * d * es))) return st;
+  if ((st = ensure(e, ln.qkv, mt * 3 * d * es))) return st;
+  if ((st = ensure(e, ln.attn, mt * d * es))) return st;
   const int64_t hidw = std::max<int64_t>({c.d_ffn, d, c.d_adapter});
-  if ((st = ensure(e, e->hid, mt * hidw * es))) return st;
-  if (!e->bf16 && (st = ensure(e, e->hid2, mt * 2 * c.d_adapter * es))) return st;
-  if ((st = ensure(e, e->z, mt * c.d_out * es))) return st;
-  if (e->bf16 && c.split_small_gemms && (st = ensure(e, e->splitk, kSplitKScratchBytes))) return st;
+  if ((st = ensure(e, ln.hid, mt * hidw * es))) return st;
+  if (!e->bf16 && (st = ensure(e, ln.hid2, mt * 2 * c.d_adapter * es))) return st;
+  if ((st = ensure(e, ln.z, mt * c.d_out * es))) return st;
+  if (e->bf16 && c.split_small_gemms && (st = ensure(e, ln.splitk, kSplitKScratchBytes))) return st;
   return ENC_OK;
 }
 
@@ -516,12 +532,12 @@ encoder_status upload_plan(encoder* e, const std::vector<ClipSpan>& clips, const
 }
 
 template <typename T>
-encoder_status launch_linear_t(encoder* e, int kid, const void* A, int64_t lda, const WMat& Wt,
+encoder_status launch_linear_t(encoder* e, encoder::Lane& ln, int kid, const void* A, int64_t lda, const WMat& Wt,
                                const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
                                int epi, hipStream_t s, const float* pe = nullptr,
                                const int32_t* tok_pos = nullptr) {
   LinearArgs a{A, lda, Wt.w, bias, C, ldc, M, N, K, pe, tok_pos, Wt.q, Wt.s,
-               (float*)e->splitk.p, e->splitk.bytes};
+               (float*)ln.splitk.p, ln.splitk.bytes};
   LAUNCH(kid, launch_linear<T>(a, epi, kid, s));
   return ENC_OK;
 }
@@ -541,8 +557,8 @@ struct TapReq {
 // One pass over windows [p.win0, p.win0 + p.nwin): conv stack -> ... -> adapter, writing
 // rows [p.tok0, p.tok0 + p.ntok) of `out`.  Stops after `stop` (debug) when stop >= 0.
 template <typename T>
-encoder_status run_pass(encoder* e, const Pass& p, void* out, hipStream_t s, int stop = -1,
-                        int stop_layer = -1, const TapReq* taps = nullptr) {
+encoder_status run_pass(encoder* e, encoder::Lane& ln, const Pass& p, void* out, hipStream_t s,
+                        int stop = -1, int stop_layer = -1, const TapReq* taps = nullptr) {
   const encoder_cfg& c = e->cfg;
   const int C = c.conv_channels, d = c.d_model, W = c.window_tokens;
   PassGeom g;
@@ -552,15 +568,15 @@ encoder_status run_pass(encoder* e, const Pass& p, void* out, hipStream_t s, int
   g.n_tok = p.ntok;
   g.tok_pos = reinterpret_cast<const int32_t*>(e->tpos.p) + p.tok0;
   const int64_t M = p.ntok;
-  T* act1 = (T*)e->act1.p;
-  T* act2 = (T*)e->act2.p;
-  T* tokA = (T*)e->tokA.p;
-  float* resid = (float*)e->resid.p;
-  T* xn = (T*)e->xn.p;
-  T* qkv = (T*)e->qkv.p;
-  T* attn = (T*)e->attn.p;
-  T* hid = (T*)e->hid.p;
-  T* z = (T*)e->z.p;
+  T* act1 = (T*)ln.act1.p;
+  T* act2 = (T*)ln.act2.p;
+  T* tokA = (T*)ln.tokA.p;
+  float* resid = (float*)ln.resid.p;
+  T* xn = (T*)ln.xn.p;
+  T* qkv = (T*)ln.qkv.p;
+  T* attn = (T*)ln.attn.p;
+  T* hid = (T*)ln.hid.p;
+  T* z = (T*)ln.z.p;
 
   LAUNCH(ENC_K_CONV1, launch_conv1<T>(g, (const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
                                       e->conv1_w, e->conv1_b, C, act1, s));
@@ -570,24 +586,24 @@ encoder_status run_pass(encoder* e, const Pass& p, void* out, hipStream_t s, int
   LAUNCH(ENC_K_CONV3, launch_conv_igemm<T>(g, 3, act2, (const T*)e->conv3_w, e->conv3_b, C, tokA, s));
   if (stop == ST_CONV3) return ENC_OK;
   encoder_status st;
-  if ((st = launch_linear_t<T>(e, ENC_K_CONV_OUT, tokA, 16 * C, WMat{e->conv_out_w}, nullptr, resid, d, M,
+  if ((st = launch_linear_t<T>(e, ln, ENC_K_CONV_OUT, tokA, 16 * C, WMat{e->conv_out_w}, nullptr, resid, d, M,
                                d, 16 * C, EPI_PE, s, e->pe, g.tok_pos)))
     return st;
   if (stop == ST_EMBED) return ENC_OK;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = e->layers[l];
     LAUNCH(ENC_K_LN, launch_layernorm<T>(resid, L.ln1g, L.ln1b, xn, M, d, c.ln_eps, s));
-    if ((st = launch_linear_t<T>(e, ENC_K_QKV, xn, d, L.wqkv, L.bqkv, qkv, 3 * d, M, 3 * d, d,
+    if ((st = launch_linear_t<T>(e, ln, ENC_K_QKV, xn, d, L.wqkv, L.bqkv, qkv, 3 * d, M, 3 * d, d,
                                  EPI_BIAS, s)))
       return st;
     LAUNCH(ENC_K_ATTN, launch_attention<T>(qkv, g.wins, nullptr, g.n_win, c.n_heads, d, attn, s));
-    if ((st = launch_linear_t<T>(e, ENC_K_OPROJ, attn, d, L.wo, L.bo, resid, d, M, d, d, EPI_RESADD, s)))
+    if ((st = launch_linear_t<T>(e, ln, ENC_K_OPROJ, attn, d, L.wo, L.bo, resid, d, M, d, d, EPI_RESADD, s)))
       return st;
     LAUNCH(ENC_K_LN, launch_layernorm<T>(resid, L.ln2g, L.ln2b, xn, M, d, c.ln_eps, s));
-    if ((st = launch_linear_t<T>(e, ENC_K_FFN1, xn, d, L.w1, L.b1, hid, c.d_ffn, M, c.d_ffn, d,
+    if ((st = launch_linear_t<T>(e, ln, ENC_K_FFN1, xn, d, L.w1, L.b1, hid, c.d_ffn, M, c.d_ffn, d,
                                  EPI_BIAS_GELU, s)))
       return st;
-    if ((st = launch_linear_t<T>(e, ENC_K_FFN2, hid, c.d_ffn, L.w2, L.b2, resid, d, M, d, c.d_ffn,
+    if ((st = launch_linear_t<T>(e, ln, ENC_K_FFN2, hid, c.d_ffn, L.w2, L.b2, resid, d, M, d, c.d_ffn,
                                  EPI_RESADD, s)))
       return st;
     if (stop == ST_LAYER && stop_layer == l) return ENC_OK;
@@ -598,27 +614,27 @@ encoder_status run_pass(encoder* e, const Pass& p, void* out, hipStream_t s, int
                                 M * d * sizeof(float), hipMemcpyDeviceToDevice, s));
   }
   LAUNCH(ENC_K_LN, launch_layernorm<T>(resid, e->lnp_g, e->lnp_b, xn, M, d, c.ln_eps, s));
-  if ((st = launch_linear_t<T>(e, ENC_K_PROJ1, xn, d, e->proj1_w, e->proj1_b, hid, d, M, d, d,
+  if ((st = launch_linear_t<T>(e, ln, ENC_K_PROJ1, xn, d, e->proj1_w, e->proj1_b, hid, d, M, d, d,
                                EPI_BIAS_GELU, s)))
     return st;
-  if ((st = launch_linear_t<T>(e, ENC_K_PROJ2, hid, d, e->proj2_w, e->proj2_b, z, c.d_out, M,
+  if ((st = launch_linear_t<T>(e, ln, ENC_K_PROJ2, hid, d, e->proj2_w, e->proj2_b, z, c.d_out, M,
                                c.d_out, d, EPI_BIAS, s)))
     return st;
   if (stop == ST_HEAD) return ENC_OK;
   const int da = c.d_adapter;
   if (e->bf16) {
-    if ((st = launch_linear_t<T>(e, ENC_K_GATE_UP, z, c.d_out, e->gateup_w, nullptr, hid, da, M,
+    if ((st = launch_linear_t<T>(e, ln, ENC_K_GATE_UP, z, c.d_out, e->gateup_w, nullptr, hid, da, M,
                                  2 * da, c.d_out, EPI_SWIGLU, s)))
       return st;
   } else {
-    T* hid2 = (T*)e->hid2.p;
-    if ((st = launch_linear_t<T>(e, ENC_K_GATE_UP, z, c.d_out, e->gateup_w, nullptr, hid2, 2 * da,
+    T* hid2 = (T*)ln.hid2.p;
+    if ((st = launch_linear_t<T>(e, ln, ENC_K_GATE_UP, z, c.d_out, e->gateup_w, nullptr, hid2, 2 * da,
                                  M, 2 * da, c.d_out, EPI_BIAS, s)))
       return st;
     LAUNCH(ENC_K_OTHER, launch_swiglu_split<T>(hid2, M, 2 * da, hid, s));
   }
   T* dst = (T*)out + p.tok0 * c.d_out;
-  if ((st = launch_linear_t<T>(e, ENC_K_DOWN, hid, da, e->down_w, nullptr, dst, c.d_out, M, c.d_out,
+  if ((st = launch_linear_t<T>(e, ln, ENC_K_DOWN, hid, da, e->down_w, nullptr, dst, c.d_out, M, c.d_out,
                                da, EPI_BIAS, s)))
     return st;
   return ENC_OK;
@@ -689,8 +705,22 @@ encoder_status forward_impl(encoder* e, const float* pcm, const std::vector<int6
     t_max = std::max<int64_t>(t_max, n / c.hop);
   }
   const int64_t T = t_max;  // equal to every clip's frame count on the debug paths
-  encoder_status st = size_workspace(e, batch, n_frames, mt, mw, (int64_t)wins.size(), ntok);
+  // lanes: concurrent passes (bitwise the same as one after another), unless the call has a
+  // single pass, stops at a debug stage or is timed kernel by kernel
+  const int nl = (ps.size() > 1 && stop < 0 && !e->timing)
+                     ? (int)std::min<size_t>(ps.size(), (size_t)kLanes) : 1;
+  int64_t mtp = 1, mwp = 1;  // largest pass of the call
+  for (const Pass& p : ps) {
+    mtp = std::max<int64_t>(mtp, p.ntok);
+    mwp = std::max<int64_t>(mwp, p.nwin);
+  }
+  (void)mt;
+  (void)mw;
+  if ((int)e->lanes.size() < nl) e->lanes.resize(nl);
+  encoder_status st = size_call(e, batch, n_frames, (int64_t)wins.size(), ntok);
   if (st) return st;
+  for (int i = 0; i < nl; ++i)
+    if ((st = size_lane(e, e->lanes[i], mtp, mwp))) return st;
   if ((st = upload_plan(e, clips, wins, ps, s))) return st;
   if ((st = run_mel(e, pcm, batch, t_max, s))) return st;
   if (stop == ST_MEL) {
@@ -699,10 +729,31 @@ encoder_status forward_impl(encoder* e, const float* pcm, const std::vector<int6
     return ENC_OK;
   }
   if (taps) taps->ntok_total = ntok;
-  for (const Pass& p : ps) {
-    if (e->bf16) st = run_pass<bf16_t>(e, p, out, s, stop, stop_layer, taps);
-    else st = run_pass<float>(e, p, out, s, stop, stop_layer, taps);
-    if (st) return st;
+  auto pass = [&](encoder::Lane& ln, const Pass& p, hipStream_t ps_) {
+    return e->bf16 ? run_pass<bf16_t>(e, ln, p, out, ps_, stop, stop_layer, taps)
+                   : run_pass<float>(e, ln, p, out, ps_, stop, stop_layer, taps);
+  };
+  if (nl == 1) {
+    for (const Pass& p : ps)
+      if ((st = pass(e->lanes[0], p, s))) return st;
+  } else {
+    // fork after the log-mel, passes round-robin over the lanes, join on the caller's stream
+    if (!e->passes_ready) AE_HIP(hipEventCreateWithFlags(&e->passes_ready, hipEventDisableTiming));
+    for (int i = 0; i < nl; ++i) {
+      encoder::Lane& ln = e->lanes[i];
+      if (!ln.stream) AE_HIP(hipStreamCreateWithFlags(&ln.stream, hipStreamNonBlocking));
+      if (!ln.done) AE_HIP(hipEventCreateWithFlags(&ln.done, hipEventDisableTiming));
+    }
+    AE_HIP(hipEventRecord(e->passes_ready, s));
+    for (int i = 0; i < nl; ++i) AE_HIP(hipStreamWaitEvent(e->lanes[i].stream, e->passes_ready, 0));
+    for (size_t j = 0; j < ps.size(); ++j) {
+      encoder::Lane& ln = e->lanes[j % nl];
+      if ((st = pass(ln, ps[j], ln.stream))) return st;
+    }
+    for (int i = 0; i < nl; ++i) {
+      AE_HIP(hipEventRecord(e->lanes[i].done, e->lanes[i].stream));
+      AE_HIP(hipStreamWaitEvent(s, e->lanes[i].done, 0));
+    }
   }
   if (stop >= 0) {
     const Pass& p = ps[0];
@@ -710,15 +761,15 @@ encoder_status forward_impl(encoder* e, const float* pcm, const std::vector<int6
     const void* src = nullptr;
     int64_t n = 0;
     switch (stop) {
-      case ST_CONV1: src = e->act1.p; n = p.nwin * 4 * W * 64 * C; break;
-      case ST_CONV2: src = e->act2.p; n = p.nwin * 2 * W * 32 * C; break;
-      case ST_CONV3: src = e->tokA.p; n = p.ntok * 16 * C; break;
+      case ST_CONV1: src = e->lanes[0].act1.p; n = p.nwin * 4 * W * 64 * C; break;
+      case ST_CONV2: src = e->lanes[0].act2.p; n = p.nwin * 2 * W * 32 * C; break;
+      case ST_CONV3: src = e->lanes[0].tokA.p; n = p.ntok * 16 * C; break;
       case ST_EMBED:
       case ST_LAYER:
         if (dst_elems < p.ntok * c.d_model) return invalid("dst too small for this stage");
-        AE_HIP(hipMemcpyAsync(dst, e->resid.p, p.ntok * c.d_model * 4, hipMemcpyDeviceToDevice, s));
+        AE_HIP(hipMemcpyAsync(dst, e->lanes[0].resid.p, p.ntok * c.d_model * 4, hipMemcpyDeviceToDevice, s));
         return ENC_OK;
-      case ST_HEAD: src = e->z.p; n = p.ntok * c.d_out; break;
+      case ST_HEAD: src = e->lanes[0].z.p; n = p.ntok * c.d_out; break;
       case ST_OUT: src = out; n = p.ntok * c.d_out; break;
       default: return invalid("unknown stage");
     }
@@ -733,11 +784,18 @@ void free_all(encoder* e) {
   if (!e) return;
   hipSetDevice(e->device);
   hipDeviceSynchronize();
-  encoder::Buf* bufs[] = {&e->mel_raw, &e->max_key, &e->ctab, &e->wtab, &e->tpos, &e->rs_taps, &e->act1, &e->act2,
-                          &e->tokA, &e->resid, &e->xn, &e->qkv, &e->attn, &e->hid, &e->hid2,
-                          &e->z, &e->dbg, &e->splitk};
+  encoder::Buf* bufs[] = {&e->mel_raw, &e->max_key, &e->ctab, &e->wtab, &e->tpos, &e->rs_taps, &e->dbg};
   for (auto* b : bufs)
     if (b->p) hipFree(b->p);
+  for (auto& ln : e->lanes) {
+    encoder::Buf* lb[] = {&ln.act1, &ln.act2, &ln.tokA, &ln.resid, &ln.xn, &ln.qkv, &ln.attn,
+                          &ln.hid, &ln.hid2, &ln.z, &ln.splitk};
+    for (auto* b : lb)
+      if (b->p) hipFree(b->p);
+    if (ln.stream) hipStreamDestroy(ln.stream);
+    if (ln.done) hipEventDestroy(ln.done);
+  }
+  if (e->passes_ready) hipEventDestroy(e->passes_ready);
   if (e->wdev) hipFree(e->wdev);
   if (e->qdev) hipFree(e->qdev);
   if (e->fdev) hipFree(e->fdev);

@@ -527,10 +527,13 @@ def test_full_c3_pieces_equal_whole(full):
     pcm = to_dev(x)
     whole = enc.forward(pcm[None])[0]
     pieces = enc.forward_long(pcm, pieces_per_pass=8)
+    # one piece per pass: eight passes, run concurrently on the encoder's lanes
+    single = enc.forward_long(pcm, pieces_per_pass=1)
     torch.cuda.synchronize()
     assert pieces.shape == (6400, 2048)
     # windows are independent units, so the piece path reproduces the whole-clip path exactly
     assert torch.equal(whole, pieces)
+    assert torch.equal(whole, single)
     got = pieces.float().cpu().numpy()
     for wi in (0, 37, 63):
         res, _ = oracle_windows(x, Wt, O.FULL, [wi])
