@@ -948,13 +948,15 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const float* __restr
 //   Narrow 128x128, BK 64, 2 stages, two workgroups per CU
 //   Wide   256x128, BK 32, one-stage kernel, one workgroup per CU
 // BK 64 moves 128-byte row pieces, a whole L2 request each (64-byte pieces reach about two
-// thirds of the rate).  The GELU epilogue is VALU-heavy and runs after the K loop; with two
-// workgroups per CU one's epilogue overlaps the other's MFMAs, so it takes Narrow.  Otherwise
-// the kernel is chosen by its predicted time: rounds of tiles over the CUs times a per-tile
-// cost proportional to the tile's area.  The constants (microseconds per 10^6 x tile area x K)
-// are least-squares fits to measurements on MI355X over the tower's shapes at M = 6000 and
-// 7281 (QKV, o-proj, FFN2, proj1/2, adapter); the rule picks the fastest kernel, or one within
-// 2% of it, in every measured case.
+// thirds of the rate).  The kernel is chosen by its predicted time: rounds of tiles over the
+// CUs times a per-tile cost proportional to the tile's area.  The constants (microseconds per
+// 10^6 x tile area x K) are least-squares fits to measurements on MI355X over the tower's
+// shapes at M = 6000 and 7281 (QKV, o-proj, FFN2, proj1/2, adapter); the rule picks the
+// fastest kernel, or one within 2% of it, in every measured case.  A GELU epilogue is
+// VALU-heavy and runs after the K loop, exposed when a CU has no other workgroup to overlap
+// it: there a last round of Narrow that holds at most one workgroup per CU counts as half a
+// round (measured: FFN1 at M = 6000 runs 83 us in Large against 94 us in Narrow, proj1 30 us
+// in Narrow against 44 us in Large).
 using TileWide = Tile<256, 128, 4, 2, 32, 1>;
 using TileNarrow = Tile<128, 128, 2, 2, 64, 2>;
 using TileLarge = Tile<256, 256, 2, 4, 64, 1>;
@@ -980,12 +982,13 @@ inline int64_t tile_count(int64_t M, int64_t N, int64_t bm, int64_t bn) {
 }
 
 inline LinKind lin_kind(int64_t M, int64_t N, bool gelu_epilogue) {
-  if (gelu_epilogue) return LinKind::Narrow;
   const int64_t cus = cu_count();
   auto cost = [&](int64_t bm, int64_t bn, int64_t per_cu, double us_per_mel) {
+    const int64_t tiles = tile_count(M, N, bm, bn);
     const int64_t slots = per_cu * cus;
-    const int64_t rounds = (tile_count(M, N, bm, bn) + slots - 1) / slots;
-    return (double)rounds * us_per_mel * (double)(bm * bn);
+    double rounds = (double)((tiles + slots - 1) / slots);
+    if (gelu_epilogue && per_cu == 2 && tiles % slots != 0 && tiles % slots <= cus) rounds -= 0.5;
+    return rounds * us_per_mel * (double)(bm * bn);
   };
   const double large = cost(256, 256, 1, 0.393), tall = cost(128, 256, 1, 0.448);
   const double narrow = cost(128, 128, 2, 0.912), wide = cost(256, 128, 1, 0.502);

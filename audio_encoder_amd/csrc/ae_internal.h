@@ -49,25 +49,26 @@ template <> struct StoreT<bf16_t> {
 
 // Exact-form GELU x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)).  erfc(z) for z >= 0 is evaluated
 // with Abramowitz & Stegun's formula 7.1.28, erfc(z) ~ (1 + a1 z + ... + a6 z^6)^-16
-// (|error in erf| <= 3e-7; <= 2e-6 when evaluated in fp32): six FMAs, four squarings and one
-// hardware reciprocal (v_rcp_f32, 1 ulp; a correctly rounded division would cost ten
-// instructions and buy nothing at this error), no exponential.  The negative branch uses erfc
-// directly, so the left tail does not cancel 1 + erf; |GELU error| <= 1e-6 everywhere.
+// (|error in erf| <= 3e-7; <= 2e-6 when evaluated in fp32), with no exponential.  Two constant
+// factors are folded into the coefficients: z = |x| / sqrt 2 (a_i -> a_i 2^(-i/2), so the
+// polynomial runs on t = |x|) and 2^(1/16) (the sixteenth power doubles, so its reciprocal is
+// erfc(z) / 2 directly).  Since x Phi(x) = max(x, 0) - |x| erfc(|x| / sqrt 2) / 2 for either
+// sign, one FMA finishes it: six FMAs, four squarings, one hardware reciprocal (v_rcp_f32,
+// 1 ulp; a correctly rounded division costs ten instructions and buys nothing at this error),
+// one max.  The left tail never forms 1 + erf, so it does not cancel; |GELU error| <= 1e-6.
 __device__ inline float gelu_erf(float x) {
-  const float z = fabsf(x) * 0.70710678118654752f;
-  float p = fmaf(z, 0.0000430638f, 0.0002765672f);
-  p = fmaf(z, p, 0.0001520143f);
-  p = fmaf(z, p, 0.0092705272f);
-  p = fmaf(z, p, 0.0422820123f);
-  p = fmaf(z, p, 0.0705230784f);
-  p = fmaf(z, p, 1.0f);
+  const float t = fabsf(x);
+  float p = fmaf(t, 5.62129966e-06f, 5.10552090e-05f);  // 2^(1/16) a6 / 8, 2^(1/16) a5 / 2^2.5
+  p = fmaf(t, p, 3.96861370e-05f);                     // 2^(1/16) a4 / 4
+  p = fmaf(t, p, 3.42273924e-03f);                     // 2^(1/16) a3 / 2^1.5
+  p = fmaf(t, p, 2.20769985e-02f);                     // 2^(1/16) a2 / 2
+  p = fmaf(t, p, 5.20751630e-02f);                     // 2^(1/16) a1 / 2^0.5
+  p = fmaf(t, p, 1.04427378e+00f);                     // 2^(1/16)
   p *= p;
   p *= p;
   p *= p;
   p *= p;
-  const float erfc_z = __builtin_amdgcn_rcpf(p);
-  const float hx = 0.5f * x;
-  return x >= 0.0f ? fmaf(-hx, erfc_z, x) : hx * erfc_z;
+  return fmaf(-t, __builtin_amdgcn_rcpf(p), fmaxf(x, 0.0f));
 }
 __device__ inline float silu(float x) { return x / (1.0f + expf(-x)); }
 
