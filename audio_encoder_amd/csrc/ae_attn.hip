@@ -8,9 +8,10 @@
 //   S^T = K Q^T : 4 key blocks x 4 K-steps of v_mfma_f32_32x32x16_bf16.  K is staged in LDS
 //                 (XOR-swizzled 16-byte chunks); Q fragments come straight from HBM.  In the
 //                 transposed product each lane owns one query column, so the softmax max and
-//                 sum run over its own registers plus a single exchange with lane ^ 32.
+//                 sum run over its own registers plus a single exchange with lane ^ 32
+//                 (v_permlane32_swap, no LDS).
 //   O^T = V^T P^T: the unnormalised probabilities are packed to bf16 in registers and reordered
-//                 into the B-operand layout with one lane ^ 32 exchange per K-step (no LDS round
+//                 into the B-operand layout with two v_permlane32_swap per K-step (no LDS round
 //                 trip); V is staged transposed so each lane reads 8 consecutive keys of one
 //                 feature.  The 1/sum scale is applied to O in fp32.
 // fp32 path: one thread per query row with an online softmax over the window's keys.
@@ -87,75 +88,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   f32x16_t S[4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) S[kb][v] = 0.0f;
     const int key = kb * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int ch = ks * 2 + half;
       const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[key * HD + ((ch ^ (key & 7)) * 8)]);
-      S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[kb], 0, 0, 0);
+      S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16_t{} : S[kb], 0, 0, 0);
     }
   }
-  // softmax over keys for this lane's query: registers, then the other 32-lane half
+  // softmax over keys for this lane's query.  Keys past the valid length only exist in the
+  // last blocks (the test is uniform over the workgroup), so full blocks skip the mask.  The
+  // maximum is taken on the raw scores (the scale is positive), and exp(s/8 - m/8) is
+  // exp2(s c - m c) with c = log2(e) / 8: one FMA and one v_exp_f32 per score.
   float m = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < 4; ++kb) {
+    if (kb * 32 + 32 <= n) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-      const float sv = key < n ? S[kb][v] * 0.125f : -INFINITY;  // 1/sqrt(64)
-      S[kb][v] = sv;
-      m = fmaxf(m, sv);
+      for (int v = 0; v < 16; v += 4)
+        m = fmaxf(m, fmaxf(fmaxf(S[kb][v], S[kb][v + 1]), fmaxf(S[kb][v + 2], S[kb][v + 3])));
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        S[kb][v] = key < n ? S[kb][v] : -INFINITY;
+        m = fmaxf(m, S[kb][v]);
+      }
     }
-  m = fmaxf(m, __shfl_xor(m, 32));
+  }
+  // the other half of this query's keys sits in lane ^ 32: permlane32_swap hands each lane its
+  // partner's value in one of the two results, the other being its own
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  constexpr float kC = 0.18033688011112042f;  // log2(e) / sqrt(64)
+  const float mc = m * kC;
   float sum = 0.0f;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float e = __expf(S[kb][v] - m);
+      const float e = __builtin_amdgcn_exp2f(fmaf(S[kb][v], kC, -mc));
       S[kb][v] = e;
       sum += e;
     }
-  sum += __shfl_xor(sum, 32);
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
+    sum = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
   const float inv = 1.0f / sum;
 
-  // P^T as the B operand of O^T = V^T P^T: K-step s covers keys 16s..16s+15; lane half hh needs
-  // keys 16s + 8hh .. +8.  Its own registers hold keys 8g + 4*half + (0..3) (g = 2(s%2) + hh for
-  // the own part); the other four come from lane ^ 32.
+  // P^T as the B operand of O^T = V^T P^T: K-step s covers keys 16s..16s+15 of block s/2; lane
+  // half hh needs keys 16(s%2) + 8hh + (0..7) of that block, i.e. group g = 2(s%2) + hh (keys
+  // 8g..8g+7).  A lane holds keys 8g + 4*half + (0..3) of every group, so the half-0 lane owns
+  // the first four keys of each group and the half-1 lane the last four.  With X = group
+  // 2(s%2) and Y = group 2(s%2)+1 (two packed words each), permlane32_swap exchanges the upper
+  // half of X with the lower half of Y: afterwards every lane finds its eight keys as (X, Y).
   bf16x8_t pf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const int kb = s >> 1;
-    const int g_own = 2 * (s & 1) + half;        // group whose own half this lane keeps
-    const int g_send = 2 * (s & 1) + (1 - half);  // group the partner needs from this lane
-    uint32_t own0 = 0, own1 = 0, snd0 = 0, snd1 = 0;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t a0 = pack_bf16x2(S[kb][4 * g + 0], S[kb][4 * g + 1]);
-      const uint32_t a1 = pack_bf16x2(S[kb][4 * g + 2], S[kb][4 * g + 3]);
-      if (g == g_own) { own0 = a0; own1 = a1; }
-      if (g == g_send) { snd0 = a0; snd1 = a1; }
-    }
-    const uint32_t rc0 = (uint32_t)__shfl_xor((int)snd0, 32);
-    const uint32_t rc1 = (uint32_t)__shfl_xor((int)snd1, 32);
-    // keys 8g..8g+3 come from the half-0 lane, 8g+4..8g+7 from the half-1 lane
-    const uint4 pk = half == 0 ? make_uint4(own0, own1, rc0, rc1) : make_uint4(rc0, rc1, own0, own1);
-    pf[s] = __builtin_bit_cast(bf16x8_t, pk);
+    const int kb = s >> 1, g0 = 2 * (s & 1);
+    const uint32_t x0 = pack_bf16x2(S[kb][4 * g0 + 0], S[kb][4 * g0 + 1]);
+    const uint32_t x1 = pack_bf16x2(S[kb][4 * g0 + 2], S[kb][4 * g0 + 3]);
+    const uint32_t y0 = pack_bf16x2(S[kb][4 * g0 + 4], S[kb][4 * g0 + 5]);
+    const uint32_t y1 = pack_bf16x2(S[kb][4 * g0 + 6], S[kb][4 * g0 + 7]);
+    const auto r0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+    const auto r1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+    pf[s] = __builtin_bit_cast(bf16x8_t, make_uint4(r0[0], r1[0], r0[1], r1[1]));
   }
 
   // O^T blocks: rows = features 32*db + 8*(v/4) + 4*half + v%4, column = this lane's query
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     f32x16_t O;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) O[v] = 0.0f;
     const int feat = db * 32 + l32;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&Vt[feat * VTS + s * 16 + half * 8]);
-      O = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], O, 0, 0, 0);
+      O = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], s == 0 ? f32x16_t{} : O, 0, 0, 0);
     }
     if (q < n) {
       bf16_t* o = out + (int64_t)(tok0 + q) * d + h * HD + db * 32 + 4 * half;

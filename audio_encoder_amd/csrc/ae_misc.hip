@@ -4,7 +4,8 @@
 //
 // LayerNorm: one wave per row; each lane keeps its D/64 values in registers (float4 loads,
 // fully coalesced), so the row is read once; mean and biased variance come from two wave
-// reductions in fp32, and the normalised row is written in the GEMM operand type.
+// reductions in fp32 (DPP within rows of 16 lanes, then the four row sums), and the normalised
+// row is written in the GEMM operand type.
 #include <algorithm>
 
 #include "ae_internal.h"
@@ -16,6 +17,26 @@ __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
+}
+
+// Sum over the 64 lanes, returned in every lane, without LDS permutes: DPP swaps within each row
+// of 16 lanes (neighbours, pairs of neighbours, then the two half-rows and the two row halves
+// mirrored), then the four row sums read as scalars.
+template <int CTRL>
+__device__ inline float dpp_swap_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                    0xf, 0xf, false));
+}
+__device__ inline float wave_sum_dpp(float v) {
+  v = dpp_swap_add<0xb1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_swap_add<0x4e>(v);   // quad_perm [2,3,0,1]
+  v = dpp_swap_add<0x141>(v);  // row_half_mirror: lane i of 8 <- lane 7-i
+  v = dpp_swap_add<0x140>(v);  // row_mirror: lane i of 16 <- lane 15-i
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 template <typename T> struct Store4;
@@ -49,22 +70,24 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
   // gain and bias are loaded with the row, so their latency is not paid after the reductions
   float4 v[NJ], gg[NJ], bb[NJ];
 #pragma unroll
+  for (int j = 0; j < NJ; ++j) v[j] = xr[lane + 64 * j];
+#pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    v[j] = xr[lane + 64 * j];
     gg[j] = g4[lane + 64 * j];
     bb[j] = b4[lane + 64 * j];
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep the gain/bias loads ahead of the reductions
   float s = 0.0f;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
-  const float mean = wave_sum(s) * (1.0f / D);
+  const float mean = wave_sum_dpp(s) * (1.0f / D);
   float q = 0.0f;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const float a0 = v[j].x - mean, a1 = v[j].y - mean, a2 = v[j].z - mean, a3 = v[j].w - mean;
     q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
   }
-  const float rstd = rsqrtf(wave_sum(q) * (1.0f / D) + eps);
+  const float rstd = rsqrtf(wave_sum_dpp(q) * (1.0f / D) + eps);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int c4 = lane + 64 * j;
