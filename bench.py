@@ -204,6 +204,7 @@ def main():
     log("generating weights and input")
     weights = S.make_weights(cfg, seed=0)
     pcm_np, audio_s = make_input(args.workload)
+    free_before, _ = torch.cuda.mem_get_info()
     enc = B.Encoder(weights, cfg)
     pcm = torch.from_numpy(pcm_np).cuda()
     long_mode = args.workload in ("c3", "c4")
@@ -234,16 +235,19 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the total gives the mean, the gaps the median
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    ms_median = float(np.median([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]))
+    free_after, _ = torch.cuda.mem_get_info()
     tflops = wm["total_flops"] / (ms * 1e-3) / 1e12
     log(f"{ms:.3f} ms/step, {audio_s / (ms * 1e-3):.0f} audio-s/s, {tflops:.1f} TFLOP/s "
         f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak); wall {t_wall:.2f} s")
@@ -287,6 +291,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "median_ms_per_step": round(ms_median, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -300,7 +305,11 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "stage_ms": stage_ms,
-        "hbm_bytes": {"weights": wbytes, "workspace_high_water": ws},
+        # device memory: the library's weights and workspace high-water mark, and the drop in
+        # free device memory (hipMemGetInfo) from before the encoder was created to the end of
+        # the timed run (inputs and outputs included)
+        "hbm_bytes": {"weights": wbytes, "workspace_high_water": ws,
+                      "device_used_delta": int(free_before - free_after)},
     }
     print(json.dumps(line), flush=True)
     if args.copy_probe_mb:
