@@ -168,3 +168,35 @@ def test_forward_argument_checks():
     L = B.lib()
     assert L.encoder_forward(None, None, 1000, 1, None, None) == B.ENC_E_INVALID_ARG
     assert L.encoder_op_linear(None, None, None, None, 1, 1, 1, 0, 0, None) == B.ENC_E_INVALID_ARG
+
+
+def test_kernel_gelu_constants_follow_abramowitz_stegun_7_1_28():
+    """The device GELU (csrc/ae_internal.h, gelu_erf) folds 1/sqrt(2) and 2^(1/16) into the
+    coefficients of Abramowitz & Stegun 7.1.28, erfc(z) ~ (1 + a1 z + ... + a6 z^6)^-16.  Its seven
+    constants must be 2^(1/16) a_i 2^(-i/2) (a_0 = 1), and the formula, evaluated in float32 as
+    written, must stay within 1e-6 of x Phi(x) (float64 erf)."""
+    import math
+    src = open(os.path.join(os.path.dirname(HEADER), "..", "audio_encoder_amd", "csrc",
+                            "ae_internal.h")).read()
+    body = src[src.index("inline float gelu_erf"):src.index("inline float silu")]
+    consts = [float(c) for c in re.findall(r"([0-9]\.[0-9]+e[+-][0-9]+)f", body)]
+    # in Horner order: c6, c5, c4, c3, c2, c1, c0
+    a = [1.0, 0.0705230784, 0.0422820123, 0.0092705272, 0.0001520143, 0.0002765672, 0.0000430638]
+    want = [2 ** (1 / 16) * a[i] * 2 ** (-i / 2) for i in (6, 5, 4, 3, 2, 1, 0)]
+    assert len(consts) == 7
+    np.testing.assert_allclose(consts, want, rtol=2e-8)
+
+    f32 = np.float32
+    c = [f32(v) for v in consts]
+    x = np.linspace(-12, 12, 480001).astype(f32)
+    t = np.abs(x)
+    p = f32(np.float64(t) * c[0] + c[1])
+    for ci in c[2:]:
+        p = (np.float64(t) * p + ci).astype(f32)  # fmaf: one rounding
+    for _ in range(4):
+        p = (p * p).astype(f32)
+    with np.errstate(over="ignore", divide="ignore"):
+        r = (f32(1) / p).astype(f32)
+    g = (np.maximum(x, 0).astype(np.float64) - np.float64(t) * r).astype(f32)
+    exact = np.array([v * 0.5 * (1 + math.erf(v / math.sqrt(2))) for v in x.astype(np.float64)])
+    assert np.max(np.abs(g - exact)) < 1e-6
