@@ -586,7 +586,7 @@ __device__ inline void wait_vm_lds0() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
 }
 
-// NST-stage direct-to-LDS kernel (NST = 2..4).  Each stage is its own __shared__ array, so the
+// NST-stage direct-to-LDS kernel (NST = 2..8).  Each stage is its own __shared__ array, so the
 // compiler's wait-count tracking knows which DMA a fragment read depends on and never holds a
 // read back for the DMAs of other stages.
 //
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
                                                                    int32_t N, int32_t K, OM om, EpiP ep,
                                                                    int32_t n_tiles, int32_t pe_ld, int32_t gm,
                                                                    int32_t k_span) {
-  static_assert(NST >= 2 && NST <= 4, "stages");
+  static_assert(NST >= 2 && NST <= 8, "stages");
   constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
   constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
   constexpr int STG = (BM + BN) * BK;
@@ -623,12 +623,20 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
   __shared__ __attribute__((aligned(1024))) bf16_t st1[STG];
   __shared__ __attribute__((aligned(1024))) bf16_t st2[NST > 2 ? STG : 8];
   __shared__ __attribute__((aligned(1024))) bf16_t st3[NST > 3 ? STG : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t st4[NST > 4 ? STG : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t st5[NST > 5 ? STG : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t st6[NST > 6 ? STG : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t st7[NST > 7 ? STG : 8];
   auto stage = [&](auto sc) -> bf16_t* {
     constexpr int s = decltype(sc)::value;
     if constexpr (s == 0) return st0;
     else if constexpr (s == 1) return st1;
     else if constexpr (s == 2) return st2;
-    else return st3;
+    else if constexpr (s == 3) return st3;
+    else if constexpr (s == 4) return st4;
+    else if constexpr (s == 5) return st5;
+    else if constexpr (s == 6) return st6;
+    else return st7;
   };
 
   const int tid = threadIdx.x;
@@ -727,6 +735,10 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
   dma(1, st1);
   if constexpr (NST > 2) dma(2, st2);
   if constexpr (NST > 3) dma(3, st3);
+  if constexpr (NST > 4) dma(4, st4);
+  if constexpr (NST > 5) dma(5, st5);
+  if constexpr (NST > 6) dma(6, st6);
+  if constexpr (NST > 7) dma(7, st7);
   wait_vm_lds0<P * (NST - 1)>();  // tile 0 landed
   barrier();
   rd(st0, 0, 0);
@@ -761,6 +773,10 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
     step(kt + 1, std::integral_constant<int, 1>());
     if constexpr (NST > 2) step(kt + 2, std::integral_constant<int, 2>());
     if constexpr (NST > 3) step(kt + 3, std::integral_constant<int, 3>());
+    if constexpr (NST > 4) step(kt + 4, std::integral_constant<int, 4>());
+    if constexpr (NST > 5) step(kt + 5, std::integral_constant<int, 5>());
+    if constexpr (NST > 6) step(kt + 6, std::integral_constant<int, 6>());
+    if constexpr (NST > 7) step(kt + 7, std::integral_constant<int, 7>());
   }
   wait_vm_lds0<0>();  // the trailing zero-fill DMAs land before the stages are reused
   __syncthreads();
@@ -947,6 +963,7 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const float* __restr
 //   Tall   128x256, BK 64, 3 stages, one workgroup per CU
 //   Narrow 128x128, BK 64, 2 stages, two workgroups per CU
 //   Wide   256x128, BK 32, one-stage kernel, one workgroup per CU
+//   Small  64x64, BK 64, 4 stages; SmallW 64x128, BK 64, 6 stages (calls with few rows)
 // BK 64 moves 128-byte row pieces, a whole L2 request each (64-byte pieces reach about two
 // thirds of the rate).  The kernel is chosen by its predicted time: rounds of tiles over the
 // CUs times a per-tile cost proportional to the tile's area.  The constants (microseconds per
@@ -961,8 +978,10 @@ using TileWide = Tile<256, 128, 4, 2, 32, 1>;
 using TileNarrow = Tile<128, 128, 2, 2, 64, 2>;
 using TileLarge = Tile<256, 256, 2, 4, 64, 1>;
 using TileTall = Tile<128, 256, 2, 4, 64, 1>;
-constexpr int kLargeStages = 2, kTallStages = 3, kNarrowStages = 2;
-enum class LinKind { Narrow, Wide, Large, Tall };
+using TileSmall = Tile<64, 64, 2, 2, 64, 1>;    // four waves of 32x32
+using TileSmallW = Tile<64, 128, 2, 2, 64, 1>;  // four waves of 32x64
+constexpr int kLargeStages = 2, kTallStages = 3, kNarrowStages = 2, kSmallStages = 4, kSmallWStages = 6;
+enum class LinKind { Narrow, Wide, Large, Tall, Small, SmallW };
 
 int cu_count() {
   static int cached[64] = {0};
@@ -981,8 +1000,14 @@ inline int64_t tile_count(int64_t M, int64_t N, int64_t bm, int64_t bn) {
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
-inline LinKind lin_kind(int64_t M, int64_t N, bool gelu_epilogue) {
+inline LinKind lin_kind(int64_t M, int64_t N, bool gelu_epilogue, bool gate_epilogue) {
   const int64_t cus = cu_count();
+  // Few rows (a single clip, a 64 s piece): the tiles below leave most CUs idle and each runs
+  // its K loop at the latency of two stages.  Small tiles with deep stages spread the call over
+  // the CUs; the first kind whose tiles fit one per CU wins (the gate epilogue needs 64-column
+  // wave tiles).
+  if (!gate_epilogue && tile_count(M, N, 64, 64) <= cus) return LinKind::Small;
+  if (tile_count(M, N, 64, 128) <= cus) return LinKind::SmallW;
   auto cost = [&](int64_t bm, int64_t bn, int64_t per_cu, double us_per_mel) {
     const int64_t tiles = tile_count(M, N, bm, bn);
     const int64_t slots = per_cu * cus;
@@ -1031,9 +1056,11 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
                                                                      pe_ld, s, bq);
     }
     // Split K when even the 128x128 tiles (two per CU) would leave more than half the CUs idle
-    // (a single clip: M = 375).  Each K range writes an fp32 partial product into the scratch,
-    // and splitk_finish_kernel sums them in order and applies the epilogue.
-    if (a.ws && a.M > 0) {
+    // (a single clip: M = 375) and K is long (FFN2, conv_out, the adapter's down projection;
+    // for K = 1280 the small deep-stage tiles of the unsplit path are faster).  Each K range
+    // writes an fp32 partial product into the scratch, and splitk_finish_kernel sums them in
+    // order and applies the epilogue.
+    if (a.ws && a.M > 0 && a.K >= 4096) {
       const int64_t cus = cu_count();
       const int64_t tiles = tile_count(a.M, a.N, 128, 128);
       const int64_t step = TileNarrow::BK * kNarrowStages;
@@ -1058,7 +1085,13 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
   } else {
     if (a.Wq) return hipErrorInvalidValue;
   }
-  switch (lin_kind(a.M, a.N, EPI == EPI_BIAS_GELU)) {
+  switch (lin_kind(a.M, a.N, EPI == EPI_BIAS_GELU, EPI == EPI_SWIGLU)) {
+    case LinKind::Small:
+      if constexpr (EPI != EPI_SWIGLU)
+        return run<T, TileSmall, ALinear<T>, OLinear, EPI, TAG, kSmallStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+      return hipErrorInvalidValue;
+    case LinKind::SmallW:
+      return run<T, TileSmallW, ALinear<T>, OLinear, EPI, TAG, kSmallWStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
     case LinKind::Large:
       return run<T, TileLarge, ALinear<T>, OLinear, EPI, TAG, kLargeStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
     case LinKind::Tall:

@@ -89,10 +89,10 @@ typedef struct {
   int32_t split_small_gemms; /* 0 (default): every GEMM accumulates K in one order, so a clip's
                              embeddings are bitwise independent of what else shares its call
                              or pass.  1 (bf16): GEMMs too small to fill the GPU (a single
-                             clip) split K over workgroups and sum the fp32 partial products
-                             in a second kernel, in K-range order - faster for small calls,
-                             but rounded differently from the same rows in a large call.
-                             Needs 64 MiB of extra workspace.                               */
+                             clip) with K >= 4096 split K over workgroups and sum the fp32
+                             partial products in a second kernel, in K-range order - faster
+                             for small calls, but rounded differently from the same rows in a
+                             large call.  Needs 64 MiB of extra workspace.                  */
 } encoder_cfg;
 
 typedef struct encoder encoder; /* opaque handle */
