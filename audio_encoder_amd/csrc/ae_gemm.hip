@@ -1134,6 +1134,43 @@ hipError_t launch_linear(const LinearArgs& a, int epi, int tag, hipStream_t s) {
   }
 }
 
+// Few conv rows (a single clip, a 64 s piece): 256x256 tiles would leave over half the CUs idle
+// through a K loop of 135 steps.  128x128 (4 waves, 8 stages) or 128x256 (8 waves, 6 stages)
+// tiles spread it over more CUs; the smaller tile is taken when its tiles fit one per CU.  K is
+// accumulated in the same order, so rows do not depend on the tile.
+using TileConvT = Tile<128, 256, 2, 4, 32, 1>;
+using TileConvN = Tile<128, 128, 2, 2, 32, 1>;
+constexpr int kConvTStages = 6, kConvNStages = 8;
+
+template <typename T, class TL, int NST, int LEVEL, int TAG>
+hipError_t conv_run(const AConv<T>& as, const T* wpk, int32_t C, const PassGeom& g, int rows_per_win,
+                    int Fout, int Lout_max, int64_t m_rows, const EpiP& ep, hipStream_t s) {
+  // a wave covers TL::WTM rows of the tile
+  if (rows_per_win >= TL::WTM) {
+    OConv<LEVEL, true> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
+    return run<T, TL, AConv<T>, OConv<LEVEL, true>, EPI_BIAS_GELU, TAG, NST>(as, wpk, C, 9 * C, om, ep,
+                                                                            m_rows, 0, s);
+  }
+  OConv<LEVEL, false> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
+  return run<T, TL, AConv<T>, OConv<LEVEL, false>, EPI_BIAS_GELU, TAG, NST>(as, wpk, C, 9 * C, om, ep,
+                                                                           m_rows, 0, s);
+}
+
+template <typename T, int LEVEL, int TAG>
+hipError_t conv_dispatch(const AConv<T>& as, const T* wpk, int32_t C, const PassGeom& g, int rows_per_win,
+                         int Fout, int Lout_max, int64_t m_rows, const EpiP& ep, hipStream_t s) {
+  const int64_t cus = cu_count();
+  if (std::is_same<T, bf16_t>::value && 2 * tile_count(m_rows, C, 256, 256) < cus) {
+    if (tile_count(m_rows, C, 128, 128) <= cus)
+      return conv_run<T, TileConvN, kConvNStages, LEVEL, TAG>(as, wpk, C, g, rows_per_win, Fout, Lout_max,
+                                                              m_rows, ep, s);
+    return conv_run<T, TileConvT, kConvTStages, LEVEL, TAG>(as, wpk, C, g, rows_per_win, Fout, Lout_max,
+                                                            m_rows, ep, s);
+  }
+  return conv_run<T, TileConv, kConvStages, LEVEL, TAG>(as, wpk, C, g, rows_per_win, Fout, Lout_max, m_rows,
+                                                        ep, s);
+}
+
 template <typename T>
 hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T* wpk,
                              const float* bias, int32_t C, T* out, hipStream_t s) {
@@ -1148,25 +1185,9 @@ hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T*
   if (m_rows >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int64_t out_rows = level == 2 ? (int64_t)g.n_win * Lout_max * Fout : g.n_tok * Fout;
   EpiP ep{bias, out, nullptr, nullptr, out_rows * C * (int64_t)sizeof(T)};
-  // a wave covers TileConv::WTM rows of the tile
-  if (rows_per_win >= TileConv::WTM) {
-    if (level == 2) {
-      OConv<2, true> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
-      return run<T, TileConv, AConv<T>, OConv<2, true>, EPI_BIAS_GELU, ENC_K_CONV2, kConvStages>(
-          as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
-    }
-    OConv<3, true> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
-    return run<T, TileConv, AConv<T>, OConv<3, true>, EPI_BIAS_GELU, ENC_K_CONV3, kConvStages>(
-        as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
-  }
-  if (level == 2) {
-    OConv<2, false> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
-    return run<T, TileConv, AConv<T>, OConv<2, false>, EPI_BIAS_GELU, ENC_K_CONV2, kConvStages>(
-        as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
-  }
-  OConv<3, false> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
-  return run<T, TileConv, AConv<T>, OConv<3, false>, EPI_BIAS_GELU, ENC_K_CONV3, kConvStages>(
-      as, wpk, C, 9 * C, om, ep, m_rows, 0, s);
+  if (level == 2)
+    return conv_dispatch<T, 2, ENC_K_CONV2>(as, wpk, C, g, rows_per_win, Fout, Lout_max, m_rows, ep, s);
+  return conv_dispatch<T, 3, ENC_K_CONV3>(as, wpk, C, g, rows_per_win, Fout, Lout_max, m_rows, ep, s);
 }
 
 template hipError_t launch_linear<bf16_t>(const LinearArgs&, int, int, hipStream_t);
