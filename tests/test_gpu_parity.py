@@ -65,15 +65,15 @@ def test_op_layernorm(D, dtype):
     assert np.abs(got - ref).max() <= tol * np.abs(ref).max()
 
 
-# (M, N, K): small and ragged shapes, and one of each tile path (128x128: N = 1280 / 3840 /
-# N < 2048 while the tiles fit two per CU; 256x128: K < 2048 otherwise; 256x256 four-stage:
-# K >= 2048 otherwise, here with K not a multiple of the 128-deep stage group and M, N not
-# multiples of the tile)
+# (M, N, K): small and ragged shapes (M, N, K not multiples of any tile), and each tile kind of
+# the bf16 dispatch: 64x64 / 4 stages while those tiles fit one per CU (most small shapes here);
+# 64x128 / 6 stages while those do ((300, 3840), (800, 1280), (375, 3840)); otherwise the cost
+# model: 256x256 (N = 1280 with M = 7000 / 6600; (6000, 2048) without GELU), 128x256
+# ((6000, 1280)) and 128x128 ((6000, 2048) with the GELU epilogue)
 LINEAR_SHAPES = [(1, 64, 64), (130, 200, 72), (300, 3840, 1280), (257, 1280, 5120),
                  (129, 1024, 4320), (64, 128, 8), (333, 2560, 1032), (301, 2112, 2216),
-                 (77, 4096, 2048),
-                 # N = 1280 with more 128x128 tiles than two per CU: 256x128 / 256x256 paths
-                 (7000, 1280, 1024), (6600, 1280, 2056)]
+                 (77, 4096, 2048), (800, 1280, 5120), (375, 3840, 1280),
+                 (7000, 1280, 1024), (6600, 1280, 2056), (6000, 1280, 1280), (6000, 2048, 1280)]
 
 
 @pytest.mark.parametrize("M,N,K", LINEAR_SHAPES)
