@@ -148,13 +148,18 @@ ENC_API encoder_status encoder_memory_stats(const encoder* e, int64_t* weight_by
 /* Whole-clip path.  pcm: device float32 [batch, n_samples] (independent equal-length clips; each
  * is normalised by its own log-mel maximum).  out: device [batch, F, d_out] with F from
  * encoder_output_frames, bf16 for ENC_BF16 and float32 for ENC_F32.  n_samples > n_fft/2,
- * batch >= 1.  Inputs above max_tokens_per_pass run in several window-aligned passes. */
+ * batch >= 1.  Inputs above max_tokens_per_pass run in several window-aligned passes.  Passes of
+ * one call run concurrently on up to four internal streams (joined back onto `stream` before
+ * the call's work ends), and a single-pass call of 4000 tokens or more runs as two concurrent
+ * halves; every window's output rows are the same whatever pass it lands in. */
 ENC_API encoder_status encoder_forward(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
                                void* out, void* stream);
 
 /* Long-audio path for one recording (Ossicle card, "Long Audio").  The log-mel and its maximum
  * are computed over the whole recording, which is then encoded in pieces of piece_tokens tokens
- * (8*piece_tokens frames), pieces_per_pass pieces per pass.  The last piece may be partial.
+ * (8*piece_tokens frames), pieces_per_pass pieces per pass (passes run concurrently as for
+ * encoder_forward; a single pass of 4000 tokens or more runs as two halves of whole pieces).
+ * The last piece may be partial.
  * Output rows are written in time order: out [F, d_out].  Equals encoder_forward(batch = 1) up to
  * summation order. */
 ENC_API encoder_status encoder_forward_long(encoder* e, const float* pcm, int64_t n_samples,
