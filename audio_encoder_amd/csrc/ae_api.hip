@@ -80,8 +80,11 @@ static int64_t max_tokens(const encoder_cfg& c) {
   return c.max_tokens_per_pass > 0 ? c.max_tokens_per_pass : 8192;
 }
 static int64_t max_windows(const encoder_cfg& c) { return max_tokens(c) / c.window_tokens + 32; }
-// passes of one call that run at once (each lane holds one pass's activations)
-constexpr int kLanes = 4;
+// Passes of one call that run at once (each lane holds one pass's activations).  HIP maps
+// streams onto four hardware queues by default; three lanes plus the caller's stream keep one
+// queue each.  An hour at one 64 s piece per pass (57 passes) measured 160 ms with four lanes,
+// 153 with two, 130 with three, 141 / 130 / 131 / 144 with five to eight.
+constexpr int kLanes = 3;
 // A single-pass call of at least this many tokens runs as two concurrent halves.  Measured on
 // MI355X with 30 s clips: 12 clips (4500 tokens) 11.8 -> 11.1 ms, 16 clips 13.8 -> 13.2 ms;
 // at 3750 tokens the halves are too small to gain (9.9 -> 10.1 ms).

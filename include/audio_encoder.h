@@ -149,7 +149,7 @@ ENC_API encoder_status encoder_memory_stats(const encoder* e, int64_t* weight_by
  * is normalised by its own log-mel maximum).  out: device [batch, F, d_out] with F from
  * encoder_output_frames, bf16 for ENC_BF16 and float32 for ENC_F32.  n_samples > n_fft/2,
  * batch >= 1.  Inputs above max_tokens_per_pass run in several window-aligned passes.  Passes of
- * one call run concurrently on up to four internal streams (joined back onto `stream` before
+ * one call run concurrently on up to three internal streams (joined back onto `stream` before
  * the call's work ends), and a single-pass call of 4000 tokens or more runs as two concurrent
  * halves; every window's output rows are the same whatever pass it lands in. */
 ENC_API encoder_status encoder_forward(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
