@@ -519,6 +519,10 @@ def test_full_c2_batch_sampled_windows(full):
     # determinism
     y2 = enc.forward(to_dev(xs))
     assert torch.equal(y, y2)
+    # the 6000-token call runs as two concurrent 3000-token passes; a clip's rows equal its own
+    # single-clip encoding bit for bit, in either half
+    for b in (0, 8, 15):
+        assert torch.equal(y[b], enc.forward(to_dev(xs[b:b + 1]))[0])
 
 
 def test_full_c3_pieces_equal_whole(full):
