@@ -13,9 +13,10 @@
 // bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950 with fp32 accumulators.  Tiles move from global
 // memory straight into LDS with buffer_load_dwordx4 ... lds (16 bytes per lane, no VGPR
 // staging); LDS rows are XOR-swizzled so the fragment reads are free of bank conflicts; the
-// epilogue stages accumulator rows through LDS for coalesced stores.  Two kernels:
-//   gemm_dtl_kernel  one K tile in flight, all fragments of a tile read before the next DMA;
-//   gemm_ilv_kernel  NST stages in separate LDS arrays, refill DMAs spread over the MFMAs.
+// epilogue stages accumulator rows through LDS for coalesced stores.  Three kernels:
+//   gemm_dtl_kernel   one K tile in flight, all fragments of a tile read before the next DMA;
+//   gemm_ilv_kernel   NST stages in separate LDS arrays, refill DMAs spread over the MFMAs;
+//   gemm_ilvq_kernel  the staged kernel with int4 weights expanded into the stages' B tiles.
 // The tile shape and kernel per call are chosen in the dispatch section at the end.
 //
 // fp32 path (the fp32 tiny configuration): a 64x64 VALU tile with the same loaders and
@@ -412,14 +413,10 @@ struct BQuant {
 //   issue the DMA of the next tile into the other buffer -> MFMAs.
 // The DMA of tile kt+1 thus overlaps the MFMAs of tile kt, and the compiler's conservative
 // wait before LDS reads never falls between a DMA and the fragment reads it could delay.
-// BQ: B is int4 (BQuant): each thread loads 16-byte chunks of 32 weights into registers with the
-// next tile's A DMA, and at the top of the next iteration dequantises them into the B tile (same
-// swizzled bf16 layout as the DMA path) before the barrier.
-template <class TL, class AS, class OM, int EPI, typename OT, int TAG, bool BQ = false>
+template <class TL, class AS, class OM, int EPI, typename OT, int TAG>
 __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const bf16_t* __restrict__ Bw,
                                                                    int32_t N, int32_t K, OM om, EpiP ep,
-                                                                   int32_t n_tiles, int32_t pe_ld, int32_t gm,
-                                                                   BQuant bq) {
+                                                                   int32_t n_tiles, int32_t pe_ld, int32_t gm) {
   constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
   constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
   constexpr int SMEM = 2 * (BM + BN) * BK;
@@ -427,11 +424,8 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
   static_assert(NW * SR * (WTN + 4) * 4 <= SMEM * 2, "epilogue staging must fit in the tiles");
   constexpr int ROWS_PER_DMA = 1024 / (BK * 2);           // tile rows filled by one instruction
   constexpr int ADMA = BM / ROWS_PER_DMA / NW;            // DMA instructions per wave per tile
-  constexpr int BDMA = BQ ? 0 : BN / ROWS_PER_DMA / NW;
-  static_assert(ADMA * ROWS_PER_DMA * NW == BM && (BQ || BDMA * ROWS_PER_DMA * NW == BN), "dma split");
-  constexpr int QSEG = BK / 32;                 // 32-weight int4 chunks per tile row
-  constexpr int QCH = BN * QSEG;                // chunks per tile
-  static_assert(!BQ || QCH <= TL::NT, "one int4 chunk per thread at most");
+  constexpr int BDMA = BN / ROWS_PER_DMA / NW;
+  static_assert(ADMA * ROWS_PER_DMA * NW == BM && BDMA * ROWS_PER_DMA * NW == BN, "dma split");
   constexpr int KS = BK / 16;
   __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM];
   bf16_t* const sA = smem;
@@ -488,47 +482,6 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
     }
   };
 
-  // int4 B: thread tid < QCH owns tile row qr, 32-weight segment qs
-  const int qr = tid / QSEG, qs = tid % QSEG;
-  const bool qact = BQ && tid < QCH;
-  const bool qrow_ok = qact && n0 + qr < N;
-  const uint8_t* qrow = BQ ? bq.q + (int64_t)(n0 + qr) * (K / 2) : nullptr;
-  const bf16_t* srow = BQ ? bq.s + (int64_t)(n0 + qr) * (K / 128) : nullptr;
-  uint4 qv = make_uint4(0u, 0u, 0u, 0u);
-  bf16_t sv = 0;
-  auto qload = [&](int kt) {
-    if constexpr (BQ) {
-      qv = make_uint4(0u, 0u, 0u, 0u);
-      sv = 0;
-      const int k = kt * BK + qs * 32;
-      if (qrow_ok && k < K) {
-        qv = *reinterpret_cast<const uint4*>(qrow + k / 2);
-        sv = srow[k / 128];
-      }
-    }
-  };
-  auto qstore = [&](int buf) {
-    if constexpr (BQ) {
-      if (qact) {
-        const float sf = bf16_to_f32(sv);
-        const uint32_t w4[4] = {qv.x, qv.y, qv.z, qv.w};
-        bf16_t* row = sB + buf * BN * BK + qr * BK;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {  // 8 weights per word: nibble j holds weight 8c + j
-          uint32_t o[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int q0 = (int)(w4[c] << (28 - 8 * i)) >> 28;
-            const int q1 = (int)(w4[c] << (24 - 8 * i)) >> 28;
-            o[i] = pack_bf16x2((float)q0 * sf, (float)q1 * sf);
-          }
-          const int lc = qs * 4 + c;
-          *reinterpret_cast<uint4*>(row + ((lc ^ swz<BK>(qr)) * 8)) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-      }
-    }
-  };
-
   f32x16_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -543,11 +496,9 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
   bf16x8_t af[KS][TM], bfr[KS][TN];
   const int nk = (K + BK - 1) / BK;
   dma(0, 0);
-  qload(0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA of tile kt has landed
-    qstore(cur);                         // int4 B: dequantise tile kt into buffer cur
     __syncthreads();                     // every wave's DMA landed; buffer cur^1 is free
     const bf16_t* pa = sA + cur * BM * BK + arow0 * BK;
     const bf16_t* pb = sB + cur * BN * BK + brow0 * BK;
@@ -559,10 +510,7 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_dtl_kernel(AS as, const
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[ks][j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * BK + ch);
     }
-    if (kt + 1 < nk) {
-      dma(kt + 1, cur ^ 1);
-      qload(kt + 1);
-    }
+    if (kt + 1 < nk) dma(kt + 1, cur ^ 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -785,6 +733,247 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
                                           m0 + wm * TL::WTM, n0 + wn * TL::WTN, N, om, ep, pe_ld, lane);
 }
 
+// s_waitcnt vmcnt(VM) only (LDS operations may stay in flight)
+template <int VM>
+__device__ inline void wait_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The staged kernel with int4 weights (BQuant): A moves by LDS DMA as in gemm_ilv_kernel; B
+// arrives as 16-byte chunks of 32 int4 weights plus their bf16 scale, loaded into registers one
+// tile ahead of the stage they fill and expanded with the scale into the same swizzled bf16
+// layout right after the barrier that frees the stage.  Order of memory operations per K step:
+// [int4 chunk and scale of tile kt+NST+1, A DMAs of tile kt+NST], so the wait before the
+// expansion leaves the step's A DMAs in flight, and the wait before the barrier (for tile kt+1's
+// A) counts the same operations as in the bf16 kernel plus two per step.  The prologue issues
+// [int4(t), A(t)] for t < NST-1, then int4(NST-1), int4(NST), A(NST-1), which keeps every loop
+// wait exact or stricter.  K is accumulated in the same order as in the bf16 kernels.
+template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG>
+__global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilvq_kernel(AS as, int32_t N, int32_t K, OM om, EpiP ep,
+                                                                    int32_t n_tiles, int32_t pe_ld, int32_t gm,
+                                                                    BQuant bq) {
+  static_assert(NST >= 2 && NST <= 6, "stages");
+  constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
+  constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
+  static_assert(BK == 64, "int4 groups of 128 span two BK 64 tiles");
+  constexpr int STG = (BM + BN) * BK;
+  constexpr int SR = (NW * 32 * (WTN + 4) * 4 <= STG * 2) ? 32
+                     : (NW * 16 * (WTN + 4) * 4 <= STG * 2) ? 16 : 8;
+  static_assert(NW * SR * (WTN + 4) * 4 <= STG * 2, "epilogue staging must fit in one stage");
+  constexpr int ROWS_PER_DMA = 1024 / (BK * 2);
+  constexpr int ADMA = BM / ROWS_PER_DMA / NW;
+  static_assert(ADMA * ROWS_PER_DMA * NW == BM, "dma split");
+  constexpr int QOPS = 2;                           // int4 chunk + scale loads per thread per tile
+  constexpr int PS = ADMA + QOPS;                   // memory operations per thread per K step
+  static_assert(PS * NST < 64, "vmcnt range");
+  constexpr int QSEG = BK / 32;                     // 32-weight chunks per tile row
+  constexpr int QCH = BN * QSEG;                    // chunks per tile
+  static_assert(QCH <= TL::NT, "one int4 chunk per thread at most");
+  constexpr int KS = BK / 16;
+  static_assert(KS % 2 == 0, "the fragment double buffer alternates within a tile");
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[STG];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[STG];
+  __shared__ __attribute__((aligned(NST > 2 ? 1024 : 16))) bf16_t st2[NST > 2 ? STG : 8];
+  __shared__ __attribute__((aligned(NST > 3 ? 1024 : 16))) bf16_t st3[NST > 3 ? STG : 8];
+  __shared__ __attribute__((aligned(NST > 4 ? 1024 : 16))) bf16_t st4[NST > 4 ? STG : 8];
+  __shared__ __attribute__((aligned(NST > 5 ? 1024 : 16))) bf16_t st5[NST > 5 ? STG : 8];
+  auto stage = [&](auto sc) -> bf16_t* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return st0;
+    else if constexpr (s == 1) return st1;
+    else if constexpr (s == 2) return st2;
+    else if constexpr (s == 3) return st3;
+    else if constexpr (s == 4) return st4;
+    else return st5;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / TL::WGN, wn = wv % TL::WGN;
+  const TileCoord tc = tile_coord(n_tiles, gm);
+  const int64_t m0 = (int64_t)tc.mt * BM;
+  const int n0 = tc.nt * BN;
+  if (!as.tile_live(m0, BM)) return;
+
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(as.base(), as.bytes());
+  const __amdgpu_buffer_rsrc_t rq_rsrc = make_rsrc(bq.q, (int64_t)N * (K / 2));
+  const __amdgpu_buffer_rsrc_t rs_rsrc = make_rsrc(bq.s, (int64_t)N * (K / 128) * 2);
+  constexpr int CPR = BK / 8;
+  typename AS::BRow arow[ADMA];
+  int achunk[ADMA];
+#pragma unroll
+  for (int j = 0; j < ADMA; ++j) {
+    const int r = (wv * ADMA + j) * ROWS_PER_DMA + lane / CPR;
+    achunk[j] = (lane % CPR) ^ swz<BK>(r);
+    arow[j] = as.brow(m0 + r);
+  }
+  auto dma = [&](int kt, bf16_t* st) {
+#pragma unroll
+    for (int j = 0; j < ADMA; ++j) {
+      const int k = kt * BK + achunk[j] * 8;
+      const uint32_t off = as.boff(arow[j], as.kc(k));
+      bf16_t* dst = st + (wv * ADMA + j) * ROWS_PER_DMA * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+  };
+  // int4 B: thread tid < QCH owns tile row qr, 32-weight segment qs (rows past N, threads
+  // without a chunk and tiles past K read zeros through out-of-range offsets)
+  const int qr = tid / QSEG, qs = tid % QSEG;
+  const bool qok = tid < QCH && n0 + qr < N;
+  const uint32_t qbase = qok ? (uint32_t)(n0 + qr) * (uint32_t)(K / 2) : 0u;
+  const uint32_t sbase = qok ? (uint32_t)(n0 + qr) * (uint32_t)(K / 128) * 2u : 0u;
+  auto qload = [&](int kt, uint4& qv, uint32_t& sv) {
+    const int k = kt * BK + qs * 32;
+    const bool ok = qok && k < K;
+    qv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       rq_rsrc, ok ? (int)(qbase + (uint32_t)k / 2u) : (int)0x80000000, 0, 0));
+    sv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+        rs_rsrc, ok ? (int)(sbase + (uint32_t)(k / 128) * 2u) : (int)0x80000000, 0, 0);
+  };
+  auto qstore = [&](bf16_t* st, const uint4& qv, uint32_t sv) {
+    if (tid < QCH) {
+      const float sf = __uint_as_float(sv << 16);
+      const uint32_t w4[4] = {qv.x, qv.y, qv.z, qv.w};
+      bf16_t* row = st + BM * BK + qr * BK;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {  // 8 weights per word: nibble j holds weight 8c + j
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q0 = (int)(w4[c] << (28 - 8 * i)) >> 28;
+          const int q1 = (int)(w4[c] << (24 - 8 * i)) >> 28;
+          o[i] = pack_bf16x2((float)q0 * sf, (float)q1 * sf);
+        }
+        const int lc = qs * 4 + c;
+        *reinterpret_cast<uint4*>(row + ((lc ^ swz<BK>(qr)) * 8)) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int aoff = (wm * TL::WTM + l32) * BK;
+  const int boff = BM * BK + (wn * TL::WTN + l32) * BK;
+  const int sw = swz<BK>(l32);
+  bf16x8_t fa[2][TM], fb[2][TN];
+  auto rd = [&](const bf16_t* st, int ks, int buf) {
+    const int ch = ((ks * 2 + half) ^ sw) * 8;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoff + i * 32 * BK + ch);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boff + j * 32 * BK + ch);
+  };
+  auto mm = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  };
+  auto barrier = [&]() {
+    cbar();
+    __builtin_amdgcn_s_barrier();
+    cbar();
+  };
+
+  const int nk = (K + BK * NST - 1) / (BK * NST) * NST;
+  // prologue: [q(t), A(t)] for t < NST-1, then q(NST-1), q(NST), A(NST-1)
+  uint4 qvp[NST];
+  uint32_t svp[NST];
+  uint4 qv;
+  uint32_t sv;
+  {
+    auto pro = [&](auto tc_) {
+      constexpr int t = decltype(tc_)::value;
+      if constexpr (t < NST - 1) {
+        qload(t, qvp[t], svp[t]);
+        dma(t, stage(std::integral_constant<int, t>()));
+      }
+    };
+    pro(std::integral_constant<int, 0>());
+    pro(std::integral_constant<int, 1>());
+    pro(std::integral_constant<int, 2>());
+    pro(std::integral_constant<int, 3>());
+    pro(std::integral_constant<int, 4>());
+    qload(NST - 1, qvp[NST - 1], svp[NST - 1]);
+    qload(NST, qv, sv);
+    dma(NST - 1, stage(std::integral_constant<int, NST - 1>()));
+    // expand the first NST B tiles as their chunks arrive (operations issued after q(t):
+    // A(t), [q(u), A(u)] for t < u < NST-1, q(NST-1), q(NST), A(NST-1))
+    auto expand = [&](auto tc_) {
+      constexpr int t = decltype(tc_)::value;
+      if constexpr (t < NST - 1) {
+        wait_vm<ADMA + (NST - 2 - t) * PS + 2 * QOPS + ADMA>();
+        qstore(stage(std::integral_constant<int, t>()), qvp[t], svp[t]);
+      } else if constexpr (t == NST - 1) {
+        wait_vm<QOPS + ADMA>();
+        qstore(stage(std::integral_constant<int, t>()), qvp[t], svp[t]);
+      }
+    };
+    expand(std::integral_constant<int, 0>());
+    expand(std::integral_constant<int, 1>());
+    expand(std::integral_constant<int, 2>());
+    expand(std::integral_constant<int, 3>());
+    expand(std::integral_constant<int, 4>());
+    expand(std::integral_constant<int, 5>());
+  }
+  // tile 0's A landed (operations issued after A(0): [q(u), A(u)] for 0 < u < NST-1, q(NST-1),
+  // q(NST), A(NST-1)); every wave's expanded B tiles are written
+  wait_vm_lds0<(NST - 2) * PS + 2 * QOPS + ADMA>();
+  barrier();
+  rd(st0, 0, 0);
+
+  auto step = [&](int kt, auto sc) {
+    constexpr int s = decltype(sc)::value;
+    bf16_t* cur = stage(sc);
+    const bf16_t* nxt = stage(std::integral_constant<int, (s + 1) % NST>());
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      rd(cur, ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mm(ks & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm_lds0<PS * (NST - 2)>();  // tile kt+1's A landed; this wave's reads of tile kt retired
+    barrier();
+    rd(nxt, 0, 0);
+    wait_vm<ADMA>();                 // tile kt+NST's int4 chunk and scale arrived
+    qstore(cur, qv, sv);
+    __builtin_amdgcn_sched_barrier(0);
+    qload(kt + NST + 1, qv, sv);
+    dma(kt + NST, cur);
+    mm((KS - 1) & 1);
+#pragma unroll
+    for (int d = 0; d < PS; ++d) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int kt = 0; kt < nk; kt += NST) {
+    step(kt, std::integral_constant<int, 0>());
+    step(kt + 1, std::integral_constant<int, 1>());
+    if constexpr (NST > 2) step(kt + 2, std::integral_constant<int, 2>());
+    if constexpr (NST > 3) step(kt + 3, std::integral_constant<int, 3>());
+    if constexpr (NST > 4) step(kt + 4, std::integral_constant<int, 4>());
+    if constexpr (NST > 5) step(kt + 5, std::integral_constant<int, 5>());
+  }
+  wait_vm_lds0<0>();  // the trailing zero-fill loads land before the stages are reused
+  __syncthreads();
+
+  wave_epilogue<EPI, OT, TM, TN, WTN, SR>(acc, reinterpret_cast<float*>(st0) + wv * SR * (WTN + 4),
+                                          m0 + wm * TL::WTM, n0 + wn * TL::WTN, N, om, ep, pe_ld, lane);
+}
+
 // ============================================================================================
 // fp32 VALU kernel (tiny fp32 configuration; not a throughput path)
 // ============================================================================================
@@ -876,13 +1065,18 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
     constexpr int64_t kMaxBytes = 0x7fffffff;
     if (as.bytes() > kMaxBytes || (int64_t)N * K * 2 > kMaxBytes || ep.c_bytes > kMaxBytes)
       return hipErrorInvalidValue;
-    static_assert(!BQ || NST == 0, "int4 weights run in the one-stage kernel");
-    if (splits < 1 || (splits > 1 && (NST == 0 || k_span <= 0 || (int64_t)(splits - 1) * k_span >= K)))
+    static_assert(!BQ || NST > 0, "int4 weights run in the staged kernel");
+    if (splits < 1 || (splits > 1 && (NST == 0 || BQ || k_span <= 0 || (int64_t)(splits - 1) * k_span >= K)))
       return hipErrorInvalidValue;
-    if constexpr (NST == 0)
-      hipLaunchKernelGGL((gemm_dtl_kernel<TL, AS, OM, EPI, bf16_t, TAG, BQ>),
+    if constexpr (BQ && NST > 0) {
+      if (K % 128 != 0 || (int64_t)N * (K / 2) > kMaxBytes) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_ilvq_kernel<TL, NST, AS, OM, EPI, bf16_t, TAG>),
+                         dim3((unsigned)(m_tiles * n_tiles)), dim3(TL::NT), 0, s, as, N, K, om, ep, n_tiles,
+                         pe_ld, AE_GEMM_GROUP_M, bq);
+    } else if constexpr (NST == 0)
+      hipLaunchKernelGGL((gemm_dtl_kernel<TL, AS, OM, EPI, bf16_t, TAG>),
                          dim3((unsigned)(m_tiles * n_tiles)), dim3(TL::NT), 0, s, as, Bw, N, K, om, ep,
-                         n_tiles, pe_ld, AE_GEMM_GROUP_M, bq);
+                         n_tiles, pe_ld, AE_GEMM_GROUP_M);
     else
       hipLaunchKernelGGL((gemm_ilv_kernel<TL, NST, AS, OM, EPI, bf16_t, TAG>),
                          dim3((unsigned)(m_tiles * n_tiles), (unsigned)splits), dim3(TL::NT), 0, s, as, Bw, N,
@@ -1025,10 +1219,6 @@ inline LinKind lin_kind(int64_t M, int64_t N, bool gelu_epilogue, bool gate_epil
   return k;
 }
 
-// int4 weights run in the one-stage kernel, which dequantises B on its way into LDS
-inline bool int4_narrow(int64_t M, int64_t N) {
-  return (N == 1280 || N == 3840 || N < 2048) && tile_count(M, N, 128, 128) <= 2 * (int64_t)cu_count();
-}
 
 // conv2/conv3 (N = 480 output channels, K = 9 * 480): 256x256 tiles, BK 32, four stages (the
 // 480 channels fill two 256-wide column tiles at 94%).  Measured on MI355X against 256x256/BK 64
@@ -1047,13 +1237,28 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
   const int pe_ld = EPI == EPI_PE ? a.N : 0;
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (a.Wq) {
+      // int4 weights: the same tile choice as bf16, in the staged int4 kernel
       if (a.K % 128 != 0 || !a.Ws) return hipErrorInvalidValue;
       const BQuant bq{a.Wq, a.Ws};
-      if (int4_narrow(a.M, a.N))
-        return run<T, TileNarrow, ALinear<T>, OLinear, EPI, TAG, 0, true>(as, Bw, a.N, a.K, om, ep, a.M,
-                                                                         pe_ld, s, bq);
-      return run<T, TileWide, ALinear<T>, OLinear, EPI, TAG, 0, true>(as, Bw, a.N, a.K, om, ep, a.M,
-                                                                     pe_ld, s, bq);
+      switch (lin_kind(a.M, a.N, EPI == EPI_BIAS_GELU, EPI == EPI_SWIGLU)) {
+        case LinKind::Small:
+          if constexpr (EPI != EPI_SWIGLU)
+            return run<T, TileSmall, ALinear<T>, OLinear, EPI, TAG, kSmallStages, true>(as, Bw, a.N, a.K, om, ep,
+                                                                                        a.M, pe_ld, s, bq);
+          return hipErrorInvalidValue;
+        case LinKind::SmallW:
+          return run<T, TileSmallW, ALinear<T>, OLinear, EPI, TAG, kSmallWStages, true>(as, Bw, a.N, a.K, om, ep,
+                                                                                        a.M, pe_ld, s, bq);
+        case LinKind::Large:
+          return run<T, TileLarge, ALinear<T>, OLinear, EPI, TAG, kLargeStages, true>(as, Bw, a.N, a.K, om, ep,
+                                                                                      a.M, pe_ld, s, bq);
+        case LinKind::Tall:
+          return run<T, TileTall, ALinear<T>, OLinear, EPI, TAG, kTallStages, true>(as, Bw, a.N, a.K, om, ep,
+                                                                                    a.M, pe_ld, s, bq);
+        default:
+          return run<T, TileNarrow, ALinear<T>, OLinear, EPI, TAG, kNarrowStages, true>(as, Bw, a.N, a.K, om, ep,
+                                                                                        a.M, pe_ld, s, bq);
+      }
     }
     // Split K when even the 128x128 tiles (two per CU) would leave more than half the CUs idle
     // (a single clip: M = 375) and K is long (FFN2, conv_out, the adapter's down projection;
