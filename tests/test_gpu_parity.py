@@ -525,6 +525,19 @@ def test_full_c2_batch_sampled_windows(full):
         assert torch.equal(y[b], enc.forward(to_dev(xs[b:b + 1]))[0])
 
 
+def test_full_batch_above_one_pass(full):
+    """24 clips of 30 s = 9000 tokens: more than one pass of max_tokens_per_pass (8192), so the
+    call runs as several passes on the encoder's lanes; every clip's rows equal its own
+    single-clip encoding bit for bit."""
+    enc, Wt = full
+    xs = S.mixed_batch(range(101, 125))
+    y = enc.forward(to_dev(xs))
+    torch.cuda.synchronize()
+    assert y.shape == (24, 375, 2048)
+    for b in (0, 20, 21, 23):
+        assert torch.equal(y[b], enc.forward(to_dev(xs[b:b + 1]))[0])
+
+
 def test_full_c3_pieces_equal_whole(full):
     enc, Wt = full
     x = S.long_stream_512s()
