@@ -585,7 +585,13 @@ def test_full_int4_window_matches_oracle(full):
     log(f"int4 weights: {wbytes / 1e9:.3f} GB")
     assert wbytes < 0.45e9
     x = S.pink_plus_bursts(seed=1)
-    got = enc.forward(to_dev(x[None])).float().cpu().numpy()[0]
+    y1 = enc.forward(to_dev(x[None]))
+    got = y1.float().cpu().numpy()[0]
+    # a single clip runs the small deep-stage int4 tiles, a 16-clip batch the large ones; both
+    # accumulate K in the same order, so the clip's rows are bit-identical inside the batch
+    xs = S.mixed_batch(range(101, 116))
+    yb = enc.forward(to_dev(np.concatenate([x[None], xs])))
+    assert torch.equal(yb[0], y1[0])
     enc.close()
     log("int4: quantising the oracle's weights")
     Wt4 = O.int4_weights(Wt, O.FULL)
