@@ -14,7 +14,8 @@
 //      X[k] = sum_{n=0}^{200} u[n] cos(2 pi k n / 400) - i sum_{n=1}^{199} v[n] sin(2 pi k n / 400)
 //      where u[n] = a[n] + a[400-n], v[n] = a[n] - a[400-n] (u[0] = a[0], u[200] = a[200]);
 //      this halves the DFT work of a direct 400-point transform of real input;
-//   3. one thread per bin accumulates all FB frames against an LDS twiddle table, in fp32;
+//   3. the two real DFTs (cosine of u, sine of v) run as fp32 matrix products on MFMA, with the
+//      twiddles from an LDS table;
 //   4. the 128 sparse filters (<= 16 taps each) reduce the power spectrum, log10 is taken and
 //      the block maximum joins the clip maximum through an ordered-integer atomicMax.
 #include <algorithm>
@@ -31,6 +32,8 @@ constexpr int NM = 128;  // mel bins
 constexpr int FB = 16;   // frames per workgroup
 constexpr int NSMP = (FB - 1) * HOP + NFFT;  // samples spanned by FB frames
 constexpr int MAXTAP = 16;
+constexpr int NKB = (NB + 15) / 16;    // 16-bin blocks of the DFT
+constexpr int NSTEP = (NB + 3) / 4;    // 4-tap steps (the folded rows are zero-padded to 4*NSTEP)
 
 __device__ inline uint32_t float_to_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -48,8 +51,8 @@ __global__ __launch_bounds__(256) void log_mel_kernel(const float* __restrict__ 
                                                       uint32_t* __restrict__ max_key) {
   __shared__ float xs[NSMP];
   __shared__ float2 tw[NFFT];
-  __shared__ __attribute__((aligned(16))) float us[NB][FB];
-  __shared__ __attribute__((aligned(16))) float vs[NB][FB];
+  __shared__ __attribute__((aligned(16))) float us[4 * NSTEP][FB];
+  __shared__ __attribute__((aligned(16))) float vs[4 * NSTEP][FB];
   __shared__ float red[4];
 
   const int tid = threadIdx.x;
@@ -89,44 +92,50 @@ __global__ __launch_bounds__(256) void log_mel_kernel(const float* __restrict__ 
     us[n][f] = u;
     vs[n][f] = v;
   }
+  for (int idx = tid; idx < (4 * NSTEP - NB) * FB; idx += 256) {
+    us[NB + idx / FB][idx % FB] = 0.0f;
+    vs[NB + idx / FB][idx % FB] = 0.0f;
+  }
   __syncthreads();
 
-  // 3. DFT: thread k owns bin k for all FB frames
-  float pw[FB];
-  const int k = tid;
-  if (k < NB) {
-    float re[FB], im[FB];
+  // 3. DFT on fp32 MFMA.  As matrices, RE[f][k] = sum_n U[n][f] cos(2 pi k n / 400) and
+  // IM[f][k] = sum_n V[n][f] sin(...).  v_mfma_f32_16x16x4_f32 takes A = 16 frames x 4 taps (lane
+  // l: frame l%16, tap n0 + l/16), B = 4 taps x 16 bins (lane l: bin k0 + l%16, tap n0 + l/16)
+  // and accumulates D = 16 frames x 16 bins (lane l: bin k0 + l%16, frames 4(l/16) + v).  Each
+  // wave takes whole 16-bin blocks; a lane's twiddle index (k n) mod 400 advances by 4k per step.
+  // Products and sums are fp32, as in a direct fp32 DFT (only the summation order differs).
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lf = lane & 15, lq = lane >> 4;
+  f32x4_t pwr[(NKB + 3) / 4];
 #pragma unroll
-    for (int f = 0; f < FB; ++f) { re[f] = 0.0f; im[f] = 0.0f; }
-    int ang = 0;  // (k * n) mod 400
-    for (int n = 0; n < NB; ++n) {
-      const float2 cs = tw[ang];
-      const float4* u4 = reinterpret_cast<const float4*>(us[n]);
-      const float4* v4 = reinterpret_cast<const float4*>(vs[n]);
-#pragma unroll
-      for (int q = 0; q < FB / 4; ++q) {
-        const float4 uu = u4[q];
-        const float4 vv = v4[q];
-        re[4 * q + 0] = fmaf(uu.x, cs.x, re[4 * q + 0]);
-        re[4 * q + 1] = fmaf(uu.y, cs.x, re[4 * q + 1]);
-        re[4 * q + 2] = fmaf(uu.z, cs.x, re[4 * q + 2]);
-        re[4 * q + 3] = fmaf(uu.w, cs.x, re[4 * q + 3]);
-        im[4 * q + 0] = fmaf(vv.x, cs.y, im[4 * q + 0]);
-        im[4 * q + 1] = fmaf(vv.y, cs.y, im[4 * q + 1]);
-        im[4 * q + 2] = fmaf(vv.z, cs.y, im[4 * q + 2]);
-        im[4 * q + 3] = fmaf(vv.w, cs.y, im[4 * q + 3]);
+  for (int b = 0; b < (NKB + 3) / 4; ++b) {
+    const int kb = wave + 4 * b;
+    if (kb < NKB) {  // uniform per wave
+      const int k = kb * 16 + lf;  // bins past NB are computed and dropped
+      const int dang = (4 * k) % NFFT;
+      int ang = (k * lq) % NFFT;
+      f32x4_t re = {0.0f, 0.0f, 0.0f, 0.0f}, im = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int st = 0; st < NSTEP; ++st) {
+        const float2 c = tw[ang];
+        re = __builtin_amdgcn_mfma_f32_16x16x4f32(us[4 * st + lq][lf], c.x, re, 0, 0, 0);
+        im = __builtin_amdgcn_mfma_f32_16x16x4f32(vs[4 * st + lq][lf], c.y, im, 0, 0, 0);
+        ang += dang;
+        if (ang >= NFFT) ang -= NFFT;
       }
-      ang += k;
-      if (ang >= NFFT) ang -= NFFT;
-    }
 #pragma unroll
-    for (int f = 0; f < FB; ++f) pw[f] = re[f] * re[f] + im[f] * im[f];
+      for (int v = 0; v < 4; ++v) pwr[b][v] = re[v] * re[v] + im[v] * im[v];
+    }
   }
   __syncthreads();  // us/vs are reused as the power table below
   float* P = &us[0][0];  // [FB][NB]
-  if (k < NB) {
 #pragma unroll
-    for (int f = 0; f < FB; ++f) P[f * NB + k] = pw[f];
+  for (int b = 0; b < (NKB + 3) / 4; ++b) {
+    const int kb = wave + 4 * b;
+    const int k = kb * 16 + lf;
+    if (kb < NKB && k < NB) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) P[(4 * lq + v) * NB + k] = pwr[b][v];
+    }
   }
   __syncthreads();
 
