@@ -81,7 +81,15 @@ LINEAR_SHAPES = [(1, 64, 64), (130, 200, 72), (300, 3840, 1280), (257, 1280, 512
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_op_linear(M, N, K, epi, dtype):
     if epi == 3 and N % 64:
-        pytest.skip("SwiGLU needs N % 64 == 0")
+        # the SwiGLU epilogue pairs 32-column gate/up groups, so the call rejects such N on the
+        # host, before any launch, and leaves C untouched
+        A0 = torch.zeros((M, K), dtype=dtype, device=DEV)
+        W0 = torch.zeros((N, K), dtype=dtype, device=DEV)
+        C0 = torch.full((M, N // 2), 3.0, dtype=dtype, device=DEV)
+        with pytest.raises(B.EncoderError, match="N % 64"):
+            B.op_linear(A0, W0, None, C0, 3)
+        assert bool((C0 == 3.0).all())
+        return
     rng = np.random.default_rng(M * 7 + N + K + epi)
     A = rng.standard_normal((M, K)).astype(np.float32)
     W = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
