@@ -1359,7 +1359,9 @@ encoder_status encoder_op_linear(const void* A, const void* W, const float* bias
                                  int64_t M, int32_t N, int32_t K, int32_t epi, int32_t dtype,
                                  void* stream) {
   if (!A || !W || !C) return invalid("A, W and C must be non-NULL");
-  if (M < 0 || N <= 0 || K <= 0 || K % 8) return invalid("need M >= 0, N > 0, K > 0, K % 8 == 0");
+  // the epilogue writes four consecutive columns per lane
+  if (M < 0 || N <= 0 || N % 4 || K <= 0 || K % 8)
+    return invalid("need M >= 0, N > 0, N % 4 == 0, K > 0, K % 8 == 0");
   if (epi < 0 || epi > 3) return invalid("epi must be 0..3");
   if (epi == 3 && N % 64) return invalid("SwiGLU needs N % 64 == 0");
   if (dtype != ENC_BF16 && dtype != ENC_F32) return invalid("bad dtype");
@@ -1398,7 +1400,8 @@ encoder_status encoder_op_linear_int4(const void* A, const uint8_t* q, const uin
                                       const float* bias, void* C, int64_t M, int32_t N, int32_t K,
                                       int32_t epi, void* stream) {
   if (!A || !q || !scales || !C) return invalid("A, q, scales and C must be non-NULL");
-  if (M < 0 || N <= 0 || K < 128 || K % 128) return invalid("need M >= 0, N > 0, K % 128 == 0");
+  if (M < 0 || N <= 0 || N % 4 || K < 128 || K % 128)
+    return invalid("need M >= 0, N > 0, N % 4 == 0, K % 128 == 0");
   if (epi < 0 || epi > 3) return invalid("epi must be 0..3");
   if (epi == 3 && N % 64) return invalid("SwiGLU needs N % 64 == 0");
   static const int map[4] = {EPI_BIAS, EPI_BIAS_GELU, EPI_RESADD, EPI_SWIGLU};

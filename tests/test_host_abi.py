@@ -165,9 +165,18 @@ def test_create_rejects_bad_blob_without_touching_the_gpu():
 
 
 def test_forward_argument_checks():
+    import ctypes
     L = B.lib()
     assert L.encoder_forward(None, None, 1000, 1, None, None) == B.ENC_E_INVALID_ARG
     assert L.encoder_op_linear(None, None, None, None, 1, 1, 1, 0, 0, None) == B.ENC_E_INVALID_ARG
+    # shape checks come before any device access: the pointers below are never dereferenced
+    p = ctypes.c_void_p(256)
+    for N, K in ((6, 64), (2, 64), (64, 12), (64, 0), (0, 64)):
+        assert L.encoder_op_linear(p, p, None, p, 8, N, K, 0, 0, None) == B.ENC_E_INVALID_ARG, (N, K)
+        if N == 6:
+            assert b"N % 4" in L.encoder_last_error()
+    for N, K in ((6, 128), (64, 64)):
+        assert L.encoder_op_linear_int4(p, p, p, None, p, 8, N, K, 0, None) == B.ENC_E_INVALID_ARG, (N, K)
 
 
 def test_kernel_gelu_constants_follow_abramowitz_stegun_7_1_28():
