@@ -1365,6 +1365,8 @@ encoder_status encoder_op_linear(const void* A, const void* W, const float* bias
   if (epi < 0 || epi > 3) return invalid("epi must be 0..3");
   if (epi == 3 && N % 64) return invalid("SwiGLU needs N % 64 == 0");
   if (dtype != ENC_BF16 && dtype != ENC_F32) return invalid("bad dtype");
+  // bf16 outputs leave as eight columns per lane
+  if (dtype == ENC_BF16 && (epi == 0 || epi == 1) && N % 8) return invalid("bf16 output needs N % 8 == 0");
   hipStream_t s = (hipStream_t)stream;
   static const int map[4] = {EPI_BIAS, EPI_BIAS_GELU, EPI_RESADD, EPI_SWIGLU};
   const int64_t ldc = epi == 3 ? N / 2 : N;
@@ -1404,6 +1406,7 @@ encoder_status encoder_op_linear_int4(const void* A, const uint8_t* q, const uin
     return invalid("need M >= 0, N > 0, N % 4 == 0, K % 128 == 0");
   if (epi < 0 || epi > 3) return invalid("epi must be 0..3");
   if (epi == 3 && N % 64) return invalid("SwiGLU needs N % 64 == 0");
+  if ((epi == 0 || epi == 1) && N % 8) return invalid("bf16 output needs N % 8 == 0");
   static const int map[4] = {EPI_BIAS, EPI_BIAS_GELU, EPI_RESADD, EPI_SWIGLU};
   const int64_t ldc = epi == 3 ? N / 2 : N;
   LinearArgs a{A, K, nullptr, bias, C, ldc, M, N, K, nullptr, nullptr, q, (const bf16_t*)scales};

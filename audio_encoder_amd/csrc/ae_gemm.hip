@@ -270,8 +270,9 @@ __device__ inline void cbar() { asm volatile("" ::: "memory"); }
 
 // Epilogue of one wave.  Its TM x TN accumulator blocks (32x32 each; tile rows rbase0..,
 // columns wcol..wcol+WTN-1) pass through the wave's own SR staging rows in LDS (stride WTN + 4
-// floats), SR rows per round, and leave as 16-byte (fp32) or 8-byte (bf16) row pieces: each lane
-// owns 4 consecutive columns of every (64 / (WTN / 4))-th staged row.
+// floats), SR rows per round, and leave as 16-byte row pieces: each lane owns CPL consecutive
+// columns (4 fp32 or 8 bf16) of every (64 / (WTN / CPL))-th staged row.  The SwiGLU gate writes
+// 8-byte pieces of four outputs.
 //
 // Ordering.  The staging rows belong to this wave alone and a wave's LDS accesses execute in
 // order, so compiler fences are all the ordering the staging needs (a workgroup barrier would
@@ -292,7 +293,10 @@ __device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16
   constexpr bool GATE = EPI == EPI_SWIGLU;
   constexpr bool F32OUT = EPI == EPI_RESADD || EPI == EPI_PE || EPI == EPI_STORE_F32;
   constexpr int ES = F32OUT ? 4 : (int)sizeof(OT);
-  constexpr int Q = GATE ? WTN / 8 : WTN / 4;  // lanes per staged row
+  // output columns per lane: eight for 2-byte outputs (one 16-byte store; N % 8 == 0 there),
+  // else four; the gate reads four gate and four up columns for four outputs
+  constexpr int CPL = (ES == 2 && !GATE) ? 8 : 4;
+  constexpr int Q = GATE ? WTN / 8 : WTN / CPL;  // lanes per staged row
   constexpr int RPI = 64 / Q;                   // staged rows per 64 lanes
   constexpr int T = SR / RPI;                   // rows per lane per round
   static_assert(RPI * Q == 64 && T * RPI == SR, "epilogue lane map");
@@ -302,14 +306,17 @@ __device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16
   // gate: (gate, up) pairs of 32 columns interleaved in 64-column groups; the output column is
   // half the group's start plus the position within the pair
   const int gp = GATE ? (4 * q4) / 32 : 0, gj = GATE ? (4 * q4) % 32 : 0;
-  const int scol = GATE ? 64 * gp + gj : 4 * q4;          // staged column
-  const int col = GATE ? (wcol + 64 * gp) / 2 + gj : wcol + 4 * q4;  // output column
+  const int scol = GATE ? 64 * gp + gj : CPL * q4;          // staged column
+  const int col = GATE ? (wcol + 64 * gp) / 2 + gj : wcol + CPL * q4;  // output column
   const bool colok = GATE ? wcol + 64 * gp < N : col < N;
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(ep.C, ep.c_bytes);
   const int64_t slice = (int64_t)blockIdx.y * ep.c_slice;  // split-K partial of this K range
-  float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 bv = make_float4(0.f, 0.f, 0.f, 0.f), bv2 = bv;
   if constexpr (EPI != EPI_PE && !GATE)
-    if (ep.bias && colok) bv = *reinterpret_cast<const float4*>(ep.bias + col);
+    if (ep.bias && colok) {
+      bv = *reinterpret_cast<const float4*>(ep.bias + col);
+      if constexpr (CPL == 8) bv2 = *reinterpret_cast<const float4*>(ep.bias + col + 4);
+    }
 
   const typename OM::Ctx octx = om.ctx(rbase0);
   auto row_of = [&](int rd, int t) -> int64_t { return rbase0 + (rd / HS) * 32 + (rd % HS) * SR + rs + RPI * t; };
@@ -346,6 +353,7 @@ __device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16
     for (int t = 0; t < T; ++t) {
       a[t] = *reinterpret_cast<const float4*>(stg + (rs + RPI * t) * LDW + scol);
       if constexpr (GATE) g2[t] = *reinterpret_cast<const float4*>(stg + (rs + RPI * t) * LDW + scol + 32);
+      if constexpr (CPL == 8) g2[t] = *reinterpret_cast<const float4*>(stg + (rs + RPI * t) * LDW + scol + 4);
     }
     uint32_t off[T];
     float4 res[T];
@@ -374,7 +382,17 @@ __device__ __attribute__((always_inline)) inline void wave_epilogue(const f32x16
           x.x = gelu_erf(x.x); x.y = gelu_erf(x.y); x.z = gelu_erf(x.z); x.w = gelu_erf(x.w);
         }
       }
-      if constexpr (ES == 4) {
+      if constexpr (CPL == 8) {
+        // columns 4..7 of the lane: bias (and GELU), then one 16-byte store of all eight
+        float4 y = g2[t];
+        y.x += bv2.x; y.y += bv2.y; y.z += bv2.z; y.w += bv2.w;
+        if constexpr (EPI == EPI_BIAS_GELU) {
+          y.x = gelu_erf(y.x); y.y = gelu_erf(y.y); y.z = gelu_erf(y.z); y.w = gelu_erf(y.w);
+        }
+        const u32x4 o = {pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w), pack_bf16x2(y.x, y.y),
+                         pack_bf16x2(y.z, y.w)};
+        __builtin_amdgcn_raw_buffer_store_b128(o, crs, (int)off[t], 0, 0);
+      } else if constexpr (ES == 4) {
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), crs, (int)off[t], 0, 0);
       } else {
         const u32x2 o = {pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w)};

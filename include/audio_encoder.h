@@ -248,8 +248,9 @@ ENC_API encoder_status encoder_timing_read(encoder* e, double* ms, int64_t* laun
 /* ---- single-kernel entry points (kernel-level tests) --------------------------------------- */
 
 /* C = epi(A . W^T).  A device [M, K] row-major, W device [N, K] row-major, both bf16 (dtype
- * ENC_BF16) or float32 (ENC_F32).  bias: device float32 [N] or NULL.  N % 4 == 0, K % 8 == 0;
- * other shapes return ENC_E_INVALID_ARG before any launch.
+ * ENC_BF16) or float32 (ENC_F32).  bias: device float32 [N] or NULL.  N % 4 == 0 (N % 8 == 0
+ * for bf16 output, epi 0 and 1), K % 8 == 0; other shapes return ENC_E_INVALID_ARG before any
+ * launch.
  * epi 0: C[M,N] = acc + bias, stored in dtype.   epi 1: C = GELU(acc + bias), stored in dtype.
  * epi 2: C[M,N] float32 += acc + bias (residual update).
  * epi 3: SwiGLU over 32-column interleaved gate/up rows of W (rows 64j..64j+31 gate, 64j+32..64j+63
@@ -271,7 +272,7 @@ ENC_API encoder_status encoder_quantize_int4(const float* w, int64_t N, int64_t 
                                      uint16_t* scales);
 
 /* encoder_op_linear with int4 weights (q, scales from encoder_quantize_int4, on the device) and
- * bf16 A / C; N % 4 == 0, K % 128 == 0. */
+ * bf16 A / C; N % 4 == 0 (N % 8 == 0 for epi 0 and 1), K % 128 == 0. */
 ENC_API encoder_status encoder_op_linear_int4(const void* A, const uint8_t* q, const uint16_t* scales,
                                       const float* bias, void* C, int64_t M, int32_t N, int32_t K,
                                       int32_t epi, void* stream);

@@ -175,8 +175,11 @@ def test_forward_argument_checks():
         assert L.encoder_op_linear(p, p, None, p, 8, N, K, 0, 0, None) == B.ENC_E_INVALID_ARG, (N, K)
         if N == 6:
             assert b"N % 4" in L.encoder_last_error()
-    for N, K in ((6, 128), (64, 64)):
+    for N, K in ((6, 128), (64, 64), (12, 128)):
         assert L.encoder_op_linear_int4(p, p, p, None, p, 8, N, K, 0, None) == B.ENC_E_INVALID_ARG, (N, K)
+    # bf16 outputs (epi 0 and 1) leave eight columns per lane: N % 8 == 0
+    assert L.encoder_op_linear(p, p, None, p, 8, 12, 64, 1, B.ENC_BF16, None) == B.ENC_E_INVALID_ARG
+    assert b"N % 8" in L.encoder_last_error()
 
 
 def test_kernel_gelu_constants_follow_abramowitz_stegun_7_1_28():
