@@ -106,7 +106,9 @@ struct AConv {
   __device__ KC kc(int k) const {
     KC c;
     c.ok = k < K;
-    const int tap = k / C;
+    // k / C without an integer division: (k + 1/2) / C lies at least 1/(2C) inside its unit
+    // interval, far more than the float error for k < 2^24 and C <= 65536
+    const int tap = (int)(((float)k + 0.5f) * inv_c);
     const int ci = k - tap * C;
     const int da = tap / 3, db = tap - 3 * (tap / 3);  // frequency tap, time tap
     c.bit = 1 << tap;
@@ -124,6 +126,7 @@ struct AConv {
   __host__ __device__ int64_t bytes() const { return (int64_t)wins_bytes; }
   __device__ const void* base() const { return in; }
   int64_t wins_bytes;  // bytes of the input activation
+  float inv_c;         // 1 / C
 };
 
 // ============================================================================================
@@ -1404,8 +1407,8 @@ hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T*
   const int rows_per_win = Lout_max * Fout;
   const int64_t m_rows = (int64_t)g.n_win * rows_per_win;
   AConv<T> as{in, g.wins, C, Fin, Fout, Lin_max, level, rows_per_win, 9 * C, m_rows,
-              (int64_t)g.n_win * Lin_max * Fin * C * (int64_t)sizeof(T)};
-  if (m_rows >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+              (int64_t)g.n_win * Lin_max * Fin * C * (int64_t)sizeof(T), 1.0f / (float)C};
+  if (m_rows >= (int64_t(1) << 31) || C > 65536) return hipErrorInvalidValue;
   const int64_t out_rows = level == 2 ? (int64_t)g.n_win * Lout_max * Fout : g.n_tok * Fout;
   EpiP ep{bias, out, nullptr, nullptr, out_rows * C * (int64_t)sizeof(T)};
   if (level == 2)

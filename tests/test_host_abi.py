@@ -212,3 +212,16 @@ def test_kernel_gelu_constants_follow_abramowitz_stegun_7_1_28():
     g = (np.maximum(x, 0).astype(np.float64) - np.float64(t) * r).astype(f32)
     exact = np.array([v * 0.5 * (1 + math.erf(v / math.sqrt(2))) for v in x.astype(np.float64)])
     assert np.max(np.abs(g - exact)) < 1e-6
+
+
+def test_conv_tap_from_float_reciprocal_is_exact():
+    """The implicit-GEMM conv gather (csrc/ae_gemm.hip, AConv::kc) takes the tap of a K index k
+    as trunc((float(k) + 0.5) * float(1 / C)) instead of an integer division; the launcher allows
+    C <= 65536 (C % 32 == 0 from the config).  Exhaustive over k < 9C for every such C up to 8192
+    and for the largest ones."""
+    Cs = list(range(32, 8193, 32)) + list(range(65536 - 32 * 64, 65537, 32))
+    for C in Cs:
+        k = np.arange(9 * C, dtype=np.int64)
+        inv = np.float32(1.0) / np.float32(C)
+        tap = ((k.astype(np.float32) + np.float32(0.5)) * inv).astype(np.int64)
+        assert np.array_equal(tap, k // C), C
