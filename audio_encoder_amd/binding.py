@@ -79,6 +79,8 @@ _SIGS = {
                              POINTER(c_int32)],
     "encoder_plan_windows_ragged": [POINTER(EncoderCfg), POINTER(c_int64), c_int32, POINTER(c_int32),
                                     c_int32, POINTER(c_int32)],
+    "encoder_plan_passes": [POINTER(EncoderCfg), POINTER(c_int64), c_int32, c_int32, POINTER(c_int64),
+                            c_int32, POINTER(c_int32)],
     "encoder_create": [POINTER(c_float), c_int64, POINTER(EncoderCfg), POINTER(c_void_p)],
     "encoder_destroy": [c_void_p],
     "encoder_memory_stats": [c_void_p, POINTER(c_int64), POINTER(c_int64)],
@@ -103,6 +105,10 @@ _SIGS = {
                                c_int32, c_int32, c_void_p],
     "encoder_op_attention": [c_void_p, c_void_p, c_int32, c_int32, c_int64, c_void_p, c_int32,
                              c_void_p],
+    "encoder_op_conv1": [c_void_p, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32,
+                         c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p],
+    "encoder_op_conv": [c_int32, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int64, c_void_p,
+                        c_void_p, c_int32, c_void_p, c_int32, c_void_p],
     "encoder_op_layernorm": [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_float,
                              c_int32, c_void_p],
     "encoder_last_error": [],
@@ -178,6 +184,20 @@ def encoder_plan_windows_ragged(cfg: dict, lengths) -> np.ndarray:
     _check(lib().encoder_plan_windows_ragged(ctypes.byref(c), lp, L.size,
                                              tab.ctypes.data_as(POINTER(c_int32)), nw.value,
                                              ctypes.byref(nw)))
+    return tab
+
+
+def encoder_plan_passes(cfg: dict, lengths, pieces_per_pass: int = 0) -> np.ndarray:
+    """Passes of a forward call over clips of the given sample lengths: int64 [n_passes, 6] =
+    {first window, windows, first token, tokens, act1 rows per window, act2 rows per window}."""
+    c, n, L = make_cfg(cfg), c_int32(), _lengths(lengths)
+    lp = L.ctypes.data_as(POINTER(c_int64))
+    _check(lib().encoder_plan_passes(ctypes.byref(c), lp, L.size, pieces_per_pass, None, 0,
+                                     ctypes.byref(n)))
+    tab = np.zeros((n.value, 6), dtype=np.int64)
+    _check(lib().encoder_plan_passes(ctypes.byref(c), lp, L.size, pieces_per_pass,
+                                     tab.ctypes.data_as(POINTER(c_int64)), n.value,
+                                     ctypes.byref(n)))
     return tab
 
 
@@ -380,6 +400,27 @@ def op_linear(A, W, bias, C, epi: int):
 def op_attention(qkv, windows, n_heads: int, out):
     _check(lib().encoder_op_attention(_ptr(qkv), _ptr(windows), windows.shape[0], n_heads,
                                       qkv.shape[0], _ptr(out), _dtype_code(qkv.dtype), _stream()))
+    return out
+
+
+def op_conv1(mel, clip_max, windows, window_tokens: int, L1s: int, w, b, act1):
+    """conv1 on the windows of one pass (see encoder_op_conv1): mel float32 [rows, 128], clip_max
+    float32 [n_clips], windows int32 [n_windows, 8], w float32 [C, 3, 3], b float32 [C] and
+    act1 [n_windows, L1s, 64, C] (bf16 or float32), all CUDA tensors."""
+    C = b.shape[0]
+    _check(lib().encoder_op_conv1(_ptr(mel), mel.shape[0], _ptr(clip_max), clip_max.shape[0],
+                                  _ptr(windows), windows.shape[0], window_tokens, L1s, _ptr(w),
+                                  _ptr(b), C, _ptr(act1), _dtype_code(act1.dtype), _stream()))
+    return act1
+
+
+def op_conv(level: int, inp, windows, window_tokens: int, L1s: int, n_tok: int, w_packed, bias, out):
+    """conv2 (level 2) or conv3 (level 3) implicit GEMM (see encoder_op_conv); w_packed
+    [C_out, 9, C_in] in the dtype of inp and out."""
+    C = bias.shape[0]
+    _check(lib().encoder_op_conv(level, _ptr(inp), _ptr(windows), windows.shape[0], window_tokens,
+                                 L1s, n_tok, _ptr(w_packed), _ptr(bias), C, _ptr(out),
+                                 _dtype_code(out.dtype), _stream()))
     return out
 
 

@@ -38,6 +38,10 @@ static encoder_status invalid(const std::string& msg) {
 // ------------------------------------------------------------------------------------------
 // configuration
 // ------------------------------------------------------------------------------------------
+// The GEMM and conv kernels address their operands through buffer descriptors with 32-bit
+// byte offsets, so no operand of a pass may exceed this many bytes.
+constexpr int64_t kMaxOperandBytes = 0x7fffffff;
+
 static encoder_status check_cfg(const encoder_cfg* c) {
   if (!c) return invalid("cfg is NULL");
   if (c->n_fft != 400 || c->hop != 160 || c->n_mels != 128)
@@ -69,6 +73,19 @@ static encoder_status check_cfg(const encoder_cfg* c) {
     if (c->d_model % 128 || c->d_ffn % 128 || c->d_out % 128 || c->d_adapter % 128)
       return invalid("int4 weights need d_model, d_ffn, d_out and d_adapter multiples of 128");
   }
+  {
+    // one full window must fit one pass, and every weight matrix one buffer descriptor
+    const int64_t es = c->dtype == ENC_BF16 ? 2 : 4;
+    const int64_t C = c->conv_channels, d = c->d_model;
+    const int64_t tb = std::max<int64_t>({16 * C * es, 3 * d * es, 4 * d, (int64_t)c->d_ffn * es,
+                                          2 * (int64_t)c->d_adapter * es, (int64_t)c->d_out * es});
+    if (4 * (int64_t)c->window_tokens * 64 * C * es > kMaxOperandBytes ||
+        (int64_t)c->window_tokens * tb > kMaxOperandBytes)
+      return invalid("one window's activations exceed 2^31 - 1 bytes");
+    const int64_t wmax = std::max<int64_t>({9 * C * C, 16 * C * d, 3 * d * d, (int64_t)c->d_ffn * d,
+                                            (int64_t)c->d_out * d, 2 * (int64_t)c->d_adapter * c->d_out});
+    if (wmax * es > kMaxOperandBytes) return invalid("a weight matrix exceeds 2^31 - 1 bytes");
+  }
   if (c->sample_rate != 16000) {
     set_error("only 16 kHz input is supported (no resampling)");
     return ENC_E_UNSUPPORTED;
@@ -79,7 +96,23 @@ static encoder_status check_cfg(const encoder_cfg* c) {
 static int64_t max_tokens(const encoder_cfg& c) {
   return c.max_tokens_per_pass > 0 ? c.max_tokens_per_pass : 8192;
 }
-static int64_t max_windows(const encoder_cfg& c) { return max_tokens(c) / c.window_tokens + 32; }
+static int64_t elem_bytes(const encoder_cfg& c) { return c.dtype == ENC_BF16 ? 2 : 4; }
+
+// Bytes per token of the largest per-token operand of a pass: conv3's output (16C), the qkv
+// (3d), the fp32 residual, the FFN / head / adapter hidden rows and the output rows.
+static int64_t token_bytes(const encoder_cfg& c) {
+  const int64_t es = elem_bytes(c);
+  return std::max<int64_t>({16 * (int64_t)c.conv_channels * es, 3 * (int64_t)c.d_model * es,
+                            4 * (int64_t)c.d_model, (int64_t)c.d_ffn * es, 2 * (int64_t)c.d_adapter * es,
+                            (int64_t)c.d_out * es});
+}
+// Bytes of one time row of conv1's output (64 frequencies x C channels); act1 of a pass is
+// windows x L1s of them, the largest conv operand (conv2's A).
+static int64_t act1_row_bytes(const encoder_cfg& c) { return 64 * (int64_t)c.conv_channels * elem_bytes(c); }
+// tokens one pass may hold: the configured bound, capped by the per-token operands
+static int64_t pass_token_cap(const encoder_cfg& c) {
+  return std::min<int64_t>(max_tokens(c), kMaxOperandBytes / token_bytes(c));
+}
 // Passes of one call that run at once (each lane holds one pass's activations).  HIP maps
 // streams onto four hardware queues by default; three lanes plus the caller's stream keep one
 // queue each.  An hour at one 64 s piece per pass (57 passes) measured 160 ms with four lanes,
@@ -209,26 +242,66 @@ static int64_t conditioned_length(int64_t n_in, const ResamplePlan& r) {
   return (n_in * r.L + r.M - 1) / r.M;
 }
 
-struct Pass { int64_t win0, nwin, tok0, ntok; };
+// One pass: windows [win0, win0 + nwin) = tokens [tok0, tok0 + ntok) of the call, with the
+// conv activations at time strides L1s / L2s (PassGeom).
+struct Pass { int64_t win0, nwin, tok0, ntok; int32_t L1s, L2s; };
 
-// consecutive windows grouped into passes; a pass ends where `boundary(window)` says so or
-// where the next window would overflow the workspace
+// Consecutive windows grouped into passes.  A pass ends where `boundary(window)` says so, where
+// the next window would take it past `mt` tokens, or where its act1 (windows x L1s rows, L1s
+// the longest conv1 output of the pass, or 4W for `full` strides) would exceed the bytes a
+// buffer descriptor addresses; act2 and every per-token operand are then addressable too.
 template <class F>
-static std::vector<Pass> split_passes(const std::vector<Win>& w, int64_t mt, int64_t mw, F boundary) {
+static std::vector<Pass> split_passes(const encoder_cfg& c, const std::vector<Win>& w, int64_t mt,
+                                      bool full, F boundary) {
+  const int32_t L1full = 4 * c.window_tokens;
+  const int64_t rowb = act1_row_bytes(c);
   std::vector<Pass> ps;
-  Pass cur{0, 0, 0, 0};
+  Pass cur{0, 0, 0, 0, 0, 0};
   for (size_t i = 0; i < w.size(); ++i) {
-    const bool brk = cur.nwin > 0 &&
-                     (cur.ntok + w[i].L3 > mt || cur.nwin + 1 > mw || boundary((int64_t)i));
-    if (brk) {
+    const int32_t l1 = full ? L1full : std::max(cur.L1s, w[i].L1);
+    const bool fits = cur.ntok + w[i].L3 <= mt && (cur.nwin + 1) * (int64_t)l1 * rowb <= kMaxOperandBytes;
+    if (cur.nwin > 0 && (!fits || boundary((int64_t)i))) {
       ps.push_back(cur);
-      cur = Pass{(int64_t)i, 0, w[i].tok, 0};
+      cur = Pass{(int64_t)i, 0, w[i].tok, 0, 0, 0};
     }
     if (cur.nwin == 0) cur.tok0 = w[i].tok, cur.win0 = (int64_t)i;
     cur.nwin += 1;
     cur.ntok += w[i].L3;
+    cur.L1s = full ? L1full : std::max(cur.L1s, w[i].L1);
+    cur.L2s = (cur.L1s + 1) / 2;
   }
   if (cur.nwin) ps.push_back(cur);
+  return ps;
+}
+
+// Passes a call runs in.  piece_windows > 0: long mode, passes start only at multiples of it.
+// A call that fits one pass but holds at least kSplitTokens tokens runs as two halves of whole
+// windows (whole pieces in long mode), unless `halves` is false.  `full`: act1/act2 keep the
+// documented padded layout of 4W / 2W rows per window (the stage-wise debug exports).
+static std::vector<Pass> plan_passes(const encoder_cfg& c, const std::vector<Win>& wins,
+                                     int64_t piece_windows, bool halves, bool full) {
+  const int64_t mt = pass_token_cap(c);
+  std::vector<Pass> ps = split_passes(c, wins, mt, full, [&](int64_t i) {
+    return piece_windows > 0 && i % piece_windows == 0;
+  });
+  // The passes of a call run concurrently on lanes, and two passes' kernels overlap where one
+  // pass alone leaves the GPU partly idle (attention, LayerNorm, a GEMM's last round of tiles).
+  // A window's rows are the same in any pass.
+  if (halves && ps.size() == 1 && ps[0].ntok >= kSplitTokens) {
+    std::vector<Pass> two;
+    if (piece_windows > 0) {
+      const int64_t pw = c.piece_tokens / c.window_tokens;  // windows per piece
+      const int64_t np = (ps[0].nwin + pw - 1) / pw;
+      if (np >= 2) {
+        const int64_t b = (np / 2) * pw;
+        two = split_passes(c, wins, mt, full, [&](int64_t i) { return i == b; });
+      }
+    } else {
+      const int64_t half = (ps[0].ntok + 1) / 2;
+      two = split_passes(c, wins, half + c.window_tokens - 1, full, [](int64_t) { return false; });
+    }
+    if (two.size() == 2) ps.swap(two);
+  }
   return ps;
 }
 
@@ -387,6 +460,10 @@ struct encoder {
   };
   std::vector<Lane> lanes;
   hipEvent_t passes_ready = nullptr;
+  // recorded on the caller's stream at the end of every call that used the workspace: a buffer
+  // that must grow waits for it before the old one is freed (one call is in flight per handle)
+  hipEvent_t call_done = nullptr;
+  bool call_pending = false;
   Buf rs_taps;            // polyphase table of the last input-conditioning rate
   int32_t rs_rate = 0;
   int64_t ws_bytes = 0, ws_peak = 0;
@@ -394,8 +471,10 @@ struct encoder {
   void* pinned = nullptr;
   int64_t pinned_bytes = 0;
   hipEvent_t upload_done = nullptr;
-  // timing
-  bool timing = false;
+  // timing: 0 off; 1 the passes of an untimed call, one after another on one lane; 2 as 1 but
+  // a call that fits one pass is not split into halves
+  int timing = 0;
+  hipError_t timing_err = hipSuccess;  // first failed event record of the current call
   std::vector<TimedLaunch> timed;
   std::vector<hipEvent_t> event_pool;
   size_t event_next = 0;
@@ -406,7 +485,11 @@ namespace {
 encoder_status ensure(encoder* e, encoder::Buf& b, int64_t bytes) {
   if (b.bytes >= bytes) return ENC_OK;
   if (b.p) {
-    AE_HIP(hipDeviceSynchronize());  // the old buffer may still be read by queued work
+    // the old buffer may still be read by the previous call's queued work
+    if (e->call_pending) {
+      AE_HIP(hipEventSynchronize(e->call_done));
+      e->call_pending = false;
+    }
     AE_HIP(hipFree(b.p));
     e->ws_bytes -= b.bytes;
     b.p = nullptr;
@@ -437,32 +520,50 @@ hipEvent_t next_event(encoder* e) {
   return e->event_pool[e->event_next++];
 }
 
-// brackets one launch with events when timing is on
+// Brackets one launch with events when timing is on.  A failed event creation or record is
+// kept in e->timing_err (the first one of the call) and reported by LAUNCH.
 struct Tm {
   encoder* e;
   int kid;
   hipStream_t s;
   hipEvent_t a = nullptr;
+  void note(hipError_t err) {
+    if (err != hipSuccess && e->timing_err == hipSuccess) e->timing_err = err;
+  }
   Tm(encoder* e_, int k, hipStream_t s_) : e(e_), kid(k), s(s_) {
-    if (e->timing && (a = next_event(e))) hipEventRecord(a, s);
+    if (!e->timing) return;
+    a = next_event(e);
+    if (!a) {
+      note(hipErrorOutOfMemory);
+      return;
+    }
+    const hipError_t err = hipEventRecord(a, s);
+    if (err != hipSuccess) {
+      a = nullptr;
+      note(err);
+    }
   }
   ~Tm() {
     if (!a) return;
     hipEvent_t b = next_event(e);
-    if (!b) return;
-    hipEventRecord(b, s);
+    const hipError_t err = b ? hipEventRecord(b, s) : hipErrorOutOfMemory;
+    if (err != hipSuccess) {
+      note(err);
+      return;
+    }
     e->timed.push_back({kid, a, b});
   }
 };
 
-#define LAUNCH(kid, call)                              \
-  do {                                                 \
-    hipError_t _err;                                   \
-    {                                                  \
-      Tm _tm(e, kid, s);                               \
-      _err = (call);                                   \
-    }                                                  \
-    if (_err != hipSuccess) return hip_fail(_err, #call); \
+#define LAUNCH(kid, call)                                                          \
+  do {                                                                             \
+    hipError_t _err;                                                               \
+    {                                                                              \
+      Tm _tm(e, kid, s);                                                           \
+      _err = (call);                                                               \
+    }                                                                              \
+    if (_err != hipSuccess) return hip_fail(_err, #call);                          \
+    if (e->timing_err != hipSuccess) return hip_fail(e->timing_err, "hipEventRecord"); \
   } while (0)
 
 // log-mel of n_frames frames over nclip clips
@@ -482,13 +583,14 @@ encoder_status size_call(encoder* e, int64_t nclip, int64_t n_frames, int64_t n_
   return ensure(e, e->tpos, std::max<int64_t>(n_tok_total, 1) * 4);
 }
 
-// activation workspace of one lane for passes of up to mt tokens / mw windows
-encoder_status size_lane(encoder* e, encoder::Lane& ln, int64_t mt, int64_t mw) {
+// activation workspace of one lane for passes of up to mt tokens, rows1 act1 time rows
+// (windows x L1s) and rows2 act2 time rows (windows x L2s)
+encoder_status size_lane(encoder* e, encoder::Lane& ln, int64_t mt, int64_t rows1, int64_t rows2) {
   const encoder_cfg& c = e->cfg;
-  const int64_t es = (int64_t)e->esz, C = c.conv_channels, W = c.window_tokens, d = c.d_model;
+  const int64_t es = (int64_t)e->esz, C = c.conv_channels, d = c.d_model;
   encoder_status st;
-  if ((st = ensure(e, ln.act1, mw * 4 * W * 64 * C * es))) return st;
-  if ((st = ensure(e, ln.act2, mw * 2 * W * 32 * C * es))) return st;
+  if ((st = ensure(e, ln.act1, rows1 * 64 * C * es))) return st;
+  if ((st = ensure(e, ln.act2, rows2 * 32 * C * es))) return st;
   if ((st = ensure(e, ln.tokA, mt * 16 * C * es))) return st;
   if ((st = ensure(e, ln.resid, mt * d * 4))) return st;
   if ((st = ensure(e, ln.xn, mt * d * es))) return st;
@@ -572,6 +674,8 @@ encoder_status run_pass(encoder* e, encoder::Lane& ln, const Pass& p, void* out,
   g.wins = reinterpret_cast<const Win*>(e->wtab.p) + p.win0;
   g.n_win = (int32_t)p.nwin;
   g.W = W;
+  g.L1s = p.L1s;
+  g.L2s = p.L2s;
   g.n_tok = p.ntok;
   g.tok_pos = reinterpret_cast<const int32_t*>(e->tpos.p) + p.tok0;
   const int64_t M = p.ntok;
@@ -586,7 +690,7 @@ encoder_status run_pass(encoder* e, encoder::Lane& ln, const Pass& p, void* out,
   T* z = (T*)ln.z.p;
 
   LAUNCH(ENC_K_CONV1, launch_conv1<T>(g, (const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
-                                      e->conv1_w, e->conv1_b, C, act1, s));
+                                      nullptr, e->conv1_w, e->conv1_b, C, act1, s));
   if (stop == ST_CONV1) return ENC_OK;
   LAUNCH(ENC_K_CONV2, launch_conv_igemm<T>(g, 2, act1, (const T*)e->conv2_w, e->conv2_b, C, act2, s));
   if (stop == ST_CONV2) return ENC_OK;
@@ -680,11 +784,12 @@ encoder_status check_forward_args(encoder* e, const void* pcm, int64_t n_samples
   if (!e) return invalid("encoder handle is NULL");
   if (!pcm || !out) return invalid("pcm and output pointers must be non-NULL");
   if (batch < 1) return invalid("batch must be >= 1");
+  if (batch > 65535) return invalid("batch must be <= 65535");
   if (n_samples <= e->cfg.n_fft / 2)
     return invalid("n_samples must exceed n_fft/2 = 200 (reflect padding)");
   if (n_samples / e->cfg.hop >= (int64_t(1) << 30)) return invalid("clip too long");
-  if ((int64_t)batch * frames_out(e->cfg, n_samples) >= (int64_t(1) << 31))
-    return invalid("too many output frames for one call");
+  if ((int64_t)batch * (n_samples / e->cfg.hop) >= (int64_t(1) << 31))
+    return invalid("too many log-mel frames for one call");
   return ENC_OK;
 }
 
@@ -694,38 +799,18 @@ encoder_status forward_impl(encoder* e, const float* pcm, const std::vector<int6
                             int stop_layer = -1, float* dst = nullptr, int64_t dst_elems = 0,
                             TapReq* taps = nullptr) {
   AE_HIP(hipSetDevice(e->device));
+  e->timing_err = hipSuccess;
   const encoder_cfg& c = e->cfg;
   const int32_t batch = (int32_t)lens.size();
   std::vector<ClipSpan> clips;
   clip_spans(c, lens, clips);
   std::vector<Win> wins;
   plan_windows(c, lens, wins);
-  const int64_t mt = max_tokens(c), mw = max_windows(c);
-  std::vector<Pass> ps = split_passes(wins, mt, mw, [&](int64_t i) {
-    return piece_windows > 0 && i % piece_windows == 0;
-  });
-  if (stop >= 0 && ps.size() > 1) return invalid("debug stages need a single pass");
-  // The passes of a call run concurrently on lanes, and two passes' kernels overlap where one
-  // pass alone leaves the GPU partly idle (attention, LayerNorm, a GEMM's last round of tiles).
-  // A call that fits one pass but has at least kSplitTokens tokens therefore runs as two halves
-  // of whole windows (whole pieces in long mode).  A window's rows are the same in any pass.
-  // Kernel-by-kernel timing runs one lane, where halves would only under-fill the GPU, so it
-  // keeps the single pass.
-  if (ps.size() == 1 && stop < 0 && !e->timing && ps[0].ntok >= kSplitTokens) {
-    std::vector<Pass> two;
-    if (piece_windows > 0) {
-      const int64_t pw = c.piece_tokens / c.window_tokens;  // windows per piece
-      const int64_t np = (ps[0].nwin + pw - 1) / pw;
-      if (np >= 2) {
-        const int64_t b = (np / 2) * pw;
-        two = split_passes(wins, mt, mw, [&](int64_t i) { return i == b; });
-      }
-    } else {
-      const int64_t half = (ps[0].ntok + 1) / 2;
-      two = split_passes(wins, half + c.window_tokens - 1, mw, [](int64_t) { return false; });
-    }
-    if (two.size() == 2) ps.swap(two);
-  }
+  // Debug stages export the padded conv layouts from a single pass; kernel-by-kernel timing
+  // runs one lane, where halves help only when asked for (timing mode 1).
+  const bool debug = stop >= 0;
+  const std::vector<Pass> ps = plan_passes(c, wins, piece_windows, !debug && e->timing != 2, debug);
+  if (debug && ps.size() > 1) return invalid("debug stages need a single pass");
   int64_t ntok = 0, n_frames = 0, t_max = 0;
   for (auto& p : ps) ntok += p.ntok;
   for (int64_t n : lens) {
@@ -735,55 +820,68 @@ encoder_status forward_impl(encoder* e, const float* pcm, const std::vector<int6
   const int64_t T = t_max;  // equal to every clip's frame count on the debug paths
   // lanes: concurrent passes (bitwise the same as one after another), unless the call has a
   // single pass, stops at a debug stage or is timed kernel by kernel
-  const int nl = (ps.size() > 1 && stop < 0 && !e->timing)
+  const int nl = (ps.size() > 1 && !debug && !e->timing)
                      ? (int)std::min<size_t>(ps.size(), (size_t)kLanes) : 1;
-  int64_t mtp = 1, mwp = 1;  // largest pass of the call
+  int64_t mtp = 1, rows1 = 1, rows2 = 1;  // largest pass of the call
   for (const Pass& p : ps) {
     mtp = std::max<int64_t>(mtp, p.ntok);
-    mwp = std::max<int64_t>(mwp, p.nwin);
+    rows1 = std::max<int64_t>(rows1, p.nwin * p.L1s);
+    rows2 = std::max<int64_t>(rows2, p.nwin * p.L2s);
   }
-  (void)mt;
-  (void)mw;
   if ((int)e->lanes.size() < nl) e->lanes.resize(nl);
   encoder_status st = size_call(e, batch, n_frames, (int64_t)wins.size(), ntok);
   if (st) return st;
   for (int i = 0; i < nl; ++i)
-    if ((st = size_lane(e, e->lanes[i], mtp, mwp))) return st;
-  if ((st = upload_plan(e, clips, wins, ps, s))) return st;
-  if ((st = run_mel(e, pcm, batch, t_max, s))) return st;
-  if (stop == ST_MEL) {
-    LAUNCH(ENC_K_OTHER, launch_mel_normalize((const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
-                                             T, batch, dst, s));
-    return ENC_OK;
-  }
-  if (taps) taps->ntok_total = ntok;
-  auto pass = [&](encoder::Lane& ln, const Pass& p, hipStream_t ps_) {
-    return e->bf16 ? run_pass<bf16_t>(e, ln, p, out, ps_, stop, stop_layer, taps)
-                   : run_pass<float>(e, ln, p, out, ps_, stop, stop_layer, taps);
-  };
-  if (nl == 1) {
-    for (const Pass& p : ps)
-      if ((st = pass(e->lanes[0], p, s))) return st;
-  } else {
-    // fork after the log-mel, passes round-robin over the lanes, join on the caller's stream
+    if ((st = size_lane(e, e->lanes[i], mtp, rows1, rows2))) return st;
+  if (nl > 1) {
     if (!e->passes_ready) AE_HIP(hipEventCreateWithFlags(&e->passes_ready, hipEventDisableTiming));
     for (int i = 0; i < nl; ++i) {
       encoder::Lane& ln = e->lanes[i];
       if (!ln.stream) AE_HIP(hipStreamCreateWithFlags(&ln.stream, hipStreamNonBlocking));
       if (!ln.done) AE_HIP(hipEventCreateWithFlags(&ln.done, hipEventDisableTiming));
     }
-    AE_HIP(hipEventRecord(e->passes_ready, s));
-    for (int i = 0; i < nl; ++i) AE_HIP(hipStreamWaitEvent(e->lanes[i].stream, e->passes_ready, 0));
-    for (size_t j = 0; j < ps.size(); ++j) {
-      encoder::Lane& ln = e->lanes[j % nl];
-      if ((st = pass(ln, ps[j], ln.stream))) return st;
-    }
-    for (int i = 0; i < nl; ++i) {
-      AE_HIP(hipEventRecord(e->lanes[i].done, e->lanes[i].stream));
-      AE_HIP(hipStreamWaitEvent(s, e->lanes[i].done, 0));
+  }
+  if ((st = upload_plan(e, clips, wins, ps, s))) return st;
+  // from here on the call has work queued on s: its end is marked for the next workspace
+  // growth, on every way out of this function
+  struct CallDone {
+    encoder* e;
+    hipStream_t s;
+    ~CallDone() { e->call_pending = hipEventRecord(e->call_done, s) == hipSuccess; }
+  } call_done_guard{e, s};
+  encoder_status body = ENC_OK;
+  if ((body = run_mel(e, pcm, batch, t_max, s)) == ENC_OK && stop == ST_MEL) {
+    LAUNCH(ENC_K_OTHER, launch_mel_normalize((const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
+                                             T, batch, dst, s));
+  } else if (body == ENC_OK) {
+    if (taps) taps->ntok_total = ntok;
+    auto pass = [&](encoder::Lane& ln, const Pass& p, hipStream_t ps_) {
+      return e->bf16 ? run_pass<bf16_t>(e, ln, p, out, ps_, stop, stop_layer, taps)
+                     : run_pass<float>(e, ln, p, out, ps_, stop, stop_layer, taps);
+    };
+    if (nl == 1) {
+      for (const Pass& p : ps)
+        if ((body = pass(e->lanes[0], p, s))) break;
+    } else {
+      // fork after the log-mel, passes round-robin over the lanes, join on the caller's stream;
+      // the join is enqueued even when a pass fails to enqueue, so that no lane's earlier work
+      // is left running past the end of the call's work on s
+      hipError_t err = hipEventRecord(e->passes_ready, s);
+      for (int i = 0; i < nl && err == hipSuccess; ++i)
+        err = hipStreamWaitEvent(e->lanes[i].stream, e->passes_ready, 0);
+      if (err != hipSuccess) return hip_fail(err, "fork onto the lanes");
+      for (size_t j = 0; j < ps.size() && body == ENC_OK; ++j) {
+        encoder::Lane& ln = e->lanes[j % nl];
+        body = pass(ln, ps[j], ln.stream);
+      }
+      for (int i = 0; i < nl; ++i) {
+        err = hipEventRecord(e->lanes[i].done, e->lanes[i].stream);
+        if (err == hipSuccess) err = hipStreamWaitEvent(s, e->lanes[i].done, 0);
+        if (err != hipSuccess && body == ENC_OK) body = hip_fail(err, "join of the lanes");
+      }
     }
   }
-  if (stop >= 0) {
+  if (body == ENC_OK && debug && stop != ST_MEL) {
     const Pass& p = ps[0];
     const int64_t W = c.window_tokens, C = c.conv_channels;
     const void* src = nullptr;
@@ -794,18 +892,29 @@ encoder_status forward_impl(encoder* e, const float* pcm, const std::vector<int6
       case ST_CONV3: src = e->lanes[0].tokA.p; n = p.ntok * 16 * C; break;
       case ST_EMBED:
       case ST_LAYER:
-        if (dst_elems < p.ntok * c.d_model) return invalid("dst too small for this stage");
-        AE_HIP(hipMemcpyAsync(dst, e->lanes[0].resid.p, p.ntok * c.d_model * 4, hipMemcpyDeviceToDevice, s));
-        return ENC_OK;
+        src = e->lanes[0].resid.p;
+        n = p.ntok * c.d_model;
+        break;
       case ST_HEAD: src = e->lanes[0].z.p; n = p.ntok * c.d_out; break;
       case ST_OUT: src = out; n = p.ntok * c.d_out; break;
-      default: return invalid("unknown stage");
+      default: body = invalid("unknown stage");
     }
-    if (dst_elems < n) return invalid("dst too small for this stage");
-    if (e->bf16) LAUNCH(ENC_K_OTHER, launch_to_f32<bf16_t>((const bf16_t*)src, n, dst, s));
-    else LAUNCH(ENC_K_OTHER, launch_to_f32<float>((const float*)src, n, dst, s));
+    if (body == ENC_OK && dst_elems < n) body = invalid("dst too small for this stage");
+    if (body == ENC_OK) {
+      if (stop == ST_EMBED || stop == ST_LAYER) {
+        const hipError_t err = hipMemcpyAsync(dst, src, n * 4, hipMemcpyDeviceToDevice, s);
+        if (err != hipSuccess) body = hip_fail(err, "hipMemcpyAsync(stage)");
+      } else {
+        auto cvt = [&]() -> encoder_status {
+          if (e->bf16) LAUNCH(ENC_K_OTHER, launch_to_f32<bf16_t>((const bf16_t*)src, n, dst, s));
+          else LAUNCH(ENC_K_OTHER, launch_to_f32<float>((const float*)src, n, dst, s));
+          return ENC_OK;
+        };
+        body = cvt();
+      }
+    }
   }
-  return ENC_OK;
+  return body;
 }
 
 void free_all(encoder* e) {
@@ -824,6 +933,7 @@ void free_all(encoder* e) {
     if (ln.done) hipEventDestroy(ln.done);
   }
   if (e->passes_ready) hipEventDestroy(e->passes_ready);
+  if (e->call_done) hipEventDestroy(e->call_done);
   if (e->wdev) hipFree(e->wdev);
   if (e->qdev) hipFree(e->qdev);
   if (e->fdev) hipFree(e->fdev);
@@ -898,6 +1008,32 @@ encoder_status encoder_plan_windows_ragged(const encoder_cfg* cfg, const int64_t
     int32_t* r = table + 7 * (int64_t)i;
     r[0] = w[i].clip; r[1] = w[i].start; r[2] = w[i].L0; r[3] = w[i].L1;
     r[4] = w[i].L2; r[5] = w[i].L3; r[6] = w[i].tok;
+  }
+  return ENC_OK;
+}
+
+encoder_status encoder_plan_passes(const encoder_cfg* cfg, const int64_t* lengths, int32_t n_clips,
+                                   int32_t pieces_per_pass, int64_t* table, int32_t max_passes,
+                                   int32_t* n_passes) {
+  encoder_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!n_passes) return invalid("n_passes is NULL");
+  if (max_passes > 0 && !table) return invalid("table is NULL");
+  if (pieces_per_pass < 0) return invalid("pieces_per_pass must be >= 0");
+  if (pieces_per_pass > 0 && n_clips != 1) return invalid("long mode takes one recording (n_clips = 1)");
+  std::vector<int64_t> lens;
+  if ((st = ragged_lengths(*cfg, lengths, n_clips, lens))) return st;
+  const int64_t pw = cfg->piece_tokens / cfg->window_tokens;
+  if (pieces_per_pass > 0 && (int64_t)pieces_per_pass * cfg->piece_tokens > pass_token_cap(*cfg))
+    return invalid("pieces_per_pass pieces exceed the tokens of one pass");
+  std::vector<Win> w;
+  plan_windows(*cfg, lens, w);
+  const std::vector<Pass> ps = plan_passes(*cfg, w, pieces_per_pass > 0 ? pw * pieces_per_pass : 0, true, false);
+  *n_passes = (int32_t)ps.size();
+  for (int32_t i = 0; i < std::min<int32_t>(max_passes, (int32_t)ps.size()); ++i) {
+    int64_t* r = table + 6 * (int64_t)i;
+    r[0] = ps[i].win0; r[1] = ps[i].nwin; r[2] = ps[i].tok0; r[3] = ps[i].ntok;
+    r[4] = ps[i].L1s; r[5] = ps[i].L2s;
   }
   return ENC_OK;
 }
@@ -1126,6 +1262,7 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
   if (err == hipSuccess) err = hipMemcpy(e->wdev, wh.data(), woff * (int64_t)es, hipMemcpyHostToDevice);
   if (err == hipSuccess) err = hipMemcpy(e->fdev, fh.data(), foff * 4, hipMemcpyHostToDevice);
   if (err == hipSuccess) err = hipEventCreateWithFlags(&e->upload_done, hipEventDisableTiming);
+  if (err == hipSuccess) err = hipEventCreateWithFlags(&e->call_done, hipEventDisableTiming);
   if (err == hipSuccess) err = hipEventRecord(e->upload_done, nullptr);
   if (err != hipSuccess) {
     encoder_status r = hip_fail(err, "encoder_create");
@@ -1193,9 +1330,11 @@ encoder_status encoder_forward_long(encoder* e, const float* pcm, int64_t n_samp
   if (st) return st;
   if (pieces_per_pass < 1) return invalid("pieces_per_pass must be >= 1");
   const int64_t pw = e->cfg.piece_tokens / e->cfg.window_tokens;  // windows per piece
-  if ((int64_t)pieces_per_pass * e->cfg.piece_tokens > max_tokens(e->cfg) ||
-      (int64_t)pieces_per_pass * pw > max_windows(e->cfg))
+  if ((int64_t)pieces_per_pass * e->cfg.piece_tokens > max_tokens(e->cfg))
     return invalid("pieces_per_pass * piece_tokens exceeds max_tokens_per_pass");
+  if ((int64_t)pieces_per_pass * e->cfg.piece_tokens > pass_token_cap(e->cfg) ||
+      (int64_t)pieces_per_pass * pw * 4 * e->cfg.window_tokens * act1_row_bytes(e->cfg) > kMaxOperandBytes)
+    return invalid("pieces_per_pass pieces exceed what one pass can address (2^31 - 1 bytes per operand)");
   return forward_impl(e, pcm, std::vector<int64_t>(1, n_samples), out, (hipStream_t)stream,
                       pw * pieces_per_pass);
 }
@@ -1294,6 +1433,8 @@ encoder_status encoder_condition_audio(encoder* e, const float* in, int64_t n_in
   }
   LAUNCH(ENC_K_OTHER, launch_resample(in, n_in, channels, r.L, r.M, r.K, (const float*)e->rs_taps.p,
                                       out, conditioned_length(n_in, r), s));
+  AE_HIP(hipEventRecord(e->call_done, s));  // the filter table is read until here
+  e->call_pending = true;
   return ENC_OK;
 }
 
@@ -1308,10 +1449,15 @@ encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, 
   std::vector<ClipSpan> clips;
   clip_spans(e->cfg, std::vector<int64_t>((size_t)batch, n_samples), clips);
   if ((st = upload_plan(e, clips, {}, {}, s))) return st;
-  if ((st = run_mel(e, pcm, batch, T, s))) return st;
-  LAUNCH(ENC_K_OTHER, launch_mel_normalize((const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
-                                           T, batch, mel, s));
-  return ENC_OK;
+  st = run_mel(e, pcm, batch, T, s);
+  if (st == ENC_OK) {
+    const hipError_t err = launch_mel_normalize((const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
+                                                T, batch, mel, s);
+    if (err != hipSuccess) st = hip_fail(err, "launch_mel_normalize");
+  }
+  // the workspace is read until here
+  e->call_pending = hipEventRecord(e->call_done, s) == hipSuccess;
+  return st;
 }
 
 encoder_status encoder_debug_stage(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
@@ -1332,7 +1478,8 @@ encoder_status encoder_debug_stage(encoder* e, const float* pcm, int64_t n_sampl
 
 encoder_status encoder_timing_enable(encoder* e, int32_t enable) {
   if (!e) return invalid("encoder handle is NULL");
-  e->timing = enable != 0;
+  if (enable < 0 || enable > 2) return invalid("timing mode must be 0, 1 or 2");
+  e->timing = enable;
   return ENC_OK;
 }
 
@@ -1436,6 +1583,75 @@ encoder_status encoder_op_attention(const void* qkv, const int32_t* windows, int
     err = launch_attention<float>((const float*)qkv, nullptr, windows, n_windows, n_heads,
                                   n_heads * 64, (float*)out, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "encoder_op_attention");
+  return ENC_OK;
+}
+
+// Window tables of the kernel-level conv entries: copied to the host and checked before any
+// launch, so that no kernel reads or writes outside the buffers the caller described.
+static encoder_status check_conv_windows(const int32_t* windows, int32_t n_windows, int32_t W, int32_t L1s,
+                                         int64_t n_tok, int64_t mel_rows, int32_t n_clips, bool conv1) {
+  if (n_windows < 1) return invalid("n_windows must be >= 1");
+  if (W < 1 || W > 128) return invalid("window_tokens must be in [1, 128]");
+  if (L1s < 1 || L1s > 4 * W) return invalid("L1s must be in [1, 4 * window_tokens]");
+  std::vector<Win> h((size_t)n_windows);
+  AE_HIP(hipMemcpy(h.data(), windows, h.size() * sizeof(Win), hipMemcpyDeviceToHost));
+  for (int32_t i = 0; i < n_windows; ++i) {
+    const Win& w = h[i];
+    const std::string at = "window " + std::to_string(i) + ": ";
+    if (w.L0 < 1 || w.L0 > 8 * W || w.L1 != (w.L0 + 1) / 2 || w.L2 != (w.L1 + 1) / 2 ||
+        w.L3 != (w.L2 + 1) / 2)
+      return invalid(at + "lengths must be 1 <= L0 <= 8W and the ceil chain L1..L3");
+    if (w.L1 > L1s) return invalid(at + "L1 exceeds L1s");
+    if (!conv1 && (w.tok < 0 || (int64_t)w.tok + w.L3 > n_tok)) return invalid(at + "tokens outside n_tok");
+    if (conv1 && (w.clip < 0 || w.clip >= n_clips || w.mel_row < 0 || (int64_t)w.mel_row + w.L0 > mel_rows))
+      return invalid(at + "clip or mel rows outside the inputs");
+  }
+  return ENC_OK;
+}
+
+encoder_status encoder_op_conv1(const float* mel, int64_t mel_rows, const float* clip_max, int32_t n_clips,
+                                const int32_t* windows, int32_t n_windows, int32_t window_tokens,
+                                int32_t L1s, const float* w, const float* b, int32_t C, void* act1,
+                                int32_t dtype, void* stream) {
+  if (!mel || !clip_max || !windows || !w || !b || !act1) return invalid("pointers must be non-NULL");
+  if (C < 32 || C % 32 || C > 2048) return invalid("C must be a multiple of 32 in [32, 2048]");
+  if (dtype != ENC_BF16 && dtype != ENC_F32) return invalid("bad dtype");
+  if (n_clips < 1 || mel_rows < 1) return invalid("n_clips and mel_rows must be >= 1");
+  encoder_status st = check_conv_windows(windows, n_windows, window_tokens, L1s, 0, mel_rows, n_clips, true);
+  if (st) return st;
+  PassGeom g{reinterpret_cast<const Win*>(windows), n_windows, window_tokens, L1s, (L1s + 1) / 2, 0, nullptr};
+  hipError_t err;
+  if (dtype == ENC_BF16)
+    err = launch_conv1<bf16_t>(g, mel, nullptr, clip_max, w, b, C, (bf16_t*)act1, (hipStream_t)stream);
+  else
+    err = launch_conv1<float>(g, mel, nullptr, clip_max, w, b, C, (float*)act1, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "encoder_op_conv1");
+  return ENC_OK;
+}
+
+encoder_status encoder_op_conv(int32_t level, const void* in, const int32_t* windows, int32_t n_windows,
+                               int32_t window_tokens, int32_t L1s, int64_t n_tok, const void* w_packed,
+                               const float* bias, int32_t C, void* out, int32_t dtype, void* stream) {
+  if (!in || !windows || !w_packed || !bias || !out) return invalid("pointers must be non-NULL");
+  if (level != 2 && level != 3) return invalid("level must be 2 (conv2) or 3 (conv3)");
+  if (C < 32 || C % 32 || C > 4096) return invalid("C must be a multiple of 32 in [32, 4096]");
+  if (dtype != ENC_BF16 && dtype != ENC_F32) return invalid("bad dtype");
+  if (n_tok < 0) return invalid("n_tok must be >= 0");
+  encoder_status st = check_conv_windows(windows, n_windows, window_tokens, L1s, n_tok, 0, 0, false);
+  if (st) return st;
+  const int64_t es = dtype == ENC_BF16 ? 2 : 4;
+  const int32_t L2s = (L1s + 1) / 2;
+  if ((int64_t)n_windows * L1s * 64 * C * es > kMaxOperandBytes || n_tok * 16 * C * es > kMaxOperandBytes)
+    return invalid("an operand exceeds 2^31 - 1 bytes");
+  PassGeom g{reinterpret_cast<const Win*>(windows), n_windows, window_tokens, L1s, L2s, n_tok, nullptr};
+  hipError_t err;
+  if (dtype == ENC_BF16)
+    err = launch_conv_igemm<bf16_t>(g, level, (const bf16_t*)in, (const bf16_t*)w_packed, bias, C, (bf16_t*)out,
+                                    (hipStream_t)stream);
+  else
+    err = launch_conv_igemm<float>(g, level, (const float*)in, (const float*)w_packed, bias, C, (float*)out,
+                                   (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "encoder_op_conv");
   return ENC_OK;
 }
 

@@ -11,7 +11,7 @@
 // one window.  It stages the 2*RT+1 normalised mel frames those steps touch in LDS (zero rows and
 // columns for the padding).  Each thread keeps the 9 taps and the bias of its 8 output channels
 // in registers and emits 16-byte stores; CG = C/8 consecutive threads write one contiguous
-// C-channel position.
+// C-channel position.  Window w's rows start at w * L1s (the pass's time stride).
 #include <algorithm>
 
 #include "ae_internal.h"
@@ -45,9 +45,10 @@ template <> struct Pack8<float> {
 
 // blockDim.x = CG * FQ; thread -> channel group cg = tid % CG, frequency phase fq = tid / CG
 template <typename T>
-__global__ __launch_bounds__(256) void conv1_kernel(const Win* __restrict__ wins, int32_t W,
+__global__ __launch_bounds__(256) void conv1_kernel(const Win* __restrict__ wins, int32_t L1s,
                                                     const float* __restrict__ mel,
                                                     const uint32_t* __restrict__ max_key,
+                                                    const float* __restrict__ max_f,
                                                     const float* __restrict__ wt,
                                                     const float* __restrict__ bias, int32_t C,
                                                     T* __restrict__ act1) {
@@ -56,14 +57,15 @@ __global__ __launch_bounds__(256) void conv1_kernel(const Win* __restrict__ wins
   const int FQ = blockDim.x / CG;
   const int tid = threadIdx.x;
   const int cg = tid % CG, fq = tid / CG;
-  const int L1max = 4 * W;
-  const int nrb = (L1max + RT - 1) / RT;
+  const int nrb = (L1s + RT - 1) / RT;
   const int w = blockIdx.x / nrb;
   const int t1_0 = (blockIdx.x - w * nrb) * RT;
   const Win wn = wins[w];
   if (t1_0 >= wn.L1) return;
 
-  const float lo = key_to_float_c(max_key[wn.clip]) - 8.0f;
+  // the clip's maximum: ordered-integer key from the log-mel kernel, or a float (kernel-level
+  // entry); uniform over the workgroup
+  const float lo = (max_f ? max_f[wn.clip] : key_to_float_c(max_key[wn.clip])) - 8.0f;
   const float* mrow = mel + (int64_t)wn.mel_row * 128;
   for (int i = tid; i < (2 * RT + 1) * 130; i += blockDim.x) {
     const int r = i / 130, c = i - r * 130;
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void conv1_kernel(const Win* __restrict__ wins
 
   const int rows = min(RT, wn.L1 - t1_0);
   for (int r = 0; r < rows; ++r) {
-    T* orow = act1 + (((int64_t)w * L1max + t1_0 + r) * 64) * C + cg * 8;
+    T* orow = act1 + (((int64_t)w * L1s + t1_0 + r) * 64) * C + cg * 8;
     for (int f1 = fq; f1 < 64; f1 += FQ) {
       float xv[9];
 #pragma unroll
@@ -109,23 +111,25 @@ __global__ __launch_bounds__(256) void conv1_kernel(const Win* __restrict__ wins
 }  // namespace
 
 template <typename T>
-hipError_t launch_conv1(const PassGeom& g, const float* mel, const uint32_t* max_key,
+hipError_t launch_conv1(const PassGeom& g, const float* mel, const uint32_t* max_key, const float* max_f,
                         const float* w, const float* b, int32_t C, T* act1, hipStream_t s) {
   const int CG = C / 8;
   const int FQ = std::max(1, std::min(64, 256 / CG));
   const int threads = CG * FQ;
   if (threads > 256 || threads < 1) return hipErrorInvalidValue;
-  const int nrb = (4 * g.W + RT - 1) / RT;
+  if (g.L1s < 1 || g.L1s > 4 * g.W) return hipErrorInvalidValue;
+  const int nrb = (g.L1s + RT - 1) / RT;
   const int64_t blocks = (int64_t)g.n_win * nrb;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(conv1_kernel<T>, dim3((unsigned)blocks), dim3(threads), 0, s, g.wins, g.W,
-                     mel, max_key, w, b, C, act1);
+  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(conv1_kernel<T>, dim3((unsigned)blocks), dim3(threads), 0, s, g.wins, g.L1s,
+                     mel, max_key, max_f, w, b, C, act1);
   return hipGetLastError();
 }
 
-template hipError_t launch_conv1<bf16_t>(const PassGeom&, const float*, const uint32_t*,
+template hipError_t launch_conv1<bf16_t>(const PassGeom&, const float*, const uint32_t*, const float*,
                                          const float*, const float*, int32_t, bf16_t*, hipStream_t);
-template hipError_t launch_conv1<float>(const PassGeom&, const float*, const uint32_t*,
+template hipError_t launch_conv1<float>(const PassGeom&, const float*, const uint32_t*, const float*,
                                         const float*, const float*, int32_t, float*, hipStream_t);
 
 }  // namespace ae

@@ -1402,8 +1402,11 @@ hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T*
                              const float* bias, int32_t C, T* out, hipStream_t s) {
   const int Fin = level == 2 ? 64 : 32;
   const int Fout = Fin / 2;
-  const int Lin_max = level == 2 ? 4 * g.W : 2 * g.W;
-  const int Lout_max = Lin_max / 2;
+  // the pass's time strides: act1 rows L1s, act2 rows L2s = ceil(L1s / 2); conv3 output rows
+  // are token rows (each window's valid ones only)
+  const int Lin_max = level == 2 ? g.L1s : g.L2s;
+  const int Lout_max = (Lin_max + 1) / 2;
+  if (g.L1s < 1 || g.L1s > 4 * g.W || g.L2s != (g.L1s + 1) / 2) return hipErrorInvalidValue;
   const int rows_per_win = Lout_max * Fout;
   const int64_t m_rows = (int64_t)g.n_win * rows_per_win;
   AConv<T> as{in, g.wins, C, Fin, Fout, Lin_max, level, rows_per_win, 9 * C, m_rows,

@@ -91,11 +91,15 @@ struct ClipSpan {
   int64_t frame_off;  // first log-mel frame (row)
 };
 
-// Geometry of one pass over a group of windows.
+// Geometry of one pass over a group of windows.  The conv activations hold every window of
+// the pass at one time stride: act1 [n_win][L1s][64][C] and act2 [n_win][L2s][32][C], where
+// L1s is at least the longest conv1 output of the pass (at most 4W) and L2s = ceil(L1s / 2).
+// Windows of short clips thus take only the rows they use.
 struct PassGeom {
   const Win* wins;     // device, n_win entries
   int32_t n_win;
-  int32_t W;           // window tokens; window frames = 8W, L1max = 4W, L2max = 2W, L3max = W
+  int32_t W;           // window tokens; window frames = 8W
+  int32_t L1s, L2s;    // time rows per window of act1 and act2 in this pass
   int64_t n_tok;
   const int32_t* tok_pos;  // device, n_tok entries: position of each token within its window
 };
@@ -133,9 +137,11 @@ hipError_t launch_clear_u32(uint32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_mel_normalize(const float* raw, const uint32_t* max_key, int64_t T,
                                 int32_t nclip, float* out, hipStream_t s);
 
-// conv1: raw packed mel (window rows at Win::mel_row) + max -> act1 [n_win][4W][64][C]
+// conv1: raw packed mel (window rows at Win::mel_row) + the clip maxima -> act1
+// [n_win][L1s][64][C].  The maxima come as ordered-integer keys (max_key, from the log-mel
+// kernel) or, when max_f is not null, as floats.
 template <typename T>
-hipError_t launch_conv1(const PassGeom& g, const float* mel, const uint32_t* max_key,
+hipError_t launch_conv1(const PassGeom& g, const float* mel, const uint32_t* max_key, const float* max_f,
                         const float* w, const float* b, int32_t C, T* act1, hipStream_t s);
 
 // GEMM epilogue kinds
@@ -166,8 +172,8 @@ constexpr int64_t kSplitKScratchBytes = int64_t(64) << 20;
 template <typename T>
 hipError_t launch_linear(const LinearArgs& a, int epi, int tag, hipStream_t s);
 
-// implicit-GEMM conv (conv2: level 2, conv3: level 3).  in: [n_win][Lin_max][Fin][C],
-// out: level 2 -> [n_win][2W][32][C]; level 3 -> [n_tok][16][C]
+// implicit-GEMM conv (conv2: level 2, conv3: level 3).  in: level 2 -> act1 [n_win][L1s][64][C],
+// level 3 -> act2 [n_win][L2s][32][C]; out: level 2 -> act2; level 3 -> [n_tok][16][C]
 template <typename T>
 hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T* wpk,
                              const float* bias, int32_t C, T* out, hipStream_t s);

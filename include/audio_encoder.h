@@ -129,6 +129,26 @@ ENC_API encoder_status encoder_plan_windows_ragged(const encoder_cfg* cfg, const
                                            int32_t n_clips, int32_t* table, int32_t max_windows,
                                            int32_t* n_windows);
 
+/* The passes a forward call runs in (windows are the independent units of the tower, so a call
+ * is encoded as passes of consecutive whole windows; "SILVERTHRONE/Ossicle-4B" card, "Many clips
+ * in one question" and "Long Audio").  lengths: host int64 [n_clips] sample counts of the clips
+ * (as encoder_forward_ragged takes them; a [batch, n] call is n_clips = batch equal lengths).
+ * pieces_per_pass: 0 for the whole-clip and ragged paths; >= 1 for encoder_forward_long, which
+ * takes n_clips = 1 and starts a pass only at a multiple of pieces_per_pass 64 s pieces.  For
+ * each pass, 6 int64 values: {first window, windows, first token, tokens, act1 time rows per
+ * window L1s, act2 time rows per window L2s = ceil(L1s / 2)}; windows and tokens index the plan
+ * of encoder_plan_windows(_ragged).  The conv activations of a pass hold windows x L1s x 64 x C
+ * (act1) and windows x L2s x 32 x C (act2) elements, L1s being the longest conv1 output of the
+ * pass.  A pass never holds more than max_tokens_per_pass tokens, and none of its operands
+ * exceeds 2^31 - 1 bytes (the kernels address operands with 32-bit byte offsets): act1, and
+ * tokens x max(16C, 3 d_model, d_ffn, 2 d_adapter, d_out) elements or tokens x d_model float32
+ * (the residual).  A call of 4000 tokens or more that fits one pass is split into two halves of
+ * whole windows (whole pieces in long mode), which run concurrently.  Writes
+ * min(n_passes, max_passes) entries (table may be NULL when max_passes is 0). */
+ENC_API encoder_status encoder_plan_passes(const encoder_cfg* cfg, const int64_t* lengths, int32_t n_clips,
+                                   int32_t pieces_per_pass, int64_t* table, int32_t max_passes,
+                                   int32_t* n_passes);
+
 /* ---- handle lifecycle -------------------------------------------------------------------- */
 
 /* Packs the host float32 weight blob (n_floats values, order above) for the current HIP device:
@@ -280,6 +300,41 @@ ENC_API encoder_status encoder_op_linear_int4(const void* A, const uint8_t* q, c
 ENC_API encoder_status encoder_op_attention(const void* qkv, const int32_t* windows, int32_t n_windows,
                                     int32_t n_heads, int64_t ntok, void* out, int32_t dtype,
                                     void* stream);
+
+/* Window table of the kernel-level conv entries: device int32 [n_windows][8] per window
+ * {clip, first frame within the clip (unused here), L0, L1, L2, L3, first token, first mel row}.
+ * L0 (1..8W) is the window's frame count and L1..L3 its valid lengths after each stride-2 conv:
+ * L1 = ceil(L0/2), L2 = ceil(L1/2), L3 = ceil(L2/2) (checked on the host before any launch).
+ * Each window is an independent image: zero padding at its own time edges and at the frequency
+ * edges (the window-local reading of the "cstr/MOSS-Transcribe-preview-2B-GGUF" card's conv
+ * front end, which the "SILVERTHRONE/Ossicle-4B" card's "Long Audio" equality needs). */
+
+/* conv1 of the conv front end ("cstr/MOSS-Transcribe-preview-2B-GGUF" card, "Architecture", row
+ * "Conv front-end": Conv2D 1 -> C, 3x3, stride 2, pad 1, + bias, exact GELU) on the windows of
+ * one pass.  mel: device float32 [mel_rows][128] raw log10 mel (window i reads rows
+ * mel_row .. mel_row + L0 - 1); clip_max: device float32 [n_clips], each clip's maximum raw
+ * value; the input image is the normalised mel (max(L, clip_max - 8) + 4) / 4.  w: device
+ * float32 [C][3][3] (taps [freq][time]), b: device float32 [C].  act1: device [n_windows][L1s]
+ * [64][C] in dtype (channels innermost), L1s >= every window's L1 (at most 4W); rows at or past
+ * a window's L1 are not written.  C a multiple of 32, at most 2048.  Kernel-level test entry. */
+ENC_API encoder_status encoder_op_conv1(const float* mel, int64_t mel_rows, const float* clip_max,
+                                int32_t n_clips, const int32_t* windows, int32_t n_windows,
+                                int32_t window_tokens, int32_t L1s, const float* w, const float* b,
+                                int32_t C, void* act1, int32_t dtype, void* stream);
+
+/* conv2 (level 2) or conv3 (level 3) of the conv front end (same card and row: Conv2D C -> C,
+ * 3x3, stride 2, pad 1, + bias, exact GELU) as the library's implicit GEMM on the windows of one
+ * pass.  L2s = ceil(L1s / 2).  level 2: in = act1 [n_windows][L1s][64][C], out = act2
+ * [n_windows][L2s][32][C]; level 3: in = act2, out = token rows [n_tok][16][C] (window i's L3
+ * rows from its first token on).  w_packed: device [C_out][9][C_in] in dtype, tap index
+ * 3*freq + time (the [out][in][freq][time] weight with its taps moved outside the input
+ * channels); bias: device float32 [C].  Rows at or past a window's output length are not
+ * written.  C a multiple of 32, at most 4096; no operand above 2^31 - 1 bytes.  Kernel-level
+ * test entry. */
+ENC_API encoder_status encoder_op_conv(int32_t level, const void* in, const int32_t* windows,
+                               int32_t n_windows, int32_t window_tokens, int32_t L1s, int64_t n_tok,
+                               const void* w_packed, const float* bias, int32_t C, void* out,
+                               int32_t dtype, void* stream);
 
 /* LayerNorm of float32 rows x [M, D] -> y [M, D] in dtype; D % 256 == 0 or D % 64 == 0. */
 ENC_API encoder_status encoder_op_layernorm(const float* x, const float* gamma, const float* beta,

@@ -501,9 +501,14 @@ def test_full_c1_stagewise(full):
     l31 = enc.debug_stage(pcm, B.STAGE_LAYER, 31).cpu().numpy()
     head = enc.debug_stage(pcm, B.STAGE_HEAD).cpu().numpy()
     c3 = enc.debug_stage(pcm, B.STAGE_CONV3).cpu().numpy()
+    c1 = enc.debug_stage(pcm, B.STAGE_CONV1).cpu().numpy()  # [4 windows, 400, 64, 480]
+    c2 = enc.debug_stage(pcm, B.STAGE_CONV2).cpu().numpy()  # [4 windows, 200, 32, 480]
     res, plan = oracle_windows(x, Wt, O.FULL, [0, 3], stages=True)
-    for tok, yref, st in res:
+    for (tok, yref, st), wi in zip(res, (0, 3)):
         n = yref.shape[0]
+        L1, L2 = plan[wi]["L1"], plan[wi]["L2"]
+        check_bf16(c1[wi, :L1].reshape(L1, -1), st["conv1"][0].transpose(2, 1, 0).reshape(L1, -1), "conv1")
+        check_bf16(c2[wi, :L2].reshape(L2, -1), st["conv2"][0].transpose(2, 1, 0).reshape(L2, -1), "conv2")
         sl = slice(tok, tok + n)
         check_bf16(c3[sl].reshape(n, -1), st["conv3"][0].transpose(2, 1, 0).reshape(n, -1), "conv3")
         check_bf16(embed[sl], st["embed"], "conv_out+pos")
@@ -513,24 +518,29 @@ def test_full_c1_stagewise(full):
         check_bf16(got[sl], yref, "adapter out")
 
 
-def test_full_c2_batch_sampled_windows(full):
+def test_full_c2_every_window(full):
     enc, Wt = full
     xs = S.mixed_batch(range(101, 117))
     y = enc.forward(to_dev(xs))
     torch.cuda.synchronize()
     got = y.float().cpu().numpy()
     assert got.shape == (16, 375, 2048) and np.isfinite(got).all()
-    for b, wi in ((0, 0), (7, 3), (15, 2)):
-        res, _ = oracle_windows(xs[b], Wt, O.FULL, [wi])
-        tok, yref, _ = res[0]
-        check_bf16(got[b, tok:tok + yref.shape[0]], yref, f"clip {b} window {wi}")
     # determinism
     y2 = enc.forward(to_dev(xs))
     assert torch.equal(y, y2)
-    # the 6000-token call runs as two concurrent 3000-token passes; a clip's rows equal its own
-    # single-clip encoding bit for bit, in either half
-    for b in (0, 8, 15):
-        assert torch.equal(y[b], enc.forward(to_dev(xs[b:b + 1]))[0])
+    # the 6000-token call runs as two concurrent 3000-token passes; every clip's rows equal its
+    # own single-clip encoding bit for bit, in either half
+    for b in range(16):
+        assert torch.equal(y[b], enc.forward(to_dev(xs[b:b + 1]))[0]), b
+    # all 64 windows (48 of 800 frames, 16 of 600) against the oracle
+    worst = (1.0, 0.0)
+    for b in range(16):
+        res, _ = oracle_windows(xs[b], Wt, O.FULL, range(4))
+        for wi, (tok, yref, _) in enumerate(res):
+            cos, rel = frame_metrics(got[b, tok:tok + yref.shape[0]], yref)
+            assert cos >= 0.999 and rel <= 2e-2, (b, wi, cos, rel)
+            worst = (min(worst[0], cos), max(worst[1], rel))
+        log(f"clip {b}: 4 windows checked; worst so far cos {worst[0]:.6f} rel {worst[1]:.3e}")
 
 
 def test_full_batch_above_one_pass(full):
@@ -649,3 +659,93 @@ def test_full_c4_hour_stream(full):
         res, _ = oracle_windows(x, Wt, O.FULL, [wi])
         tok, yref, _ = res[0]
         check_bf16(got[tok:tok + yref.shape[0]], yref, f"hour window {wi}")
+
+
+@pytest.mark.parametrize("n_clips,seconds,n_oracle", [(100, 2, 100), (200, 5, 24)])
+def test_full_many_short_clips(full, n_clips, seconds, n_oracle):
+    """Many clips per call (the "SILVERTHRONE/Ossicle-4B" card's "Many clips in one question"):
+    the pass plan keeps every operand within what the kernels address, every clip's rows equal
+    its own single-clip encoding bit for bit, and windows are checked against the oracle: every
+    clip of the 2 s call; for the 5 s call the first and last clip of every pass plus clips
+    spread over the call."""
+    enc, Wt = full
+    n = seconds * 16000
+    xs = np.stack([S.mixed_clip(2000 + i, n) for i in range(n_clips)])
+    passes = B.encoder_plan_passes(B.FULL, [n] * n_clips)
+    log(f"{n_clips} x {seconds} s: passes (windows, tokens, act1 rows) "
+        f"{[(int(p[1]), int(p[3]), int(p[4])) for p in passes]}")
+    y = enc.forward(to_dev(xs))
+    torch.cuda.synchronize()
+    F = O.n_output_frames(n, 100)
+    assert y.shape == (n_clips, F, 2048)
+    for b in range(n_clips):
+        assert torch.equal(y[b], enc.forward(to_dev(xs[b:b + 1]))[0]), b
+    pick = set(np.linspace(0, n_clips - 1, n_oracle).round().astype(int).tolist())
+    for p in passes:  # one window per clip here: window index = clip index
+        pick.update([int(p[0]), int(p[0] + p[1] - 1)])
+    got = y.float().cpu().numpy()
+    worst = (1.0, 0.0)
+    for b in sorted(pick):
+        res, _ = oracle_windows(xs[b], Wt, O.FULL, [0])
+        tok, yref, _ = res[0]
+        cos, rel = frame_metrics(got[b, tok:tok + yref.shape[0]], yref)
+        assert cos >= 0.999 and rel <= 2e-2, (b, cos, rel)
+        worst = (min(worst[0], cos), max(worst[1], rel))
+    log(f"{len(pick)} clips against the oracle: min cos {worst[0]:.6f} max rel-L2 {worst[1]:.3e}")
+
+
+def test_full_long_mode_ends_mid_window(full):
+    """A 150.37 s recording: two whole 64 s pieces and a partial third piece whose last window
+    has 637 frames (80 tokens).  One and two pieces per pass equal the whole-clip path bit for
+    bit ("SILVERTHRONE/Ossicle-4B" card, "Long Audio"), and the partial window matches the
+    oracle."""
+    enc, Wt = full
+    x = S.segment_stream(210, 150.37)
+    n = x.shape[0]
+    assert O.n_mel_frames(n) == 15037
+    pcm = to_dev(x)
+    whole = enc.forward(pcm[None])[0]
+    for ppp in (1, 2):
+        assert torch.equal(enc.forward_long(pcm, pieces_per_pass=ppp), whole), ppp
+    got = whole.float().cpu().numpy()
+    assert got.shape == (1880, 2048)
+    res, plan = oracle_windows(x, Wt, O.FULL, [17, 18])
+    assert plan[18]["L0"] == 637 and plan[18]["L3"] == 80
+    for tok, yref, _ in res:
+        check_bf16(got[tok:tok + yref.shape[0]], yref, f"150.37 s stream, tokens from {tok}")
+
+
+def test_forward_reports_a_failed_allocation(monkeypatch):
+    """A workspace allocation that fails (forced with ENCODER_FAIL_ALLOC) returns
+    ENC_E_OUT_OF_MEMORY; the handle keeps working once allocations succeed again, and its
+    memory statistics stay consistent."""
+    enc = B.Encoder(S.make_weights(B.TINY, seed=0), B.TINY)
+    x = to_dev(S.three_sines()[None])
+    y0 = enc.forward(x)
+    torch.cuda.synchronize()
+    w0, ws0 = enc.memory_stats()
+    big = to_dev(S.mixed_batch([1, 2, 3, 4], 480000))
+    monkeypatch.setenv("ENCODER_FAIL_ALLOC", "1")
+    with pytest.raises(B.EncoderError) as ei:
+        enc.forward(big)
+    assert ei.value.status == B.ENC_E_OUT_OF_MEMORY
+    w1, ws1 = enc.memory_stats()
+    assert w1 == w0 and ws1 == ws0
+    monkeypatch.delenv("ENCODER_FAIL_ALLOC")
+    assert torch.equal(enc.forward(x), y0)
+    yb = enc.forward(big)
+    torch.cuda.synchronize()
+    assert torch.equal(yb[1], enc.forward(big[1:2])[0])
+    assert enc.memory_stats()[1] > ws0
+    enc.close()
+
+
+def test_forward_rejects_batches_above_65535(tiny):
+    enc, _ = tiny
+    pcm = torch.zeros((65536, 201), dtype=torch.float32, device=DEV)
+    out = torch.full((65536, 1, 512), 5.0, dtype=torch.float32, device=DEV)
+    with pytest.raises(B.EncoderError, match="65535") as ei:
+        enc.forward(pcm, out=out)
+    assert ei.value.status == B.ENC_E_INVALID_ARG
+    torch.cuda.synchronize()
+    assert bool((out == 5.0).all())  # nothing was enqueued

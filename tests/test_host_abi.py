@@ -225,3 +225,45 @@ def test_conv_tap_from_float_reciprocal_is_exact():
         inv = np.float32(1.0) / np.float32(C)
         tap = ((k.astype(np.float32) + np.float32(0.5)) * inv).astype(np.int64)
         assert np.array_equal(tap, k // C), C
+
+
+def test_kernel_gelu_is_the_identity_from_16_up():
+    """The conv index probes of the GPU suite (bias 16, integer inputs) rely on the device GELU
+    returning x unchanged for x >= 16.  The formula of csrc/ae_internal.h, evaluated in float32
+    as written (the reciprocal correctly rounded or flushed to zero alike), returns x exactly on
+    every integer 16..1024 and on every float32 value of [16, 32) with a bf16 pattern."""
+    src = open(os.path.join(os.path.dirname(HEADER), "..", "audio_encoder_amd", "csrc",
+                            "ae_internal.h")).read()
+    body = src[src.index("inline float gelu_erf"):src.index("inline float silu")]
+    c = [np.float32(float(v)) for v in re.findall(r"([0-9]\.[0-9]+e[+-][0-9]+)f", body)]
+    assert len(c) == 7
+    f32 = np.float32
+    ints = np.arange(16, 1025, dtype=f32)
+    bf = (np.arange(0x4180, 0x4200, dtype=np.uint32) << 16).view(f32)  # [16, 32) in bf16 steps
+    for x in (ints, bf):
+        t = np.abs(x)
+        p = f32(np.float64(t) * c[0] + c[1])
+        for ci in c[2:]:
+            p = (np.float64(t) * p + ci).astype(f32)
+        with np.errstate(over="ignore", divide="ignore"):  # the 16th power overflows to inf
+            for _ in range(4):
+                p = (p * p).astype(f32)
+            r = (f32(1) / p).astype(f32)
+        for rr in (r, np.where(np.abs(r) < np.finfo(f32).tiny, f32(0), r)):  # with denormals flushed
+            g = (np.maximum(x, 0).astype(np.float64) - np.float64(t) * rr).astype(f32)  # one fma
+            assert np.array_equal(g, x)
+
+
+def test_create_reports_a_failed_allocation(monkeypatch):
+    """encoder_create with allocations refused (ENCODER_FAIL_ALLOC) returns ENC_E_OUT_OF_MEMORY
+    before touching the GPU and leaves the handle unset."""
+    import ctypes
+    c = B.make_cfg(B.TINY)
+    w = np.zeros(S.weight_count(B.TINY), dtype=np.float32)
+    h = ctypes.c_void_p()
+    monkeypatch.setenv("ENCODER_FAIL_ALLOC", "1")
+    st = B.lib().encoder_create(w.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), w.size,
+                                ctypes.byref(c), ctypes.byref(h))
+    assert st == B.ENC_E_OUT_OF_MEMORY and h.value is None
+    assert b"ENCODER_FAIL_ALLOC" in B.lib().encoder_last_error()
+

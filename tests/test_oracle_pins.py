@@ -63,6 +63,27 @@ def test_bf16_rounding_of_blob_matches_torch():
     assert np.array_equal(S.round_to_bf16(x), ref)
 
 
+def test_oracle_bf16_rounding_matches_torch():
+    """oracle.bf16 (fp32 -> nearest bf16, ties to even) against torch's float32 -> bfloat16
+    conversion, on random values over many binades, exact ties in both directions, values one
+    ulp either side of a tie, signed zeros, subnormals and the largest finite values."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-140, 120, 200000))).astype(np.float32)
+    base = rng.integers(0, 2 ** 31, 20000, dtype=np.uint64).astype(np.uint32) & np.uint32(0x7F7F0000)
+    ties = base | np.uint32(0x8000)  # exactly halfway between two bf16 values
+    near = np.concatenate([ties - np.uint32(1), ties + np.uint32(1)])
+    special = np.array([0.0, -0.0, 1e-45, -1e-45, 1e-40, 3.3895e38, -3.3895e38, 1.0, -1.0],
+                       np.float32)
+    for v in (x, ties.view(np.float32), (ties | np.uint32(0x80000000)).view(np.float32),
+              near.view(np.float32), special):
+        ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
+        got = O.bf16(v)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # ties go to the even neighbour: 1 + 2^-8 -> 1, 1 + 3 * 2^-8 -> 1 + 2^-6
+    assert O.bf16(np.float32(1 + 2 ** -8)) == 1.0
+    assert O.bf16(np.float32(1 + 3 * 2 ** -8)) == np.float32(1 + 2 ** -6)
+
+
 # --------------------------------------------------------------------------------------------
 # O1 framing, frame counts, 12.5 Hz
 # --------------------------------------------------------------------------------------------
