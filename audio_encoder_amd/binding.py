@@ -94,6 +94,7 @@ _SIGS = {
     "encoder_splice": [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_int64, c_int32, c_void_p,
                        c_void_p],
     "encoder_log_mel": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
+    "encoder_log_mel_noalloc": [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p],
     "encoder_debug_stage": [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p,
                             c_int64, c_void_p],
     "encoder_timing_enable": [c_void_p, c_int32],
@@ -320,6 +321,16 @@ class Encoder:
         B, N = pcm.shape
         mel = torch.empty((B, N // 160, 128), dtype=torch.float32, device=pcm.device)
         _check(lib().encoder_log_mel(self._h, _ptr(pcm), N, B, _ptr(mel), _stream()))
+        return mel
+
+    def log_mel_noalloc(self, pcm, mel=None):
+        """encoder_log_mel_noalloc: the log-mel with no allocation in the library (batch <= 4096);
+        `mel` float32 [batch, n_samples/160, 128] may be passed in."""
+        import torch
+        B_, N = pcm.shape
+        if mel is None:
+            mel = torch.empty((B_, N // 160, 128), dtype=torch.float32, device=pcm.device)
+        _check(lib().encoder_log_mel_noalloc(self._h, _ptr(pcm), N, B_, _ptr(mel), _stream()))
         return mel
 
     def debug_stage(self, pcm, stage: int, layer: int = 0):

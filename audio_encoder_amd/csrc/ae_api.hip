@@ -16,12 +16,22 @@
 #include <cmath>
 #include <cstring>
 #include <string>
+#include <mutex>
 #include <thread>
 #include <vector>
 
 #include "ae_internal.h"
 
 namespace ae {
+
+// Scratch of the allocation-free entry point (encoder_log_mel_noalloc): clip spans and the
+// per-clip maximum keys of up to kScratchClips clips.  One copy per GPU, held until the
+// process ends; its device address is looked up once per device (scratch_on_device) and
+// passed to the kernels; host code never uses the array's name as an address.
+constexpr int32_t kScratchClips = 4096;
+constexpr int64_t kScratchSpanBytes = ((int64_t)kScratchClips * (int64_t)sizeof(ClipSpan) + 255) & ~int64_t(255);
+constexpr int64_t kScratchBytes = kScratchSpanBytes + (int64_t)kScratchClips * 4;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 static thread_local std::string g_err;
 void set_error(const std::string& msg) { g_err = msg; }
@@ -464,6 +474,9 @@ struct encoder {
   // that must grow waits for it before the old one is freed (one call is in flight per handle)
   hipEvent_t call_done = nullptr;
   bool call_pending = false;
+  // the allocation-free entry point's scratch on this handle's device (null: unavailable)
+  void* scratch = nullptr;
+  hipError_t scratch_err = hipSuccess;
   Buf rs_taps;            // polyphase table of the last input-conditioning rate
   int32_t rs_rate = 0;
   int64_t ws_bytes = 0, ws_peak = 0;
@@ -945,6 +958,32 @@ void free_all(encoder* e) {
 
 }  // namespace
 
+// Device address of `scratch` on the current device, looked up once per device (the first
+// lookup happens in encoder_create, with the handle's device current).  Null if the lookup
+// failed (the error is in hip_err).
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+static hipError_t g_scratch_err[kMaxDevices] = {};
+static bool g_scratch_done[kMaxDevices] = {};
+
+static void* scratch_on_device(int dev, hipError_t* hip_err) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    *hip_err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_done[dev]) {
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = err == hipSuccess ? p : nullptr;
+    g_scratch_err[dev] = err;
+    g_scratch_done[dev] = true;
+  }
+  *hip_err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
 // ==========================================================================================
 // C ABI
 // ==========================================================================================
@@ -1269,6 +1308,7 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
     free_all(e);
     return r;
   }
+  e->scratch = scratch_on_device(dev, &e->scratch_err);
   e->wbytes = woff * (int64_t)es;
   e->fbytes = foff * 4;
   e->qbytes = qoff;
@@ -1458,6 +1498,28 @@ encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, 
   // the workspace is read until here
   e->call_pending = hipEventRecord(e->call_done, s) == hipSuccess;
   return st;
+}
+
+encoder_status encoder_log_mel_noalloc(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+                                       float* mel, void* stream) {
+  encoder_status st = check_forward_args(e, pcm, n_samples, batch, mel);
+  if (st) return st;
+  if (batch > kScratchClips)
+    return invalid("encoder_log_mel_noalloc takes at most " + std::to_string(kScratchClips) +
+                   " clips (its scratch holds that many); use encoder_log_mel");
+  if (!e->scratch) return hip_fail(e->scratch_err, "hipGetSymbolAddress(scratch)");
+  AE_HIP(hipSetDevice(e->device));
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t T = n_samples / e->cfg.hop;
+  ClipSpan* spans = reinterpret_cast<ClipSpan*>(e->scratch);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(e->scratch) + kScratchSpanBytes);
+  // spans written by a kernel and keys cleared by a kernel (no host staging, no memset); the
+  // raw log10 mel goes straight into the output and is normalised there
+  AE_HIP(launch_batch_spans(spans, batch, n_samples, s));
+  AE_HIP(launch_clear_u32(keys, batch, s));
+  AE_HIP(launch_log_mel(pcm, spans, batch, T, e->mel, mel, keys, s));
+  AE_HIP(launch_mel_normalize(mel, keys, T, batch, mel, s));
+  return ENC_OK;
 }
 
 encoder_status encoder_debug_stage(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,

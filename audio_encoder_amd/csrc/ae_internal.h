@@ -133,6 +133,8 @@ struct MelTables {
 hipError_t launch_log_mel(const float* pcm, const ClipSpan* clips, int32_t nclip, int64_t t_max,
                           const MelTables& t, float* mel, uint32_t* max_key, hipStream_t s);
 hipError_t launch_clear_u32(uint32_t* p, int64_t n, hipStream_t s);
+// the spans of a [batch, n] call written on the device (no host staging)
+hipError_t launch_batch_spans(ClipSpan* spans, int32_t batch, int64_t n, hipStream_t s);
 // normalised mel from raw + max keys (in place or out of place)
 hipError_t launch_mel_normalize(const float* raw, const uint32_t* max_key, int64_t T,
                                 int32_t nclip, float* out, hipStream_t s);

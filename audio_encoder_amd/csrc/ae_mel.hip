@@ -173,9 +173,10 @@ __device__ inline float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// (max(L, max - 8) + 4) / 4
-__global__ void mel_normalize_kernel(const float* __restrict__ raw, const uint32_t* __restrict__ mk,
-                                     int64_t T, int32_t nclip, float* __restrict__ out) {
+// (max(L, max - 8) + 4) / 4; raw and out may be the same buffer (each element is read, then
+// written, by one thread), so neither is declared restrict
+__global__ void mel_normalize_kernel(const float* raw, const uint32_t* __restrict__ mk,
+                                     int64_t T, int32_t nclip, float* out) {
   const int64_t total = (int64_t)nclip * T * NM;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -194,6 +195,18 @@ hipError_t launch_log_mel(const float* pcm, const ClipSpan* clips, int32_t nclip
   dim3 grid((unsigned)((t_max + FB - 1) / FB), (unsigned)nclip);
   hipLaunchKernelGGL(log_mel_kernel, grid, dim3(256), 0, s, pcm, clips, t.twiddle, t.window,
                      t.fb_start, t.fb_len, t.fb_w, mel, max_key);
+  return hipGetLastError();
+}
+
+// spans of a [batch, n] call: clip b at samples b * n, frames b * (n / hop)
+__global__ void batch_spans_kernel(ClipSpan* spans, int32_t batch, int64_t n) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) spans[b] = ClipSpan{(int64_t)b * n, n, (int64_t)b * (n / HOP)};
+}
+
+hipError_t launch_batch_spans(ClipSpan* spans, int32_t batch, int64_t n, hipStream_t s) {
+  if (batch < 1) return hipSuccess;
+  hipLaunchKernelGGL(batch_spans_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, s, spans, batch, n);
   return hipGetLastError();
 }
 

@@ -239,6 +239,17 @@ ENC_API encoder_status encoder_condition_audio(encoder* e, const float* in, int6
 ENC_API encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
                                float* mel, void* stream);
 
+/* encoder_log_mel for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops, harnesses that forbid hipMalloc): same arguments, same result, and no
+ * allocation of any kind in the call.  Its per-call scratch (clip spans and per-clip maximum
+ * keys) lives in a fixed 128 KiB array of device memory per GPU, held until the process ends,
+ * so batch is at most 4096 (larger calls return ENC_E_INVALID_ARG).  Every call on one GPU
+ * shares that array: calls that overlap on one GPU (from several threads or streams) race and
+ * must be serialised by the caller.  The raw log-mel is written into `mel` and normalised in
+ * place. */
+ENC_API encoder_status encoder_log_mel_noalloc(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
+                                       float* mel, void* stream);
+
 /* Stage-wise check point: runs the whole-clip path up to `stage` and writes that stage's output
  * as float32 to dst (dst_elems values available).  Single pass only (batch*F <=
  * max_tokens_per_pass).  Stages and layouts (nw = windows, ntok = batch*F):

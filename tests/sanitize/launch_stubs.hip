@@ -16,6 +16,7 @@ hipError_t refused(const char* what) {
 hipError_t launch_log_mel(const float*, const ClipSpan*, int32_t, int64_t, const MelTables&, float*, uint32_t*,
                           hipStream_t) { return refused("log_mel"); }
 hipError_t launch_clear_u32(uint32_t*, int64_t, hipStream_t) { return refused("clear_u32"); }
+hipError_t launch_batch_spans(ClipSpan*, int32_t, int64_t, hipStream_t) { return refused("batch_spans"); }
 hipError_t launch_mel_normalize(const float*, const uint32_t*, int64_t, int32_t, float*, hipStream_t) {
   return refused("mel_normalize");
 }

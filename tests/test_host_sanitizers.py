@@ -1,8 +1,8 @@
 """The library's host-only entry points (configuration checks, window and pass plans, the int4
 quantiser, conditioning lengths, create's blob-size rejection) built with AddressSanitizer and
 UndefinedBehaviorSanitizer and run on the CPU by tests/sanitize/host_driver.cpp.  The API source
-is compiled for the host only (it holds no kernels) and linked with launcher stubs that refuse
-any launch; the sanitizers instrument host code only."""
+(which holds no kernels) is linked with launcher stubs that refuse any launch; the sanitizers
+instrument host code only."""
 import os
 import subprocess
 
@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=all"]
-COMMON = ["--offload-host-only", "-O1", "-g", "-std=c++17", "-fno-omit-frame-pointer",
+COMMON = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fno-omit-frame-pointer",
           "-I", os.path.join(ROOT, "include"), "-Wno-unused-result"]
 
 
