@@ -356,8 +356,10 @@ class Encoder:
         _check(lib().encoder_memory_stats(self._h, ctypes.byref(w), ctypes.byref(ws)))
         return w.value, ws.value
 
-    def timing_enable(self, on: bool = True):
-        _check(lib().encoder_timing_enable(self._h, 1 if on else 0))
+    def timing_enable(self, mode: int = 1):
+        """0 off; 1 time each kernel launch, running the passes of an untimed call one after
+        another on one stream; 2 as 1, with a call that fits one pass run as that one pass."""
+        _check(lib().encoder_timing_enable(self._h, int(mode)))
 
     def timing_read(self, reset: bool = True) -> dict:
         ms = (c_double * len(KERNELS))()

@@ -98,9 +98,10 @@ def make_input(workload: str):
     raise ValueError(workload)
 
 
-def measured_traffic(role: str, cfg_note: str = "full-size tower, 16 x 30 s clips"):
-    """HBM bytes per launch of `role` from the committed counter summary, or None when the
-    GEMM source changed since the counters were taken (or no summary exists)."""
+def measured_traffic(role: str, launches_per_step: int):
+    """HBM bytes per launch of `role` from the committed counter summary, or None when the GEMM
+    source changed since the counters were taken, when they were taken on launches of another
+    size, or when no summary exists."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic_full_16x30s.json")
     src = os.path.join(ROOT, "audio_encoder_amd", "csrc", "ae_gemm.hip")
@@ -112,6 +113,8 @@ def measured_traffic(role: str, cfg_note: str = "full-size tower, 16 x 30 s clip
     except OSError:
         return None
     if rec.get("gemm_source_sha256") != sha or role not in rec.get("per_launch", {}):
+        return None
+    if rec.get("launches_per_step", {}).get(role) != launches_per_step:
         return None
     t = rec["per_launch"][role]
     return round(t["fetch_bytes"] + t["write_bytes"])
@@ -252,33 +255,48 @@ def main():
     log(f"{ms:.3f} ms/step, {audio_s / (ms * 1e-3):.0f} audio-s/s, {tflops:.1f} TFLOP/s "
         f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak); wall {t_wall:.2f} s")
 
-    # per-kernel timing on the forward's own stream (a one-element int16 fill first marks where
-    # these steps begin in a profiler's kernel trace)
-    torch.full((1,), 7, dtype=torch.int16, device="cuda")
-    torch.cuda.synchronize()
-    enc.timing_enable(True)
-    enc.timing_read(reset=True)
-    for _ in range(args.roofline_steps):
-        step()
-    tm = enc.timing_read(reset=True)
-    enc.timing_enable(False)
+    # Per-kernel timing on the forward's own stream, in extra steps run kernel by kernel on one
+    # stream.  Mode 1 runs the passes of the timed steps (a 6000-token call: two 3000-token
+    # halves) one after another; mode 2 runs a call that fits one pass as that single pass.  A
+    # one-element int16 fill before each marks where these steps begin in a profiler's kernel
+    # trace.
     R = args.roofline_steps
+
+    def role_times(mode):
+        torch.full((1,), 7, dtype=torch.int16, device="cuda")
+        torch.cuda.synchronize()
+        enc.timing_enable(mode)
+        enc.timing_read(reset=True)
+        for _ in range(R):
+            step()
+        tm = enc.timing_read(reset=True)
+        enc.timing_enable(0)
+        return tm
+
+    def roofline(tm, dom, passes):
+        dom_ms, dom_n = tm[dom]
+        avg_ms = dom_ms / dom_n
+        per_launch = wm["flops"][dom] / (dom_n / R)
+        achieved = per_launch / (avg_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg_ms, 5),
+                "launches_per_step": dom_n // R, "algorithmic_unit": "FLOP per launch",
+                "algorithmic_per_launch": per_launch,
+                "method": "HIP events around each launch on the forward's stream, in extra steps "
+                          f"run kernel by kernel on one stream ({passes})"}
+
+    tm = role_times(1)
     stage_ms = {k: round(v[0] / R, 4) for k, v in tm.items() if v[1]}
     dom = max((k for k in tm if k in wm["flops"]), key=lambda k: tm[k][0])
-    dom_ms, dom_n = tm[dom]
-    avg_ms = dom_ms / dom_n
-    per_launch = wm["flops"][dom] / (dom_n / R)
-    achieved = per_launch / (avg_ms * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "avg_launch_ms": round(avg_ms, 5), "launches_per_step": dom_n // R,
-            "traffic": measured_traffic(dom) if args.workload == "c2" else None,
-            "algorithmic_unit": "FLOP per launch", "algorithmic_per_launch": per_launch,
-            "method": "HIP events around each launch in extra steps run kernel by kernel on one "
-                      "stream, each call as a single pass (the throughput steps may run a large "
-                      "call as two concurrent half passes)"}
+    roof = roofline(tm, dom, "the passes of the timed steps, one after another")
+    roof["traffic"] = measured_traffic(dom, roof["launches_per_step"]) if args.workload == "c2" else None
+    tm2 = role_times(2)
+    roof_single = roofline(tm2, dom, "a call that fits one pass run as that one pass")
     for k, v in stage_ms.items():
         log(f"  {k:10s} {v:8.3f} ms/step")
+    log(f"dominant kernel {dom}: {roof['frac']:.4f} of peak in the timed passes, "
+        f"{roof_single['frac']:.4f} as one pass")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -309,6 +327,7 @@ def main():
         "tflops": round(tflops, 2),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roof,
+        "roofline_single_pass": roof_single,
         "cpu_baseline": cpu,
         "stage_ms": stage_ms,
         # device memory: the library's weights and workspace high-water mark, and the drop in

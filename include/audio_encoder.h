@@ -270,9 +270,13 @@ enum {
   ENC_K_ATTN, ENC_K_OPROJ, ENC_K_FFN1, ENC_K_FFN2, ENC_K_PROJ1, ENC_K_PROJ2, ENC_K_GATE_UP,
   ENC_K_DOWN, ENC_K_OTHER, ENC_K_COUNT
 };
-/* When enabled, forward calls bracket each kernel launch with events.  encoder_timing_read
- * synchronises on the recorded events and returns, per ENC_K_* id, the summed milliseconds and
- * the launch count since the last reset (arrays of ENC_K_COUNT entries). */
+/* mode 0: off.  mode 1: forward calls bracket each kernel launch with events on the call's
+ * stream and run their passes one after another there (the passes of an untimed call: a call of
+ * 4000 tokens or more that fits one pass still runs as its two halves).  mode 2: as mode 1, but
+ * a call that fits one pass runs as that single pass.  Other modes return ENC_E_INVALID_ARG.
+ * encoder_timing_read synchronises on the recorded events and returns, per ENC_K_* id, the
+ * summed milliseconds and the launch count since the last reset (arrays of ENC_K_COUNT
+ * entries). */
 ENC_API encoder_status encoder_timing_enable(encoder* e, int32_t enable);
 ENC_API encoder_status encoder_timing_read(encoder* e, double* ms, int64_t* launches, int32_t reset);
 
