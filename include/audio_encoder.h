@@ -111,7 +111,10 @@ ENC_API encoder_status encoder_validate_cfg(const encoder_cfg* cfg);
 ENC_API encoder_status encoder_weight_count(const encoder_cfg* cfg, int64_t* n_floats);
 
 /* Embeddings per clip: the sum over windows of the 3 x stride-2 ceil chain of each window's
- * frame count = ceil((n_samples/160)/8) (12.5 Hz).  n_samples must exceed n_fft/2. */
+ * frame count = ceil((n_samples/160)/8): 12.5 embeddings per second of audio
+ * ("SILVERTHRONE/Ossicle-4B" card, "Model Overview"; frame count from the
+ * "cstr/MOSS-Transcribe-preview-2B-GGUF" card, "Non-obvious gotchas" item 2).  n_samples must
+ * exceed n_fft/2, else ENC_E_INVALID_ARG. */
 ENC_API encoder_status encoder_output_frames(const encoder_cfg* cfg, int64_t n_samples, int64_t* n_frames);
 
 /* The window plan of a [batch, n_samples] call: for each window, 7 int32 values
@@ -165,7 +168,9 @@ ENC_API encoder_status encoder_memory_stats(const encoder* e, int64_t* weight_by
 
 /* ---- forward passes ------------------------------------------------------------------------ */
 
-/* Whole-clip path.  pcm: device float32 [batch, n_samples] (independent equal-length clips; each
+/* Whole-clip path: the forward pass of the tower ("cstr/MOSS-Transcribe-preview-2B-GGUF" card,
+ * "Architecture": 16 kHz mono PCM in, 12.5 Hz embeddings of width d_out out, in time order).
+ * pcm: device float32 [batch, n_samples] (independent equal-length clips; each
  * is normalised by its own log-mel maximum).  out: device [batch, F, d_out] with F from
  * encoder_output_frames, bf16 for ENC_BF16 and float32 for ENC_F32.  n_samples > n_fft/2,
  * batch >= 1.  Inputs above max_tokens_per_pass run in several window-aligned passes.  Passes of
@@ -235,7 +240,10 @@ ENC_API encoder_status encoder_conditioned_length(int64_t n_in, int32_t sample_r
 ENC_API encoder_status encoder_condition_audio(encoder* e, const float* in, int64_t n_in, int32_t channels,
                                        int32_t sample_rate, float* out, void* stream);
 
-/* Normalised log-mel only: mel device float32 [batch, n_samples/160, 128]. */
+/* Normalised log-mel only ("cstr/MOSS-Transcribe-preview-2B-GGUF" card, "Architecture" row
+ * "Audio": 128 Whisper-style mel bins, n_fft 400, hop 160; "Non-obvious gotchas" item 2):
+ * mel device float32 [batch, n_samples/160, 128], each clip normalised by its own maximum.
+ * Same argument checks as encoder_forward; the workspace grows on demand. */
 ENC_API encoder_status encoder_log_mel(encoder* e, const float* pcm, int64_t n_samples, int32_t batch,
                                float* mel, void* stream);
 
@@ -294,9 +302,6 @@ ENC_API encoder_status encoder_op_linear(const void* A, const void* W, const flo
                                  int64_t M, int32_t N, int32_t K, int32_t epi, int32_t dtype,
                                  void* stream);
 
-/* Windowed attention.  qkv device [ntok, 3*n_heads*64] (q | k | v, head h = columns 64h..64h+63
- * of each part), windows device int32 [n_windows, 2] = {first token, length <= 128}.  out device
- * [ntok, n_heads*64].  Softmax in float32. */
 /* int4 weight-only quantisation of a float32 [N, K] weight (host; K % 128 == 0): per row and
  * group of 128 inputs, scale s = bf16(max |w| / 7) and q = clamp(rint(w / s), -8, 7) (0 for an
  * all-zero group); q packed two per byte [N, K/2] (even k in the low nibble, two's complement),
@@ -312,6 +317,12 @@ ENC_API encoder_status encoder_op_linear_int4(const void* A, const uint8_t* q, c
                                       const float* bias, void* C, int64_t M, int32_t N, int32_t K,
                                       int32_t epi, void* stream);
 
+/* Windowed (block-diagonal) self-attention ("cstr/MOSS-Transcribe-preview-2B-GGUF" card,
+ * "Architecture", row "Audio encoder": each token attends to the tokens of its own window only).
+ * qkv device [ntok, 3*n_heads*64] (q | k | v, head h = columns 64h..64h+63 of each part), windows
+ * device int32 [n_windows, 2] = {first token, length 1..128} (copied to the host and checked
+ * before the launch).  out device [ntok, n_heads*64]; rows outside every window are not
+ * written.  Scores scaled by 1/8, softmax in float32.  dtype ENC_BF16 or ENC_F32. */
 ENC_API encoder_status encoder_op_attention(const void* qkv, const int32_t* windows, int32_t n_windows,
                                     int32_t n_heads, int64_t ntok, void* out, int32_t dtype,
                                     void* stream);
