@@ -3,11 +3,12 @@
 //   C[m, n] = epilogue( sum_k A[m, k] * B[n, k] )
 //
 // A is an activation (row-major, K contiguous) or, for the 3x3 stride-2 convolutions, the
-// im2col view of a channels-last activation generated on the fly by the loader (K ordered as
-// tap-major, channel-minor, so each 8-element chunk is one contiguous 16-byte read of one input
-// position; out-of-image taps and positions past a window's valid length read as zero).  B is a
-// weight matrix [N, K] (PyTorch Linear layout; conv weights permuted to [out][tap][in] at pack
-// time).  Epilogues fuse the bias, exact GELU, the fp32 residual update, the sinusoidal
+// im2col view of a channels-last activation generated on the fly by the loader (logical K
+// ordered as tap-major, channel-minor, so each 8-element chunk is one contiguous 16-byte read of
+// one input position; out-of-image taps and positions past a window's valid length read as
+// zero; the staged kernels walk K as 32-channel blocks, then taps, then channels, see AConv).
+// B is a weight matrix [N, K] (PyTorch Linear layout; conv weights permuted to [out][tap][in]
+// at pack time).  Epilogues fuse the bias, exact GELU, the fp32 residual update, the sinusoidal
 // positions and the SwiGLU gate into the store.
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950 with fp32 accumulators.  Tiles move from global
@@ -43,6 +44,9 @@ struct ALinear {
   __device__ bool tile_live(int64_t m0, int) const { return m0 < M; }
   __device__ Row row(int64_t r) const { return Row{r < M ? A + r * lda : nullptr}; }
   __device__ KC kc(int k) const { return KC{k, k < K}; }
+  // the staged kernels' K order is the natural one (step base eb, lane offset off)
+  __device__ KC kc_step(int eb, int off) const { return kc(eb + off); }
+  __device__ int k_logical(int eb, int off) const { return eb + off; }
   __device__ const T* ptr(const Row& x, const KC& c) const {
     return (x.p && c.ok) ? x.p + c.k : nullptr;
   }
@@ -114,6 +118,25 @@ struct AConv {
     c.bit = 1 << tap;
     c.toff = (db * Fin + da) * C + ci;
     return c;
+  }
+  // K order of the staged kernels: blocks of 32 input channels outermost, then the nine taps,
+  // then the channels of the block (C % 32 == 0), so that the nine taps reading one input
+  // neighbourhood run in consecutive K steps and their re-reads of each input position hit in
+  // L2.  With 32-wide K steps a step is one (block, tap) pair: the step base eb (a multiple of
+  // 32, wave-uniform) selects it, and the lane offset off < 32 the channel within the block.
+  // Step element eb + off is logical index tap * C + channel of the packed weights.
+  __device__ KC kc_step(int eb, int off) const {
+    const int b = eb / 288, tap = (eb - b * 288) >> 5;
+    const int da = tap / 3, db = tap - 3 * (tap / 3);
+    KC c;
+    c.ok = eb < K;
+    c.bit = 1 << tap;
+    c.toff = (db * Fin + da) * C + (b << 5) + off;
+    return c;
+  }
+  __device__ int k_logical(int eb, int off) const {
+    const int b = eb / 288, tap = (eb - b * 288) >> 5;
+    return tap * C + (b << 5) + off;
   }
   __device__ const T* ptr(const Row& x, const KC& c) const {
     return (c.ok && (x.mask & c.bit)) ? in + (x.off + c.toff) : nullptr;
@@ -641,10 +664,11 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
   const int k0 = __builtin_amdgcn_readfirstlane((int)blockIdx.y * k_span);
   const int kend = K < k0 + k_span ? K : k0 + k_span;
   auto dma = [&](int kt, bf16_t* st) {
+    const int eb = __builtin_amdgcn_readfirstlane(k0 + kt * BK);
 #pragma unroll
     for (int j = 0; j < ADMA; ++j) {
       const int k = k0 + kt * BK + achunk[j] * 8;
-      auto kc = as.kc(k);
+      auto kc = as.kc_step(eb, achunk[j] * 8);
       kc.ok = kc.ok && k < kend;
       const uint32_t off = as.boff(arow[j], kc);
       bf16_t* dst = st + (wv * ADMA + j) * ROWS_PER_DMA * BK;
@@ -654,7 +678,9 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
 #pragma unroll
     for (int j = 0; j < BDMA; ++j) {
       const int k = k0 + kt * BK + bchunk[j] * 8;
-      const uint32_t off = (k < kend && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)k * 2u : 0x80000000u;
+      const uint32_t off =
+          (k < kend && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)as.k_logical(eb, bchunk[j] * 8) * 2u
+                                                : 0x80000000u;
       bf16_t* dst = st + BM * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
                                                (int)off, 0, 0, 0);
@@ -737,7 +763,12 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  for (int kt = 0; kt < nk; kt += NST) {
+  // Every group of NST steps but the last runs branch-free.  The last group always holds a real
+  // tile first; its later steps run only while their tiles lie within K (the steps it skips
+  // would only multiply the zero tiles).  Its exits are forward branches to the end, so the
+  // waits of the loop and of the steps before each exit stay exact.
+  const int nreal = (kend - k0 + BK - 1) / BK;
+  for (int kt = 0; kt < nk - NST; kt += NST) {
     step(kt, std::integral_constant<int, 0>());
     step(kt + 1, std::integral_constant<int, 1>());
     if constexpr (NST > 2) step(kt + 2, std::integral_constant<int, 2>());
@@ -746,6 +777,17 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
     if constexpr (NST > 5) step(kt + 5, std::integral_constant<int, 5>());
     if constexpr (NST > 6) step(kt + 6, std::integral_constant<int, 6>());
     if constexpr (NST > 7) step(kt + 7, std::integral_constant<int, 7>());
+  }
+  {
+    const int kt = nk - NST;
+    auto tail = [&](auto self, auto sc) -> void {
+      constexpr int t = decltype(sc)::value;
+      step(kt + t, sc);
+      if constexpr (t + 1 < NST) {
+        if (kt + t + 1 < nreal) self(self, std::integral_constant<int, t + 1>());
+      }
+    };
+    tail(tail, std::integral_constant<int, 0>());
   }
   wait_vm_lds0<0>();  // the trailing zero-fill DMAs land before the stages are reused
   __syncthreads();
@@ -980,13 +1022,27 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilvq_kernel(AS as, int3
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  for (int kt = 0; kt < nk; kt += NST) {
+  // all groups but the last branch-free; the last stops after its last tile within K (as in
+  // gemm_ilv_kernel)
+  const int nreal = (K + BK - 1) / BK;
+  for (int kt = 0; kt < nk - NST; kt += NST) {
     step(kt, std::integral_constant<int, 0>());
     step(kt + 1, std::integral_constant<int, 1>());
     if constexpr (NST > 2) step(kt + 2, std::integral_constant<int, 2>());
     if constexpr (NST > 3) step(kt + 3, std::integral_constant<int, 3>());
     if constexpr (NST > 4) step(kt + 4, std::integral_constant<int, 4>());
     if constexpr (NST > 5) step(kt + 5, std::integral_constant<int, 5>());
+  }
+  {
+    const int kt = nk - NST;
+    auto tail = [&](auto self, auto sc) -> void {
+      constexpr int t = decltype(sc)::value;
+      step(kt + t, sc);
+      if constexpr (t + 1 < NST) {
+        if (kt + t + 1 < nreal) self(self, std::integral_constant<int, t + 1>());
+      }
+    };
+    tail(tail, std::integral_constant<int, 0>());
   }
   wait_vm_lds0<0>();  // the trailing zero-fill loads land before the stages are reused
   __syncthreads();
@@ -1371,6 +1427,7 @@ constexpr int kConvTStages = 6, kConvNStages = 8;
 template <typename T, class TL, int NST, int LEVEL, int TAG>
 hipError_t conv_run(const AConv<T>& as, const T* wpk, int32_t C, const PassGeom& g, int rows_per_win,
                     int Fout, int Lout_max, int64_t m_rows, const EpiP& ep, hipStream_t s) {
+  static_assert(TL::BK == 32, "the conv K order takes one (channel block, tap) pair per K step");
   // a wave covers TL::WTM rows of the tile
   if (rows_per_win >= TL::WTM) {
     OConv<LEVEL, true> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
