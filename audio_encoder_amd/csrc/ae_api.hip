@@ -431,6 +431,7 @@ struct WMat {
   void* w = nullptr;
   const uint8_t* q = nullptr;
   const bf16_t* s = nullptr;
+  int32_t blk = 0;  // w in the K-blocked layout with this K block (0: plain [N][K])
 };
 
 struct LayerW {
@@ -451,7 +452,9 @@ struct encoder {
   float* fdev = nullptr;  // float32 parameters and tables
   int64_t wbytes = 0, fbytes = 0, qbytes = 0;
   float *conv1_w, *conv1_b, *conv2_b, *conv3_b;
-  void *conv2_w, *conv3_w, *conv_out_w;
+  void *conv2_w, *conv3_w;
+  int32_t conv_blk = 0;  // K block of conv2_w / conv3_w (0: plain [C][9][C])
+  WMat conv_out_w;
   std::vector<LayerW> layers;
   float *lnp_g, *lnp_b, *proj1_b, *proj2_b;
   WMat proj1_w, proj2_w, gateup_w, down_w;
@@ -659,7 +662,7 @@ encoder_status launch_linear_t(encoder* e, encoder::Lane& ln, int kid, const voi
                                int epi, hipStream_t s, const float* pe = nullptr,
                                const int32_t* tok_pos = nullptr) {
   LinearArgs a{A, lda, Wt.w, bias, C, ldc, M, N, K, pe, tok_pos, Wt.q, Wt.s,
-               (float*)ln.splitk.p, ln.splitk.bytes};
+               (float*)ln.splitk.p, ln.splitk.bytes, Wt.blk};
   LAUNCH(kid, launch_linear<T>(a, epi, kid, s));
   return ENC_OK;
 }
@@ -705,12 +708,12 @@ encoder_status run_pass(encoder* e, encoder::Lane& ln, const Pass& p, void* out,
   LAUNCH(ENC_K_CONV1, launch_conv1<T>(g, (const float*)e->mel_raw.p, (const uint32_t*)e->max_key.p,
                                       nullptr, e->conv1_w, e->conv1_b, C, act1, s));
   if (stop == ST_CONV1) return ENC_OK;
-  LAUNCH(ENC_K_CONV2, launch_conv_igemm<T>(g, 2, act1, (const T*)e->conv2_w, e->conv2_b, C, act2, s));
+  LAUNCH(ENC_K_CONV2, launch_conv_igemm<T>(g, 2, act1, (const T*)e->conv2_w, e->conv2_b, C, act2, s, e->conv_blk));
   if (stop == ST_CONV2) return ENC_OK;
-  LAUNCH(ENC_K_CONV3, launch_conv_igemm<T>(g, 3, act2, (const T*)e->conv3_w, e->conv3_b, C, tokA, s));
+  LAUNCH(ENC_K_CONV3, launch_conv_igemm<T>(g, 3, act2, (const T*)e->conv3_w, e->conv3_b, C, tokA, s, e->conv_blk));
   if (stop == ST_CONV3) return ENC_OK;
   encoder_status st;
-  if ((st = launch_linear_t<T>(e, ln, ENC_K_CONV_OUT, tokA, 16 * C, WMat{e->conv_out_w}, nullptr, resid, d, M,
+  if ((st = launch_linear_t<T>(e, ln, ENC_K_CONV_OUT, tokA, 16 * C, e->conv_out_w, nullptr, resid, d, M,
                                d, 16 * C, EPI_PE, s, e->pe, g.tok_pos)))
     return st;
   if (stop == ST_EMBED) return ENC_OK;
@@ -1294,6 +1297,35 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
     std::memcpy(fh.data() + f_fbl, fl.data(), 128 * 4);
   }
 
+  // bf16 matrices read by the staged kernels go to the K-blocked layout (conv2/conv3 with the
+  // conv tiles' 32-wide K steps, the linear layers with 64); a shape that does not divide into
+  // blocks stays plain
+  auto blockify = [&](int64_t o, int64_t N_, int64_t K_, int BK) -> int32_t {
+    const int64_t R = 512 / BK;
+    if (es != 2 || N_ % R != 0 || K_ % BK != 0) return 0;
+    bf16_t* p = reinterpret_cast<bf16_t*>(wh.data()) + o;
+    std::vector<bf16_t> plain(p, p + N_ * K_);
+    const int64_t kb = K_ / BK;
+    parallel_for(N_ / R, [&](int64_t g0, int64_t g1) {
+      for (int64_t g = g0; g < g1; ++g)
+        for (int64_t r = 0; r < R; ++r)
+          for (int64_t k = 0; k < K_; ++k)
+            p[(g * kb + k / BK) * 512 + r * BK + k % BK] = plain[(g * R + r) * K_ + k];
+    });
+    return BK;
+  };
+  const int32_t b_conv2 = blockify(o_conv2, C, 9 * C, 32), b_conv3 = blockify(o_conv3, C, 9 * C, 32);
+  const int32_t b_co = blockify(o_co, d, 16 * C, 64);
+  std::vector<int32_t> b_qkv, b_o, b_1, b_2;
+  for (int l = 0; l < c.n_layers; ++l) {
+    b_qkv.push_back(q4 ? 0 : blockify(o_qkv[l], 3 * d, d, 64));
+    b_o.push_back(q4 ? 0 : blockify(o_o[l], d, d, 64));
+    b_1.push_back(q4 ? 0 : blockify(o_1[l], F, d, 64));
+    b_2.push_back(q4 ? 0 : blockify(o_2[l], d, F, 64));
+  }
+  const int32_t b_p1 = q4 ? 0 : blockify(o_p1, d, d, 64), b_p2 = q4 ? 0 : blockify(o_p2, O, d, 64);
+  const int32_t b_gu = q4 ? 0 : blockify(o_gu, 2 * A, O, 64), b_dn = q4 ? 0 : blockify(o_dn, O, A, 64);
+
   hipError_t err = hipMalloc(&e->wdev, woff * (int64_t)es);
   if (err == hipSuccess) err = hipMalloc((void**)&e->fdev, foff * 4);
   if (err == hipSuccess && q4) err = hipMalloc((void**)&e->qdev, qoff);
@@ -1313,30 +1345,35 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
   e->fbytes = foff * 4;
   e->qbytes = qoff;
   auto W_ = [&](int64_t o) { return (void*)((uint8_t*)e->wdev + o * (int64_t)es); };
-  auto M_ = [&](int64_t o, const QSlot& qs) {
+  auto M_ = [&](int64_t o, const QSlot& qs, int32_t blk) {
     WMat m;
     if (q4) {
       m.q = e->qdev + qs.q;
       m.s = reinterpret_cast<const bf16_t*>(e->qdev + qs.s);
     } else {
       m.w = W_(o);
+      m.blk = blk;
     }
     return m;
   };
   auto F_ = [&](int64_t o) { return e->fdev + o; };
   e->conv1_w = F_(f_c1w); e->conv1_b = F_(f_c1b); e->conv2_b = F_(f_c2b); e->conv3_b = F_(f_c3b);
-  e->conv2_w = W_(o_conv2); e->conv3_w = W_(o_conv3); e->conv_out_w = W_(o_co);
+  e->conv2_w = W_(o_conv2); e->conv3_w = W_(o_conv3);
+  e->conv_blk = b_conv2;  // conv3 has the same shape, so the same layout
+  (void)b_conv3;
+  e->conv_out_w.w = W_(o_co);
+  e->conv_out_w.blk = b_co;
   for (int l = 0; l < c.n_layers; ++l) {
     LayerW L;
-    L.wqkv = M_(o_qkv[l], q_qkv[l]); L.wo = M_(o_o[l], q_o[l]);
-    L.w1 = M_(o_1[l], q_1[l]); L.w2 = M_(o_2[l], q_2[l]);
+    L.wqkv = M_(o_qkv[l], q_qkv[l], b_qkv[l]); L.wo = M_(o_o[l], q_o[l], b_o[l]);
+    L.w1 = M_(o_1[l], q_1[l], b_1[l]); L.w2 = M_(o_2[l], q_2[l], b_2[l]);
     L.bqkv = F_(f_bqkv[l]); L.bo = F_(f_bo[l]); L.b1 = F_(f_b1[l]); L.b2 = F_(f_b2[l]);
     L.ln1g = F_(f_l1g[l]); L.ln1b = F_(f_l1b[l]); L.ln2g = F_(f_l2g[l]); L.ln2b = F_(f_l2b[l]);
     e->layers.push_back(L);
   }
   e->lnp_g = F_(f_lpg); e->lnp_b = F_(f_lpb); e->proj1_b = F_(f_p1b); e->proj2_b = F_(f_p2b);
-  e->proj1_w = M_(o_p1, q_p1); e->proj2_w = M_(o_p2, q_p2);
-  e->gateup_w = M_(o_gu, q_gu); e->down_w = M_(o_dn, q_dn);
+  e->proj1_w = M_(o_p1, q_p1, b_p1); e->proj2_w = M_(o_p2, q_p2, b_p2);
+  e->gateup_w = M_(o_gu, q_gu, b_gu); e->down_w = M_(o_dn, q_dn, b_dn);
   e->pe = F_(f_pe);
   e->mel.twiddle = F_(f_tw);
   e->mel.window = F_(f_win);

@@ -595,7 +595,7 @@ template <class TL, int NST, class AS, class OM, int EPI, typename OT, int TAG>
 __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const bf16_t* __restrict__ Bw,
                                                                    int32_t N, int32_t K, OM om, EpiP ep,
                                                                    int32_t n_tiles, int32_t pe_ld, int32_t gm,
-                                                                   int32_t k_span) {
+                                                                   int32_t k_span, int32_t b_tiled) {
   static_assert(NST >= 2 && NST <= 8, "stages");
   constexpr int BM = TL::BM, BN = TL::BN, TM = TL::TM, TN = TL::TN;
   constexpr int WTN = TL::WTN, BK = TL::BK, NW = TL::NW;
@@ -658,13 +658,23 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
     const int r = (wv * BDMA + j) * ROWS_PER_DMA + lane / CPR;
     bchunk[j] = (lane % CPR) ^ swz<BK>(r);
     const int n = n0 + r;
-    boffr[j] = n < N ? (uint32_t)n * (uint32_t)K * 2u : 0x80000000u;
+    // byte offset of this lane's 16-byte piece at logical k 0, in either weight layout
+    if (n >= N)
+      boffr[j] = 0x80000000u;
+    else if (b_tiled)
+      boffr[j] = (uint32_t)(n / ROWS_PER_DMA) * (uint32_t)(K / BK) * 1024u + (uint32_t)(lane / CPR) * (BK * 2u) +
+                 (uint32_t)bchunk[j] * 16u;
+    else
+      boffr[j] = (uint32_t)n * (uint32_t)K * 2u + (uint32_t)bchunk[j] * 16u;
   }
   // all DMA instructions of tile kt into stage st (A rows first, then B rows)
   const int k0 = __builtin_amdgcn_readfirstlane((int)blockIdx.y * k_span);
   const int kend = K < k0 + k_span ? K : k0 + k_span;
   auto dma = [&](int kt, bf16_t* st) {
     const int eb = __builtin_amdgcn_readfirstlane(k0 + kt * BK);
+    // B: the step's logical k (a multiple of BK) as a byte offset in the weight layout
+    const int kl = as.k_logical(eb, 0);
+    const uint32_t kadd = b_tiled ? (uint32_t)(kl / BK) * 1024u : (uint32_t)kl * 2u;
 #pragma unroll
     for (int j = 0; j < ADMA; ++j) {
       const int k = k0 + kt * BK + achunk[j] * 8;
@@ -678,9 +688,7 @@ __global__ __launch_bounds__(TL::NT, TL::MINB) void gemm_ilv_kernel(AS as, const
 #pragma unroll
     for (int j = 0; j < BDMA; ++j) {
       const int k = k0 + kt * BK + bchunk[j] * 8;
-      const uint32_t off =
-          (k < kend && boffr[j] != 0x80000000u) ? boffr[j] + (uint32_t)as.k_logical(eb, bchunk[j] * 8) * 2u
-                                                : 0x80000000u;
+      const uint32_t off = (k < kend && boffr[j] != 0x80000000u) ? boffr[j] + kadd : 0x80000000u;
       bf16_t* dst = st + BM * BK + (wv * BDMA + j) * ROWS_PER_DMA * BK;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)dst, 16,
                                                (int)off, 0, 0, 0);
@@ -1132,7 +1140,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(AS as, const float* __res
 template <typename T, class TL, class AS, class OM, int EPI, int TAG, int NST = 0, bool BQ = false>
 hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, const EpiP& ep,
                int64_t m_rows, int32_t pe_ld, hipStream_t s, BQuant bq = BQuant{nullptr, nullptr},
-               int32_t splits = 1, int32_t k_span = 0) {
+               int32_t splits = 1, int32_t k_span = 0, int32_t b_tiled = 0) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     const int n_tiles = (N + TL::BN - 1) / TL::BN;
     const int64_t m_tiles = (m_rows + TL::BM - 1) / TL::BM;
@@ -1144,6 +1152,10 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
       return hipErrorInvalidValue;
     static_assert(!BQ || NST > 0, "int4 weights run in the staged kernel");
     if (splits < 1 || (splits > 1 && (NST == 0 || BQ || k_span <= 0 || (int64_t)(splits - 1) * k_span >= K)))
+      return hipErrorInvalidValue;
+    // a blocked weight layout (b_tiled = its K block) is read by the staged bf16 kernel with the
+    // same BK only
+    if (b_tiled != 0 && (NST == 0 || BQ || b_tiled != TL::BK || K % TL::BK != 0 || N % (512 / TL::BK) != 0))
       return hipErrorInvalidValue;
     if constexpr (BQ && NST > 0) {
       if (K % 128 != 0 || (int64_t)N * (K / 2) > kMaxBytes) return hipErrorInvalidValue;
@@ -1157,8 +1169,9 @@ hipError_t run(const AS& as, const T* Bw, int32_t N, int32_t K, const OM& om, co
     else
       hipLaunchKernelGGL((gemm_ilv_kernel<TL, NST, AS, OM, EPI, bf16_t, TAG>),
                          dim3((unsigned)(m_tiles * n_tiles), (unsigned)splits), dim3(TL::NT), 0, s, as, Bw, N,
-                         K, om, ep, n_tiles, pe_ld, AE_GEMM_GROUP_M, splits > 1 ? k_span : K);
+                         K, om, ep, n_tiles, pe_ld, AE_GEMM_GROUP_M, splits > 1 ? k_span : K, b_tiled);
   } else {
+    if (b_tiled != 0) return hipErrorInvalidValue;
     if constexpr (EPI == EPI_SWIGLU) {
       return hipErrorInvalidValue;  // the fp32 path applies SwiGLU in a separate kernel
     } else {
@@ -1355,7 +1368,8 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
         OLinear om_p{a.M, a.N};
         EpiP ep_p{nullptr, a.ws, nullptr, nullptr, S * a.M * a.N * 4, a.M * a.N};
         hipError_t err = run<T, TileNarrow, ALinear<T>, OLinear, EPI_STORE_F32, TAG, kNarrowStages>(
-            as_p, Bw, a.N, a.K, om_p, ep_p, a.M, 0, s, BQuant{nullptr, nullptr}, (int32_t)S, (int32_t)k_span);
+            as_p, Bw, a.N, a.K, om_p, ep_p, a.M, 0, s, BQuant{nullptr, nullptr}, (int32_t)S, (int32_t)k_span,
+            a.b_tiled);
         if (err != hipSuccess) return err;
         const int64_t groups = a.M * ((EPI == EPI_SWIGLU ? a.N / 2 : a.N) / 4);
         const int64_t blocks = std::min<int64_t>((groups + 255) / 256, 16 * cus);
@@ -1367,21 +1381,30 @@ hipError_t lin(const LinearArgs& a, hipStream_t s) {
   } else {
     if (a.Wq) return hipErrorInvalidValue;
   }
-  switch (lin_kind(a.M, a.N, EPI == EPI_BIAS_GELU, EPI == EPI_SWIGLU)) {
+  // the staged kernels read either weight layout; the one-stage Wide kernel only the plain one
+  LinKind kind = lin_kind(a.M, a.N, EPI == EPI_BIAS_GELU, EPI == EPI_SWIGLU);
+  if (kind == LinKind::Wide && a.b_tiled) kind = LinKind::Large;
+  const BQuant nq{nullptr, nullptr};
+  switch (kind) {
     case LinKind::Small:
       if constexpr (EPI != EPI_SWIGLU)
-        return run<T, TileSmall, ALinear<T>, OLinear, EPI, TAG, kSmallStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+        return run<T, TileSmall, ALinear<T>, OLinear, EPI, TAG, kSmallStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s,
+                                                                              nq, 1, 0, a.b_tiled);
       return hipErrorInvalidValue;
     case LinKind::SmallW:
-      return run<T, TileSmallW, ALinear<T>, OLinear, EPI, TAG, kSmallWStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+      return run<T, TileSmallW, ALinear<T>, OLinear, EPI, TAG, kSmallWStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s,
+                                                                              nq, 1, 0, a.b_tiled);
     case LinKind::Large:
-      return run<T, TileLarge, ALinear<T>, OLinear, EPI, TAG, kLargeStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+      return run<T, TileLarge, ALinear<T>, OLinear, EPI, TAG, kLargeStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s,
+                                                                            nq, 1, 0, a.b_tiled);
     case LinKind::Tall:
-      return run<T, TileTall, ALinear<T>, OLinear, EPI, TAG, kTallStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+      return run<T, TileTall, ALinear<T>, OLinear, EPI, TAG, kTallStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s,
+                                                                          nq, 1, 0, a.b_tiled);
     case LinKind::Wide:
       return run<T, TileWide, ALinear<T>, OLinear, EPI, TAG>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
     default:
-      return run<T, TileNarrow, ALinear<T>, OLinear, EPI, TAG, kNarrowStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s);
+      return run<T, TileNarrow, ALinear<T>, OLinear, EPI, TAG, kNarrowStages>(as, Bw, a.N, a.K, om, ep, a.M, pe_ld, s,
+                                                                              nq, 1, 0, a.b_tiled);
   }
 }
 
@@ -1426,37 +1449,37 @@ constexpr int kConvTStages = 6, kConvNStages = 8;
 
 template <typename T, class TL, int NST, int LEVEL, int TAG>
 hipError_t conv_run(const AConv<T>& as, const T* wpk, int32_t C, const PassGeom& g, int rows_per_win,
-                    int Fout, int Lout_max, int64_t m_rows, const EpiP& ep, hipStream_t s) {
+                    int Fout, int Lout_max, int64_t m_rows, const EpiP& ep, hipStream_t s, int32_t w_tiled) {
   static_assert(TL::BK == 32, "the conv K order takes one (channel block, tap) pair per K step");
   // a wave covers TL::WTM rows of the tile
   if (rows_per_win >= TL::WTM) {
     OConv<LEVEL, true> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
-    return run<T, TL, AConv<T>, OConv<LEVEL, true>, EPI_BIAS_GELU, TAG, NST>(as, wpk, C, 9 * C, om, ep,
-                                                                            m_rows, 0, s);
+    return run<T, TL, AConv<T>, OConv<LEVEL, true>, EPI_BIAS_GELU, TAG, NST>(
+        as, wpk, C, 9 * C, om, ep, m_rows, 0, s, BQuant{nullptr, nullptr}, 1, 0, w_tiled);
   }
   OConv<LEVEL, false> om{g.wins, rows_per_win, Fout, C, Lout_max, m_rows};
-  return run<T, TL, AConv<T>, OConv<LEVEL, false>, EPI_BIAS_GELU, TAG, NST>(as, wpk, C, 9 * C, om, ep,
-                                                                           m_rows, 0, s);
+  return run<T, TL, AConv<T>, OConv<LEVEL, false>, EPI_BIAS_GELU, TAG, NST>(
+      as, wpk, C, 9 * C, om, ep, m_rows, 0, s, BQuant{nullptr, nullptr}, 1, 0, w_tiled);
 }
 
 template <typename T, int LEVEL, int TAG>
 hipError_t conv_dispatch(const AConv<T>& as, const T* wpk, int32_t C, const PassGeom& g, int rows_per_win,
-                         int Fout, int Lout_max, int64_t m_rows, const EpiP& ep, hipStream_t s) {
+                         int Fout, int Lout_max, int64_t m_rows, const EpiP& ep, hipStream_t s, int32_t w_tiled) {
   const int64_t cus = cu_count();
   if (std::is_same<T, bf16_t>::value && 2 * tile_count(m_rows, C, 256, 256) < cus) {
     if (tile_count(m_rows, C, 128, 128) <= cus)
       return conv_run<T, TileConvN, kConvNStages, LEVEL, TAG>(as, wpk, C, g, rows_per_win, Fout, Lout_max,
-                                                              m_rows, ep, s);
+                                                              m_rows, ep, s, w_tiled);
     return conv_run<T, TileConvT, kConvTStages, LEVEL, TAG>(as, wpk, C, g, rows_per_win, Fout, Lout_max,
-                                                            m_rows, ep, s);
+                                                            m_rows, ep, s, w_tiled);
   }
   return conv_run<T, TileConv, kConvStages, LEVEL, TAG>(as, wpk, C, g, rows_per_win, Fout, Lout_max, m_rows,
-                                                        ep, s);
+                                                        ep, s, w_tiled);
 }
 
 template <typename T>
 hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T* wpk,
-                             const float* bias, int32_t C, T* out, hipStream_t s) {
+                             const float* bias, int32_t C, T* out, hipStream_t s, int32_t w_tiled) {
   const int Fin = level == 2 ? 64 : 32;
   const int Fout = Fin / 2;
   // the pass's time strides: act1 rows L1s, act2 rows L2s = ceil(L1s / 2); conv3 output rows
@@ -1472,15 +1495,15 @@ hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T*
   const int64_t out_rows = level == 2 ? (int64_t)g.n_win * Lout_max * Fout : g.n_tok * Fout;
   EpiP ep{bias, out, nullptr, nullptr, out_rows * C * (int64_t)sizeof(T)};
   if (level == 2)
-    return conv_dispatch<T, 2, ENC_K_CONV2>(as, wpk, C, g, rows_per_win, Fout, Lout_max, m_rows, ep, s);
-  return conv_dispatch<T, 3, ENC_K_CONV3>(as, wpk, C, g, rows_per_win, Fout, Lout_max, m_rows, ep, s);
+    return conv_dispatch<T, 2, ENC_K_CONV2>(as, wpk, C, g, rows_per_win, Fout, Lout_max, m_rows, ep, s, w_tiled);
+  return conv_dispatch<T, 3, ENC_K_CONV3>(as, wpk, C, g, rows_per_win, Fout, Lout_max, m_rows, ep, s, w_tiled);
 }
 
 template hipError_t launch_linear<bf16_t>(const LinearArgs&, int, int, hipStream_t);
 template hipError_t launch_linear<float>(const LinearArgs&, int, int, hipStream_t);
 template hipError_t launch_conv_igemm<bf16_t>(const PassGeom&, int, const bf16_t*, const bf16_t*,
-                                              const float*, int32_t, bf16_t*, hipStream_t);
+                                              const float*, int32_t, bf16_t*, hipStream_t, int32_t);
 template hipError_t launch_conv_igemm<float>(const PassGeom&, int, const float*, const float*,
-                                             const float*, int32_t, float*, hipStream_t);
+                                             const float*, int32_t, float*, hipStream_t, int32_t);
 
 }  // namespace ae

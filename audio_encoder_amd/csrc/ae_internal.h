@@ -168,6 +168,8 @@ struct LinearArgs {
   const uint8_t* Wq = nullptr; const bf16_t* Ws = nullptr;
   // split-K scratch for GEMMs too small to fill the GPU (bf16 path; null: never split)
   float* ws = nullptr; int64_t ws_bytes = 0;
+  // bf16 W in K-blocked layout (0: plain [N][K]; else its K block, see below)
+  int32_t b_tiled = 0;
 };
 // split-K scratch each encoder keeps (fp32 partial products of the small-M GEMMs)
 constexpr int64_t kSplitKScratchBytes = int64_t(64) << 20;
@@ -175,10 +177,17 @@ template <typename T>
 hipError_t launch_linear(const LinearArgs& a, int epi, int tag, hipStream_t s);
 
 // implicit-GEMM conv (conv2: level 2, conv3: level 3).  in: level 2 -> act1 [n_win][L1s][64][C],
-// level 3 -> act2 [n_win][L2s][32][C]; out: level 2 -> act2; level 3 -> [n_tok][16][C]
+// level 3 -> act2 [n_win][L2s][32][C]; out: level 2 -> act2; level 3 -> [n_tok][16][C].  wpk:
+// [C][9][C] (w_tiled 0) or K-blocked (w_tiled 32: blocks of 16 rows x 32 k, bf16 only)
 template <typename T>
 hipError_t launch_conv_igemm(const PassGeom& g, int level, const T* in, const T* wpk,
-                             const float* bias, int32_t C, T* out, hipStream_t s);
+                             const float* bias, int32_t C, T* out, hipStream_t s, int32_t w_tiled = 0);
+
+// K-blocked weight layout read by the staged bf16 kernels (b_tiled / w_tiled = BK): W [N][K]
+// stored as blocks of R = 512 / BK rows x BK columns, one kilobyte each, so that every LDS-DMA
+// instruction of a K step reads one contiguous kilobyte instead of R row pieces.  Block
+// (n / R, k / BK) starts at element ((n / R) * (K / BK) + k / BK) * 512; row n % R of it at
+// (n % R) * BK.  Needs N % R == 0 and K % BK == 0.
 
 template <typename T>
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, T* y, int64_t M,

@@ -26,7 +26,8 @@ hipError_t launch_conv1(const PassGeom&, const float*, const uint32_t*, const fl
 template <typename T>
 hipError_t launch_linear(const LinearArgs&, int, int, hipStream_t) { return refused("linear"); }
 template <typename T>
-hipError_t launch_conv_igemm(const PassGeom&, int, const T*, const T*, const float*, int32_t, T*, hipStream_t) {
+hipError_t launch_conv_igemm(const PassGeom&, int, const T*, const T*, const float*, int32_t, T*, hipStream_t,
+                             int32_t) {
   return refused("conv_igemm");
 }
 template <typename T>
@@ -53,7 +54,7 @@ hipError_t launch_splice(const T*, int64_t, int32_t, const int64_t*, T*, int64_t
                                       const float*, const float*, int32_t, T*, hipStream_t);               \
   template hipError_t launch_linear<T>(const LinearArgs&, int, int, hipStream_t);                          \
   template hipError_t launch_conv_igemm<T>(const PassGeom&, int, const T*, const T*, const float*, int32_t, \
-                                           T*, hipStream_t);                                               \
+                                           T*, hipStream_t, int32_t);                                      \
   template hipError_t launch_layernorm<T>(const float*, const float*, const float*, T*, int64_t, int32_t,  \
                                           float, hipStream_t);                                             \
   template hipError_t launch_attention<T>(const T*, const Win*, const int32_t*, int32_t, int32_t, int32_t, \

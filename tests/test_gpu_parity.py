@@ -518,6 +518,60 @@ def test_full_c1_stagewise(full):
         check_bf16(got[sl], yref, "adapter out")
 
 
+@pytest.mark.parametrize("n_clips", [1, 8])
+def test_full_blocked_weights_equal_plain_entries(full, n_clips):
+    """The forward holds its bf16 weights in the K-blocked layout, the kernel-level entries take
+    them plain ([N][K], conv [C][9][C]).  Both put the same bits into LDS, so conv2 and layer 0
+    recomputed through the kernel-level entries from the forward's own stage inputs equal the
+    forward's stages bit for bit: one clip runs the small-row tiles and the 256x256 conv tile,
+    eight clips (3000 tokens) the tiles of the 16-clip batch's lanes."""
+    enc, Wt = full
+    cfg = B.FULL
+    x = np.stack([S.pink_plus_bursts(seed=40 + i) for i in range(n_clips)])
+    pcm = to_dev(x)
+    plan = B.encoder_plan_windows(cfg, x.shape[1], n_clips)
+    nw, W, C, d = len(plan), cfg["window_tokens"], cfg["conv_channels"], cfg["d_model"]
+    F = int(plan[-1, 6] + plan[-1, 5])
+    bf = torch.bfloat16
+
+    def dbf(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(bf)
+
+    def df(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+    if n_clips == 1:
+        c1 = enc.debug_stage(pcm, B.STAGE_CONV1)
+        c2 = enc.debug_stage(pcm, B.STAGE_CONV2).cpu().numpy()
+        tab = np.zeros((nw, 8), np.int32)
+        tab[:, :7] = plan
+        wp = Wt["conv2.w"].reshape(C, C, 9).transpose(0, 2, 1)
+        act2 = torch.zeros((nw, 2 * W, 32, C), dtype=bf, device=DEV)
+        B.op_conv(2, c1.to(bf), torch.from_numpy(tab).to(DEV), W, 4 * W, F, dbf(wp), df(Wt["conv2.b"]), act2)
+        got = act2.float().cpu().numpy()
+        for i, r in enumerate(plan):
+            L2 = int(r[4])
+            assert np.array_equal(got[i, :L2], c2[i, :L2]), ("conv2", i)
+    x0 = enc.debug_stage(pcm, B.STAGE_EMBED)
+    l0 = enc.debug_stage(pcm, B.STAGE_LAYER, 0)
+    p = "layers.0."
+    xn = torch.empty((F, d), dtype=bf, device=DEV)
+    B.op_layernorm(x0, df(Wt[p + "ln1.g"]), df(Wt[p + "ln1.b"]), xn)
+    qkv = torch.empty((F, 3 * d), dtype=bf, device=DEV)
+    B.op_linear(xn, dbf(np.concatenate([Wt[p + "q.w"], Wt[p + "k.w"], Wt[p + "v.w"]])),
+                df(np.concatenate([Wt[p + "q.b"], Wt[p + "k.b"], Wt[p + "v.b"]])), qkv, 0)
+    att = torch.zeros((F, d), dtype=bf, device=DEV)
+    B.op_attention(qkv, torch.from_numpy(np.ascontiguousarray(plan[:, [6, 5]])).to(DEV), cfg["n_heads"], att)
+    xr = x0.clone()
+    B.op_linear(att, dbf(Wt[p + "o.w"]), df(Wt[p + "o.b"]), xr, 2)
+    B.op_layernorm(xr, df(Wt[p + "ln2.g"]), df(Wt[p + "ln2.b"]), xn)
+    h = torch.empty((F, cfg["d_ffn"]), dtype=bf, device=DEV)
+    B.op_linear(xn, dbf(Wt[p + "fc1.w"]), df(Wt[p + "fc1.b"]), h, 1)
+    B.op_linear(h, dbf(Wt[p + "fc2.w"]), df(Wt[p + "fc2.b"]), xr, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(xr, l0), float((xr - l0).abs().max())
+
+
 def test_full_c2_every_window(full):
     enc, Wt = full
     xs = S.mixed_batch(range(101, 117))
