@@ -186,6 +186,8 @@ def main():
     ap.add_argument("--split-small-gemms", action="store_true",
                     help="split K of GEMMs too small to fill the GPU (single clips); their rows then "
                          "round differently from the same rows in a large call")
+    ap.add_argument("--pieces-per-pass", type=int, default=0,
+                    help="long-audio workloads: 64 s pieces per pass (default 8 for c3, 1 for c4)")
     ap.add_argument("--roofline-steps", type=int, default=3)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the run, launch one plain device copy of this many MiB (a "
@@ -212,7 +214,7 @@ def main():
     pcm = torch.from_numpy(pcm_np).cuda()
     long_mode = args.workload in ("c3", "c4")
     ragged = args.workload == "ragged"
-    ppp = 8 if args.workload == "c3" else 1
+    ppp = args.pieces_per_pass or (8 if args.workload == "c3" else 1)
     if ragged:
         lengths = ragged_lengths()
         n_clips, n_samples = len(lengths), max(lengths)
@@ -323,7 +325,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload], "clips": int(n_clips),
                    "samples_per_clip": int(n_samples) if not ragged else lengths,
-                   "tokens_per_step": wm["ntok"], "audio_seconds_per_step": audio_s},
+                   "tokens_per_step": wm["ntok"], "audio_seconds_per_step": audio_s,
+                   **({"pieces_per_pass": ppp} if long_mode else {})},
         "tflops": round(tflops, 2),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roof,
