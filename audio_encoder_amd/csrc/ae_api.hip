@@ -1314,7 +1314,9 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
     });
     return BK;
   };
-  const int32_t b_conv2 = blockify(o_conv2, C, 9 * C, 32), b_conv3 = blockify(o_conv3, C, 9 * C, 32);
+  // conv2 and conv3 have the same shape, hence the same layout (one flag for both)
+  const int32_t b_conv = blockify(o_conv2, C, 9 * C, 32);
+  blockify(o_conv3, C, 9 * C, 32);
   const int32_t b_co = blockify(o_co, d, 16 * C, 64);
   std::vector<int32_t> b_qkv, b_o, b_1, b_2;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -1359,8 +1361,7 @@ encoder_status encoder_create(const float* weights, int64_t n_floats, const enco
   auto F_ = [&](int64_t o) { return e->fdev + o; };
   e->conv1_w = F_(f_c1w); e->conv1_b = F_(f_c1b); e->conv2_b = F_(f_c2b); e->conv3_b = F_(f_c3b);
   e->conv2_w = W_(o_conv2); e->conv3_w = W_(o_conv3);
-  e->conv_blk = b_conv2;  // conv3 has the same shape, so the same layout
-  (void)b_conv3;
+  e->conv_blk = b_conv;
   e->conv_out_w.w = W_(o_co);
   e->conv_out_w.blk = b_co;
   for (int l = 0; l < c.n_layers; ++l) {
