@@ -8,8 +8,10 @@
 // one input position; out-of-image taps and positions past a window's valid length read as
 // zero; the staged kernels walk K as 32-channel blocks, then taps, then channels, see AConv).
 // B is a weight matrix [N, K] (PyTorch Linear layout; conv weights permuted to [out][tap][in]
-// at pack time).  Epilogues fuse the bias, exact GELU, the fp32 residual update, the sinusoidal
-// positions and the SwiGLU gate into the store.
+// at pack time), plain or, for the staged kernel, K-blocked (b_tiled: blocks of 512/BK rows x
+// BK columns, so that each LDS-DMA instruction reads one contiguous kilobyte; the forward's own
+// weights are stored so).  Epilogues fuse the bias, exact GELU, the fp32 residual update, the
+// sinusoidal positions and the SwiGLU gate into the store.
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950 with fp32 accumulators.  Tiles move from global
 // memory straight into LDS with buffer_load_dwordx4 ... lds (16 bytes per lane, no VGPR
